@@ -1,0 +1,204 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse mixture-of-experts block forward.
+ *
+ * The operation is the forward pass of one Qwen3/Mixtral-style sparse MoE block:
+ *   router linear (hidden -> E logits, no bias) -> fp32 softmax -> top-k
+ *   -> optional renormalisation of the k weights -> dispatch of each token to
+ *   its k experts -> per-expert SwiGLU MLP down(silu(gate x) * up x)
+ *   -> routing-weighted combine back into token order,
+ * plus the load-balance statistics f_i, P_i and aux = E * sum_i f_i * P_i.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [QWEN3-READ]  "大模型-qwen3 MoE 详细解读" (cnblogs.com/cavalier-chen), the
+ *                 Qwen3MoeSparseMoeBlock code block and its annotated copy (§二),
+ *                 and the design notes of §三 (Mixtral difference, permutation).
+ *   [MOE-128x8]   "MoE架构深度解析：128专家与8激活的智能路由" (mcp.csdn.net), the
+ *                 config JSON, the load-balancing section (辅助损失) and the
+ *                 parameter-distribution table (参数分布与存储结构).
+ *   [LAB17]       "项目 17：稀疏性的调度艺术：实现双专家 MoE 路由" (sshipanoo.com),
+ *                 第一阶段 (linear router + softmax) and 第二阶段 实现流程.
+ *   [WHY-MOE]     "为什么MoE不是“堆更多参数”的简单答案" (hncyxsy.com), §1 (top-2 of
+ *                 eight router scores) and §2.2 (router taxonomy).
+ *   [QWEN3-ROUTE] "Qwen3 细粒度专家路由策略全解析" (lpnh.cn), §二 step 5 (per-token
+ *                 top-k and renormalisation).
+ *
+ * Notation: T tokens, H hidden size, E experts, k experts per token,
+ * I = moe_intermediate_size. A routing pair is (token t, slot j), pair id
+ * p = t*k + j, P = T*k pairs.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
+ *    row-major, 16-byte aligned. Weights use the nn.Linear [out, in] layout.
+ *  - `dtype` (moe_config.dtype) is the element type of x, every weight, h,
+ *    y_sorted and out. Logits, probabilities, weights and statistics are fp32;
+ *    indices and counts are int32.
+ *  - The library never allocates device memory, never synchronises the host
+ *    with the device, and keeps no mutable global state: all work is enqueued
+ *    on `stream` in call order. Scratch space is the caller's `workspace`,
+ *    of at least moe_workspace_size(cfg) bytes, 256-byte aligned.
+ *  - Argument checks run on the host before any launch and return a status;
+ *    on error nothing is enqueued. MOE_ERR_HIP means a launch failed
+ *    (hipGetLastError); faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - Supported sizes (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 256,
+ *    1 <= k <= min(E, 16), H and I multiples of 64, T >= 1, T*k < 2^31,
+ *    T*k*max(H,I) < 2^31 elements.
+ *  - Non-finite values in x or the weights are outside the contract.
+ *  - Results are deterministic: the same inputs give bitwise-identical
+ *    outputs on every call (fixed reduction orders, no float atomics).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null required pointer, T<1, k<1, k>E, bad dtype */
+  MOE_ERR_UNSUPPORTED = 2,      /* outside the supported sizes listed above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4               /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Block configuration; the field names follow the config keys of [MOE-128x8]
+ * (config JSON) and [QWEN3-READ] (__init__ of the block). */
+typedef struct {
+  int32_t num_tokens;     /* T */
+  int32_t hidden;         /* H  (hidden_size) */
+  int32_t num_experts;    /* E  (num_experts) */
+  int32_t top_k;          /* k  (num_experts_per_tok) */
+  int32_t intermediate;   /* I  (moe_intermediate_size) */
+  int32_t norm_topk_prob; /* 1: renormalise the k weights (Qwen3); 0: use the
+                             softmax probabilities as they are (Mixtral) */
+  moe_dtype dtype;        /* element type of x, weights, h, y_sorted, out */
+} moe_config;
+
+/* Load-balance outputs; every field may be NULL (then it is not written).
+ *   counts[E] int32 : n_e = number of pairs routed to expert e
+ *   f[E]      fp32  : f_e = n_e / (T*k), the fraction of routed pairs
+ *   P[E]      fp32  : P_e = (1/T) * sum_t softmax(l_t)_e, the mean router
+ *                     probability (full softmax, before top-k)
+ *   aux[1]    fp32  : E * sum_e f_e * P_e
+ * Definition: [MOE-128x8], load-balancing section (负载均衡机制), with n = E. */
+typedef struct {
+  int32_t* counts;
+  float* f;
+  float* P;
+  float* aux;
+} moe_aux_out;
+
+/* Bytes of workspace every entry point below needs for `cfg` (the maximum
+ * over all of them). Host-only and pure; returns 0 if `cfg` is invalid. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Router: logits, softmax, top-k, renormalisation.
+ * [QWEN3-READ] forward code: gate linear (bias=False), softmax in fp32 over the
+ * experts, top-k, and division of the k weights by their sum when
+ * norm_topk_prob.
+ *   x         [T,H] dtype. If NULL, `logits` is an INPUT: [T,E] fp32 logits are
+ *             read instead of computed (w_router and logit_bias are then
+ *             ignored; bias must already be included).
+ *   w_router  [E,H] dtype (required when x != NULL).
+ *   logit_bias[E] fp32 or NULL: added to every token's logits before the
+ *             softmax and the selection.
+ *   logits    [T,E] fp32: output (may be NULL) when x != NULL; input when x == NULL.
+ *   topk_idx  [T,k] int32 out: the k experts with the largest logits, in
+ *             descending logit order; equal logits are ordered by ascending
+ *             expert index (+0.0 and -0.0 compare equal).
+ *   topk_w    [T,k] fp32 out: softmax probability of each selected expert,
+ *             divided by the sum of the k selected probabilities iff
+ *             norm_topk_prob.
+ * No workspace is needed. */
+moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_router,
+                           const float* logit_bias, float* logits, int32_t* topk_idx,
+                           float* topk_w, hipStream_t stream);
+
+/* Dispatch: group the T*k pairs by expert (a stable counting sort).
+ * Replaces the one-hot mask + per-expert torch.where loop of [QWEN3-READ]
+ * (forward code) by the token permutation described in its §三.
+ *   topk_idx       [T,k] int32 in, every value in [0,E).
+ *   expert_counts  [E]   int32 out: n_e.
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of n_e; [E] = T*k.
+ *   sorted_pair    [T*k] int32 out: pair ids grouped by expert, ascending
+ *                  pair id inside a group: pairs of expert e are at
+ *                  [offsets[e], offsets[e+1]).
+ *   pair_pos       [T*k] int32 out: inverse, sorted_pair[pair_pos[p]] == p.
+ * Out-of-range expert ids are outside the contract (the kernels clamp reads
+ * but the permutation is then meaningless). */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Experts, first half: for every sorted row i of expert e (offsets[e] <= i <
+ * offsets[e+1]) with token t = sorted_pair[i] / k:
+ *     h[i, :] = silu(W_gate[e] x_t) * (W_up[e] x_t),  silu(z) = z / (1 + e^-z)
+ * [MOE-128x8] (gate_proj / up_proj of each expert, parameter table) and
+ * [QWEN3-READ] (one MLP per expert with moe_intermediate_size).
+ *   x      [T,H] dtype; w_gate, w_up [E,I,H] dtype; h [T*k, I] dtype out.
+ * Accumulation is fp32; h is rounded once to dtype. Experts with no rows
+ * read no weight bytes. */
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_t* sorted_pair,
+                              const int32_t* expert_offsets, const void* w_gate,
+                              const void* w_up, void* h, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Experts, second half: y_sorted[i, :] = W_down[e] h[i, :] for the rows of
+ * every expert e.  h [T*k, I] dtype; w_down [E,H,I] dtype;
+ * y_sorted [T*k, H] dtype out (fp32 accumulation, one rounding). */
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                           const void* w_down, void* y_sorted, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Both halves: y_sorted[i] = W_down[e] (silu(W_gate[e] x_t) * W_up[e] x_t),
+ * the unweighted output of expert e for the token of sorted row i. The
+ * intermediate h lives in `workspace`. */
+moe_status moe_expert_swiglu(const moe_config* cfg, const void* x, const int32_t* sorted_pair,
+                             const int32_t* expert_offsets, const void* w_gate,
+                             const void* w_up, const void* w_down, void* y_sorted,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Combine: out[t, :] = sum_{j=0}^{k-1} topk_w[t,j] * y_sorted[pair_pos[t*k+j], :]
+ * summed in fp32 in slot order j = 0..k-1 and rounded once to dtype; no
+ * atomics. Replaces the index_add_ scatter of [QWEN3-READ] (forward code).
+ *   y_sorted [T*k,H] dtype; pair_pos [T*k] int32; topk_w [T,k] fp32;
+ *   out [T,H] dtype. */
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_t* pair_pos,
+                       const float* topk_w, void* out, hipStream_t stream);
+
+/* Load-balance statistics from router logits (bias included) and the
+ * selection: see moe_aux_out. [MOE-128x8] load-balancing section.
+ *   logits [T,E] fp32; topk_idx [T,k] int32. */
+moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
+                         moe_aux_out out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* The whole block: router -> dispatch -> experts -> combine -> statistics,
+ * all on `stream`, with no host synchronisation.
+ *   x [T,H], w_router [E,H], logit_bias [E] fp32 or NULL, w_gate/w_up [E,I,H],
+ *   w_down [E,H,I], out [T,H] (dtype).
+ *   router_logits [T,E] fp32, topk_idx [T,k], topk_w [T,k]: optional outputs
+ *   (NULL: kept in the workspace). aux: optional statistics (fields NULL: not
+ *   computed). The computation of every stage is that of the entry points
+ *   above. */
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logit_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* out, float* router_logits,
+                             int32_t* topk_idx, float* topk_w, moe_aux_out aux,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,273 @@
+/*
+ * moe_oracle.c — plain CPU oracle of the sparse MoE block forward.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this file's library. The GPU product path shares no
+ * code with it and never calls it.
+ *
+ * Every function is the written-out definition of one step, as scalar loops
+ * with fp64 accumulation; no blocking, fusion or reordering beyond what the
+ * definition states. OpenMP only splits independent tokens / rows.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [QWEN3-READ]  "大模型-qwen3 MoE 详细解读" (cnblogs), Qwen3MoeSparseMoeBlock
+ *                 forward code and §三 (Mixtral difference).
+ *   [MOE-128x8]   "MoE架构深度解析：128专家与8激活的智能路由" (csdn), load-balancing
+ *                 section and the expert parameter table.
+ *   [LAB17]       "项目 17：稀疏性的调度艺术：实现双专家 MoE 路由" (sshipanoo),
+ *                 第二阶段 实现流程.
+ *
+ * Element types: dtype 0 = fp32 array, dtype 1 = bf16 array given as the
+ * 16-bit patterns (widened to double exactly).
+ * All functions return 0 on success, -1 on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact widening of one element to double. */
+static double elem(const void* p, int dtype, size_t i) {
+  if (dtype == 0) return (double)((const float*)p)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static void round_bf16_inplace(double* v) {
+  /* round-to-nearest-even of the fp32 value to bf16, back to double */
+  float f = (float)*v;
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  uint32_t lsb = (b >> 16) & 1u;
+  b = (b + 0x7FFFu + lsb) & 0xFFFF0000u;
+  memcpy(&f, &b, sizeof f);
+  *v = (double)f;
+}
+
+/* Router logits, [QWEN3-READ] forward code (gate = Linear(H, E, bias=False)):
+ *   l[t,e] = fp32( sum_{h ascending} x[t,h] * Wr[e,h]  (+ bias[e]) )
+ * bias is an optional additive per-expert logit offset (NULL: none). */
+int orc_logits(int T, int H, int E, int dtype, const void* x, const void* wr,
+               const float* bias, float* logits) {
+  if (T < 0 || H < 1 || E < 1 || !x || !wr || !logits) return -1;
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int h = 0; h < H; ++h)
+        s += elem(x, dtype, (size_t)t * H + h) * elem(wr, dtype, (size_t)e * H + h);
+      if (bias) s += (double)bias[e];
+      logits[(size_t)t * E + e] = (float)s;
+    }
+  }
+  return 0;
+}
+
+/* Softmax over the experts and top-k selection, [QWEN3-READ] forward code:
+ *   p[t,e] = exp(l[t,e] - m_t) / sum_e' exp(l[t,e'] - m_t),  m_t = max_e l[t,e]
+ *   slots j = 0..k-1 hold the k experts with the largest logits, in descending
+ *   order of the fp32 logit; equal logits are ordered by ascending expert index
+ *   (C float comparison, so +0.0 == -0.0). Selecting on logits is selecting on
+ *   p, since softmax is strictly increasing.
+ *   w[t,j] = p[t,e_j] / sum_j' p[t,e_j']  if norm (Qwen3), else p[t,e_j]
+ *   (Mixtral keeps the unrenormalised probabilities, [QWEN3-READ] §三).
+ * forced_idx (nullable): use these experts instead of selecting (weights are
+ * computed the same way from them).
+ * probs (nullable) receives the full softmax [T,E]. */
+int orc_route(int T, int E, int k, int norm, const float* logits, const int32_t* forced_idx,
+              int32_t* idx, double* w, double* probs) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if ((double)l[e] > m) m = (double)l[e];
+    double s = 0.0;
+    for (int e = 0; e < E; ++e) s += exp((double)l[e] - m);
+    if (probs)
+      for (int e = 0; e < E; ++e) probs[(size_t)t * E + e] = exp((double)l[e] - m) / s;
+
+    int32_t* sel = idx + (size_t)t * k;
+    if (forced_idx) {
+      for (int j = 0; j < k; ++j) {
+        sel[j] = forced_idx[(size_t)t * k + j];
+        if (sel[j] < 0 || sel[j] >= E) bad = 1;
+      }
+    } else {
+      /* k passes of "largest remaining logit, lowest index on ties" */
+      for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+          int taken = 0;
+          for (int q = 0; q < j; ++q)
+            if (sel[q] == e) taken = 1;
+          if (taken) continue;
+          if (best < 0 || l[e] > l[best]) best = e; /* strict: earlier index wins ties */
+        }
+        sel[j] = best;
+      }
+    }
+    if (bad) continue;
+    double psum = 0.0;
+    for (int j = 0; j < k; ++j) psum += exp((double)l[sel[j]] - m) / s;
+    for (int j = 0; j < k; ++j) {
+      double p = exp((double)l[sel[j]] - m) / s;
+      w[(size_t)t * k + j] = norm ? p / psum : p;
+    }
+  }
+  return bad ? -1 : 0;
+}
+
+/* Dispatch as a counting sort of the pairs by expert ([QWEN3-READ] §三: put the
+ * tokens of one expert next to each other, and keep the inverse):
+ *   counts[e] = #{p : idx[p] == e};  offsets = exclusive prefix sum;
+ *   sorted_pair = pair ids grouped by expert, ascending inside a group;
+ *   pair_pos[sorted_pair[i]] = i. */
+int orc_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_pair, int32_t* pair_pos) {
+  if (T < 0 || E < 1 || k < 1 || !idx || !counts || !offsets || !sorted_pair || !pair_pos)
+    return -1;
+  const long P = (long)T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (long p = 0; p < P; ++p) {
+    if (idx[p] < 0 || idx[p] >= E) return -1;
+    counts[idx[p]] += 1;
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!fill) return -1;
+  for (int e = 0; e < E; ++e) fill[e] = offsets[e];
+  for (long p = 0; p < P; ++p) {
+    int32_t pos = fill[idx[p]]++;
+    sorted_pair[pos] = (int32_t)p;
+    pair_pos[p] = pos;
+  }
+  free(fill);
+  return 0;
+}
+
+/* One expert MLP per requested row, [MOE-128x8] gate_proj / up_proj / down_proj
+ * with the SwiGLU form down(silu(gate x) * up x), no biases:
+ *   g_i = sum_h Wg[e,i,h] x[t,h],  u_i = sum_h Wu[e,i,h] x[t,h]
+ *   a_i = silu(g_i) * u_i,  silu(z) = z / (1 + exp(-z))
+ *   y[r,h] = sum_i Wd[e,h,i] a_i
+ * Layouts: x [*,H]; Wg, Wu [E,I,H]; Wd [E,H,I]. Row r uses token tok[r] and
+ * expert ex[r]. round_h != 0 rounds each a_i to bf16 first (diagnostic mode
+ * mirroring a bf16 intermediate). */
+int orc_expert_rows(int H, int I, int dtype, const void* x, const void* wg, const void* wu,
+                    const void* wd, int n, const int32_t* tok, const int32_t* ex, int round_h,
+                    double* y) {
+  if (H < 1 || I < 1 || n < 0 || !x || !wg || !wu || !wd || !tok || !ex || !y) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!a) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int r = 0; r < n; ++r) {
+      if (!a) continue;
+      const size_t t = (size_t)tok[r], e = (size_t)ex[r];
+      for (int i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        const size_t wrow = (e * (size_t)I + (size_t)i) * (size_t)H;
+        for (int h = 0; h < H; ++h) {
+          const double xv = elem(x, dtype, t * (size_t)H + h);
+          g += elem(wg, dtype, wrow + h) * xv;
+          u += elem(wu, dtype, wrow + h) * xv;
+        }
+        a[i] = g / (1.0 + exp(-g)) * u;
+        if (round_h) round_bf16_inplace(&a[i]);
+      }
+      for (int h = 0; h < H; ++h) {
+        double s = 0.0;
+        const size_t drow = (e * (size_t)H + (size_t)h) * (size_t)I;
+        for (int i = 0; i < I; ++i) s += elem(wd, dtype, drow + i) * a[i];
+        y[(size_t)r * H + h] = s;
+      }
+    }
+    free(a);
+  }
+  return bad ? -1 : 0;
+}
+
+/* Routing-weighted combine, [QWEN3-READ] forward code (expert output times its
+ * routing weight, accumulated into the token's row):
+ *   out[t,:] = sum_{j=0..k-1} w[t,j] * y_pair[t*k+j, :]   (slot order, double) */
+int orc_combine(int T, int H, int k, const double* w, const double* y_pair, double* out) {
+  if (T < 0 || H < 1 || k < 1 || !w || !y_pair || !out) return -1;
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double s = 0.0;
+      for (int j = 0; j < k; ++j)
+        s += w[(size_t)t * k + j] * y_pair[((size_t)t * k + j) * H + h];
+      out[(size_t)t * H + h] = s;
+    }
+  }
+  return 0;
+}
+
+/* Load-balance statistics, [MOE-128x8] load-balancing section, n = E:
+ *   f_e = counts[e] / (T*k)       (fraction of routed pairs)
+ *   P_e = (1/T) sum_t probs[t,e]  (mean full-softmax probability)
+ *   aux = E * sum_e f_e * P_e */
+int orc_aux(int T, int E, int k, const int32_t* counts, const double* probs, double* f,
+            double* P, double* aux) {
+  if (T < 1 || E < 1 || k < 1 || !counts || !probs || !f || !P || !aux) return -1;
+  double acc = 0.0;
+  for (int e = 0; e < E; ++e) {
+    double s = 0.0;
+    for (int t = 0; t < T; ++t) s += probs[(size_t)t * E + e];
+    f[e] = (double)counts[e] / ((double)T * (double)k);
+    P[e] = s / (double)T;
+    acc += f[e] * P[e];
+  }
+  *aux = (double)E * acc;
+  return 0;
+}
+
+/* The block forward for the tokens listed in `tokens` (all T when tokens ==
+ * NULL): logits -> route -> experts -> combine, [QWEN3-READ] forward code.
+ * n = number of listed tokens. Outputs are per listed token:
+ *   logits [n,E] fp32, idx [n,k], w [n,k], out [n,H] double.
+ * forced_idx [n,k] (nullable) replaces the selection. */
+int orc_forward_tokens(int T, int H, int E, int k, int I, int norm, int dtype, const void* x,
+                       const void* wr, const float* bias, const void* wg, const void* wu,
+                       const void* wd, int n, const int32_t* tokens, const int32_t* forced_idx,
+                       int round_h, float* logits, int32_t* idx, double* w, double* out) {
+  if (T < 1 || n < 0 || !logits || !idx || !w || !out) return -1;
+  const size_t rowb = (size_t)H * (dtype == 0 ? 4 : 2);
+  /* gather the listed rows of x so the steps below see a dense [n,H] block */
+  char* xs = (char*)malloc(rowb * (size_t)(n > 0 ? n : 1));
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1) * k);
+  int32_t* ex = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1) * k);
+  double* y = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * k * H);
+  int rc = -1;
+  if (!xs || !tok || !ex || !y) goto done;
+  for (int r = 0; r < n; ++r) {
+    int t = tokens ? tokens[r] : r;
+    if (t < 0 || t >= T) goto done;
+    memcpy(xs + rowb * r, (const char*)x + rowb * (size_t)t, rowb);
+  }
+  if (orc_logits(n, H, E, dtype, xs, wr, bias, logits)) goto done;
+  if (orc_route(n, E, k, norm, logits, forced_idx, idx, w, NULL)) goto done;
+  for (int r = 0; r < n; ++r)
+    for (int j = 0; j < k; ++j) {
+      tok[r * k + j] = r;
+      ex[r * k + j] = idx[r * k + j];
+    }
+  if (orc_expert_rows(H, I, dtype, xs, wg, wu, wd, n * k, tok, ex, round_h, y)) goto done;
+  if (orc_combine(n, H, k, w, y, out)) goto done;
+  rc = 0;
+done:
+  free(xs);
+  free(tok);
+  free(ex);
+  free(y);
+  return rc;
+}

@@ -1,0 +1,188 @@
+"""Python view of the plain CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module. The GPU product path
+never calls it and shares no code with it.
+
+Arrays are numpy: fp32 configs pass float32 arrays, bf16 configs pass the bf16
+bit patterns as uint16 arrays (the C side widens them exactly). Outputs that the
+definition computes in double (weights, probabilities, expert outputs, the block
+output) come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.orc_logits.argtypes = [i, i, i, i, P, P, P, P]
+        lib.orc_route.argtypes = [i, i, i, i, P, P, P, P, P]
+        lib.orc_dispatch.argtypes = [i, i, i, P, P, P, P, P]
+        lib.orc_expert_rows.argtypes = [i, i, i, P, P, P, P, i, P, P, i, P]
+        lib.orc_combine.argtypes = [i, i, i, P, P, P]
+        lib.orc_aux.argtypes = [i, i, i, P, P, P, P, P]
+        lib.orc_forward_tokens.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P, i,
+                                           P, P, P, P]
+        for f in (lib.orc_logits, lib.orc_route, lib.orc_dispatch, lib.orc_expert_rows,
+                  lib.orc_combine, lib.orc_aux, lib.orc_forward_tokens):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle takes float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+    return a
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise ValueError(f"oracle {name}: bad argument")
+
+
+def logits(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """Router logits [T,E] fp32 (fp64 sum, one rounding)."""
+    x, w_router = _c(x), _c(w_router)
+    bias = _c(bias, np.float32)
+    T, H = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape == (E, H) and x.dtype == w_router.dtype
+    out = np.empty((T, E), np.float32)
+    _check(_load().orc_logits(T, H, E, _dtype_code(x), _p(x), _p(w_router), _p(bias), _p(out)),
+           "logits")
+    return out
+
+
+def route(lg: np.ndarray, k: int, norm: bool, forced_idx: np.ndarray | None = None):
+    """Softmax + top-k (+ renormalisation). Returns (idx int32 [T,k],
+    w float64 [T,k], probs float64 [T,E])."""
+    lg = _c(lg, np.float32)
+    T, E = lg.shape
+    forced_idx = _c(forced_idx, np.int32)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    probs = np.empty((T, E), np.float64)
+    _check(_load().orc_route(T, E, k, int(bool(norm)), _p(lg), _p(forced_idx), _p(idx), _p(w),
+                             _p(probs)), "route")
+    return idx, w, probs
+
+
+def dispatch(idx: np.ndarray, E: int):
+    """Counting sort of the pairs by expert. Returns (counts [E],
+    offsets [E+1], sorted_pair [P], pair_pos [P]), all int32."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.empty(T * k, np.int32)
+    pp = np.empty(T * k, np.int32)
+    _check(_load().orc_dispatch(T, E, k, _p(idx), _p(counts), _p(offsets), _p(sp), _p(pp)),
+           "dispatch")
+    return counts, offsets, sp, pp
+
+
+def expert_rows(x, w_gate, w_up, w_down, tok, ex, round_h: bool = False) -> np.ndarray:
+    """SwiGLU expert output (float64 [n,H]) for rows (token tok[r], expert ex[r])."""
+    x, w_gate, w_up, w_down = _c(x), _c(w_gate), _c(w_up), _c(w_down)
+    tok, ex = _c(tok, np.int32), _c(ex, np.int32)
+    H = x.shape[1]
+    E, I, H2 = w_gate.shape
+    assert H2 == H and w_up.shape == (E, I, H) and w_down.shape == (E, H, I)
+    assert len({a.dtype for a in (x, w_gate, w_up, w_down)}) == 1
+    n = tok.shape[0]
+    y = np.empty((n, H), np.float64)
+    _check(_load().orc_expert_rows(H, I, _dtype_code(x), _p(x), _p(w_gate), _p(w_up),
+                                   _p(w_down), n, _p(tok), _p(ex), int(round_h), _p(y)),
+           "expert_rows")
+    return y
+
+
+def combine(w: np.ndarray, y_pair: np.ndarray) -> np.ndarray:
+    """out[t] = sum_j w[t,j] * y_pair[t*k+j] (float64)."""
+    w = _c(w, np.float64)
+    y_pair = _c(y_pair, np.float64)
+    T, k = w.shape
+    H = y_pair.shape[1]
+    out = np.empty((T, H), np.float64)
+    _check(_load().orc_combine(T, H, k, _p(w), _p(y_pair), _p(out)), "combine")
+    return out
+
+
+def aux(counts: np.ndarray, probs: np.ndarray, k: int):
+    """Returns (f [E], P [E], aux) in float64."""
+    counts = _c(counts, np.int32)
+    probs = _c(probs, np.float64)
+    T, E = probs.shape
+    f = np.empty(E, np.float64)
+    P = np.empty(E, np.float64)
+    a = np.empty(1, np.float64)
+    _check(_load().orc_aux(T, E, k, _p(counts), _p(probs), _p(f), _p(P), _p(a)), "aux")
+    return f, P, float(a[0])
+
+
+def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool = False):
+    """Block forward for the listed tokens (all when None).
+
+    inp: dict with x, w_router, w_gate, w_up, w_down, logit_bias (None or
+    float32 [E]); cfg: an object with T, H, E, k, I, norm.
+    Returns dict(logits fp32 [n,E], idx [n,k], w [n,k] f64, out [n,H] f64)."""
+    x = _c(inp["x"])
+    wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
+    bias = _c(inp.get("logit_bias"), np.float32)
+    T, H = x.shape
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = _c(tokens, np.int32)
+    n = tokens.shape[0]
+    forced_idx = _c(forced_idx, np.int32)
+    k = cfg.k
+    lg = np.empty((n, cfg.E), np.float32)
+    idx = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    out = np.empty((n, H), np.float64)
+    _check(_load().orc_forward_tokens(T, H, cfg.E, k, cfg.I, int(bool(cfg.norm)),
+                                      _dtype_code(x), _p(x), _p(wr), _p(bias), _p(wg), _p(wu),
+                                      _p(wd), n, _p(tokens), _p(forced_idx), int(round_h),
+                                      _p(lg), _p(idx), _p(w), _p(out)), "forward_tokens")
+    return {"logits": lg, "idx": idx, "w": w, "out": out}

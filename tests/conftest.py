@@ -1,0 +1,20 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP library)")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    from oracle import oracle
+    if not os.path.exists(os.path.join(ROOT, "oracle", "libmoe_oracle.so")):
+        oracle.build()
+    return oracle

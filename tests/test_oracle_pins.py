@@ -1,0 +1,297 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: the pages'
+worked example and parameter table, brute force on tiny inputs, closed forms,
+library routines (numpy matmul / sort, scipy softmax) and invariants. The
+combination is chosen so that a dropped term, a wrong sign or index, or a
+transposed operand in any oracle step fails at least one test.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax
+
+from sparse_mixture_experts_40_amd.configs import MoEConfig, PREFILL128_BF16, WORKLOADS
+from sparse_mixture_experts_40_amd.inputs import as_f32, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _brute_topk(row, k):
+    # full sort of (value desc, index asc); Python float compare has -0.0 == 0.0
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+
+
+def _swiglu_np(x, wg, wu, wd):
+    """Dense SwiGLU MLP with numpy float64 matmuls: x [n,H] -> [n,H]."""
+    g = x @ wg.T
+    u = x @ wu.T
+    a = g / (1.0 + np.exp(-g)) * u
+    return a @ wd.T
+
+
+# --------------------------------------------------------------------- router
+
+
+def test_worked_example_top2(orc):
+    """[WHY-MOE] §1: eight scores, top-2 picks experts 6 and 2 (1-based)."""
+    g = json.load(open(os.path.join(GOLDEN, "why_moe_top2_example.json")))
+    lg = np.array([g["scores"]], np.float32)
+    want = [e - 1 for e in g["selected_experts_1based"]]
+    idx, w, probs = orc.route(lg, g["k"], norm=True)
+    assert idx[0].tolist() == want
+    # closed form: renormalised top-2 softmax weights are sigmoid of the logit gap
+    d = float(lg[0, want[0]]) - float(lg[0, want[1]])
+    assert w[0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-d)), rel=1e-12)
+    assert w[0, 1] == pytest.approx(1.0 / (1.0 + math.exp(d)), rel=1e-12)
+    # Mixtral variant: the plain softmax probabilities of the two winners
+    idx2, w2, _ = orc.route(lg, g["k"], norm=False)
+    p = sp_softmax(lg[0].astype(np.float64))
+    assert idx2[0].tolist() == want
+    np.testing.assert_allclose(w2[0], p[want], rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force_sort(orc, seed):
+    rng = _rng(seed)
+    for E in (1, 2, 3, 5, 8, 16):
+        T = int(rng.integers(1, 65))
+        if seed % 2 == 0:
+            lg = rng.standard_normal((T, E)).astype(np.float32)
+        else:  # heavy ties: few distinct values, including +0.0 and -0.0
+            vals = np.array([0.0, -0.0, 1.0, -1.0, 0.5], np.float32)
+            lg = vals[rng.integers(0, len(vals), (T, E))]
+        for k in range(1, E + 1):
+            idx, _, _ = orc.route(lg, k, norm=True)
+            for t in range(T):
+                assert idx[t].tolist() == _brute_topk(lg[t], k), (E, k, t, lg[t])
+
+
+def test_topk_adversarial_ties(orc):
+    E = 16
+    # all equal -> experts 0..k-1
+    lg = np.zeros((3, E), np.float32)
+    lg[1] = 2.5
+    lg[2] = -0.0
+    for k in (1, 4, 16):
+        idx, w, _ = orc.route(lg, k, norm=True)
+        assert (idx == np.arange(k)).all()
+        np.testing.assert_allclose(w, 1.0 / k, rtol=1e-15)
+    # duplicated maxima at high indices, +0/-0 mix
+    lg = np.full((1, E), -3.0, np.float32)
+    lg[0, [15, 9, 12]] = 7.0
+    lg[0, 4] = -0.0
+    lg[0, 2] = 0.0
+    idx, _, _ = orc.route(lg, 6, norm=False)
+    assert idx[0].tolist() == [9, 12, 15, 2, 4, 0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_renormalised_weights_sum_to_one_and_equal_topk_softmax(orc, seed):
+    """softmax -> top-k -> renormalise == softmax over the k selected logits
+    ([QWEN3-READ] forward code vs [LAB17] 第二阶段 / [MOE-128x8] router pseudocode)."""
+    rng = _rng(100 + seed)
+    T, E = 50, 32
+    lg = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    for k in (1, 2, 7, 32):
+        idx, w, probs = orc.route(lg, k, norm=True)
+        assert np.abs(w.sum(1) - 1.0).max() <= 1e-12
+        sel = np.take_along_axis(lg.astype(np.float64), idx.astype(np.int64), 1)
+        np.testing.assert_allclose(w, sp_softmax(sel, axis=1), rtol=1e-12)
+        # without renormalisation: the plain softmax probabilities, sum <= 1
+        idx2, w2, _ = orc.route(lg, k, norm=False)
+        assert (idx2 == idx).all()
+        full = sp_softmax(lg.astype(np.float64), axis=1)
+        np.testing.assert_allclose(w2, np.take_along_axis(full, idx.astype(np.int64), 1),
+                                   rtol=1e-12)
+        assert (w2.sum(1) <= 1.0 + 1e-12).all()
+        np.testing.assert_allclose(probs, full, rtol=1e-12)
+
+
+def test_forced_routing_weights(orc):
+    rng = _rng(7)
+    lg = rng.standard_normal((10, 8)).astype(np.float32)
+    forced = np.stack([rng.permutation(8)[:3] for _ in range(10)]).astype(np.int32)
+    idx, w, _ = orc.route(lg, 3, norm=True, forced_idx=forced)
+    assert (idx == forced).all()
+    full = sp_softmax(lg.astype(np.float64), axis=1)
+    pf = np.take_along_axis(full, forced.astype(np.int64), 1)
+    np.testing.assert_allclose(w, pf / pf.sum(1, keepdims=True), rtol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_logits_match_numpy_matmul(orc, dtype):
+    cfg = MoEConfig("t", T=33, H=192, E=12, k=3, I=64, norm=True, dtype=dtype, zipf_s=1.2)
+    d = make_inputs(cfg, seed=3, weights=False)
+    lg = orc.logits(d["x"], d["w_router"], d["logit_bias"])
+    ref = (as_f32(d["x"]).astype(np.float64) @ as_f32(d["w_router"]).astype(np.float64).T
+           + d["logit_bias"].astype(np.float64))
+    np.testing.assert_allclose(lg, ref.astype(np.float32), rtol=2e-7, atol=1e-7)
+    # transposed operand / dropped bias would fail:
+    assert not np.allclose(lg, (ref - d["logit_bias"]).astype(np.float32), atol=1e-3)
+
+
+# ------------------------------------------------------------------- dispatch
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_dispatch_matches_stable_sort(orc, seed):
+    rng = _rng(200 + seed)
+    E = int(rng.integers(1, 40))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(1, 300))
+    # distinct experts per token (as top-k gives), skewed toward low ids
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=None) for _ in range(T)]).astype(
+        np.int32)
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    flat = idx.ravel()
+    assert counts.sum() == T * k
+    assert (counts == np.bincount(flat, minlength=E)).all()
+    assert offsets[0] == 0 and offsets[E] == T * k
+    assert (np.diff(offsets) == counts).all()
+    assert (sp == np.argsort(flat, kind="stable")).all()
+    assert (sp[pp] == np.arange(T * k)).all()
+    for e in range(E):
+        grp = sp[offsets[e]:offsets[e + 1]]
+        assert (flat[grp] == e).all() and (np.diff(grp) > 0).all()
+
+
+# --------------------------------------------------------------------- expert
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_expert_rows_match_numpy(orc, dtype):
+    cfg = MoEConfig("t", T=9, H=64, E=3, k=2, I=128, norm=True, dtype=dtype)
+    d = make_inputs(cfg, seed=11)
+    x, wg, wu, wd = (as_f32(d[n]).astype(np.float64) for n in ("x", "w_gate", "w_up", "w_down"))
+    tok = np.array([0, 3, 8, 8, 5], np.int32)
+    ex = np.array([2, 0, 1, 2, 0], np.int32)
+    y = orc.expert_rows(d["x"], d["w_gate"], d["w_up"], d["w_down"], tok, ex)
+    for r in range(len(tok)):
+        ref = _swiglu_np(x[tok[r]][None], wg[ex[r]], wu[ex[r]], wd[ex[r]])[0]
+        np.testing.assert_allclose(y[r], ref, rtol=1e-10, atol=1e-12)
+    # the bf16-intermediate diagnostic mode stays within bf16 rounding of h
+    yb = orc.expert_rows(d["x"], d["w_gate"], d["w_up"], d["w_down"], tok, ex, round_h=True)
+    assert np.abs(yb - y).max() <= 2e-2 * np.sqrt((y ** 2).mean())
+
+
+def test_identical_experts_equal_one_dense_mlp_times_weight_sum(orc):
+    """All experts share weights: out = (sum_j w_j) * SwiGLU(x); with
+    renormalisation that is the textbook dense SwiGLU MLP."""
+    for norm in (True, False):
+        cfg = MoEConfig("t", T=20, H=64, E=6, k=3, I=64, norm=norm, dtype="f32")
+        d = make_inputs(cfg, seed=5)
+        for n in ("w_gate", "w_up", "w_down"):
+            d[n] = np.ascontiguousarray(np.broadcast_to(d[n][:1], d[n].shape))
+        r = orc.forward_tokens(d, cfg)
+        x = d["x"].astype(np.float64)
+        dense = _swiglu_np(x, d["w_gate"][0].astype(np.float64), d["w_up"][0].astype(np.float64),
+                           d["w_down"][0].astype(np.float64))
+        np.testing.assert_allclose(r["out"], r["w"].sum(1, keepdims=True) * dense, rtol=1e-10,
+                                   atol=1e-12)
+        if norm:
+            np.testing.assert_allclose(r["out"], dense, rtol=1e-10, atol=1e-12)
+
+
+def test_k1_is_argmax_expert_and_kE_is_soft_router(orc):
+    """k=1 with renormalisation: the argmax expert's MLP. k=E with
+    renormalisation: the dense soft router sum_e p_e MLP_e(x) ([WHY-MOE] §2.2)."""
+    cfg = MoEConfig("t", T=12, H=64, E=5, k=1, I=64, norm=True, dtype="f32")
+    d = make_inputs(cfg, seed=9)
+    x = d["x"].astype(np.float64)
+    W = {n: d[n].astype(np.float64) for n in ("w_gate", "w_up", "w_down")}
+    mlp = np.stack([_swiglu_np(x, W["w_gate"][e], W["w_up"][e], W["w_down"][e])
+                    for e in range(cfg.E)])  # [E,T,H]
+    lg = x @ d["w_router"].astype(np.float64).T
+    r1 = orc.forward_tokens(d, cfg)
+    am = lg.argmax(1)
+    np.testing.assert_allclose(r1["out"], mlp[am, np.arange(cfg.T)], rtol=1e-10, atol=1e-12)
+    cfgE = MoEConfig("t", T=12, H=64, E=5, k=5, I=64, norm=True, dtype="f32")
+    rE = orc.forward_tokens(d, cfgE)
+    p = sp_softmax(r1["logits"].astype(np.float64), axis=1)  # [T,E]
+    soft = np.einsum("te,eth->th", p, mlp)
+    np.testing.assert_allclose(rE["out"], soft, rtol=1e-9, atol=1e-12)
+
+
+def test_combine_matches_weighted_sum(orc):
+    rng = _rng(31)
+    T, k, H = 7, 3, 16
+    w = rng.random((T, k))
+    y = rng.standard_normal((T * k, H))
+    out = orc.combine(w, y)
+    ref = (w[:, :, None] * y.reshape(T, k, H)).sum(1)
+    np.testing.assert_allclose(out, ref, rtol=1e-13)
+
+
+# ------------------------------------------------------------------------ aux
+
+
+def test_zero_router_closed_form(orc):
+    """W_router = 0: all logits 0, experts 0..k-1 everywhere, w = 1/k (renorm)
+    or 1/E, n_e = T for e < k, P_e = 1/E and aux = 1."""
+    for norm in (True, False):
+        cfg = MoEConfig("t", T=40, H=64, E=10, k=4, I=64, norm=norm, dtype="f32")
+        d = make_inputs(cfg, seed=1)
+        d["w_router"] = np.zeros_like(d["w_router"])
+        r = orc.forward_tokens(d, cfg)
+        assert (r["logits"] == 0).all()
+        assert (r["idx"] == np.arange(cfg.k)).all()
+        np.testing.assert_allclose(r["w"], 1.0 / (cfg.k if norm else cfg.E), rtol=1e-15)
+        idx, _, probs = orc.route(r["logits"], cfg.k, norm)
+        counts, _, _, _ = orc.dispatch(idx, cfg.E)
+        assert counts.tolist() == [cfg.T] * cfg.k + [0] * (cfg.E - cfg.k)
+        f, P, aux = orc.aux(counts, probs, cfg.k)
+        np.testing.assert_allclose(P, 1.0 / cfg.E, rtol=1e-14)
+        assert aux == pytest.approx(1.0, abs=1e-14)
+
+
+def test_aux_brute_force_and_invariants(orc):
+    rng = _rng(77)
+    T, E, k = 64, 16, 4
+    lg = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx, _, probs = orc.route(lg, k, True)
+    counts, _, _, _ = orc.dispatch(idx, E)
+    f, P, aux = orc.aux(counts, probs, k)
+    assert f.sum() == pytest.approx(1.0, abs=1e-14)
+    assert P.sum() == pytest.approx(1.0, abs=1e-12)
+    full = sp_softmax(lg.astype(np.float64), axis=1)
+    ref = E * float((np.bincount(idx.ravel(), minlength=E) / (T * k) * full.mean(0)).sum())
+    assert aux == pytest.approx(ref, rel=1e-12)
+    # perfect balance: token t -> expert t (k=1), uniform probabilities -> aux = 1
+    counts1 = np.ones(E, np.int32)
+    f1, P1, aux1 = orc.aux(counts1, np.full((E, E), 1.0 / E), 1)
+    assert aux1 == pytest.approx(1.0, abs=1e-14)
+
+
+# --------------------------------------------------------------------- shapes
+
+
+def test_shapes_pinned_by_parameter_table():
+    """[MOE-128x8] parameter table: 4096*1536 per expert projection and
+    4096*128 for the router at the 128-expert configuration."""
+    g = json.load(open(os.path.join(GOLDEN, "moe128x8_param_table.json")))
+    c = PREFILL128_BF16
+    assert (c.E, c.k, c.I, c.H) == (g["config"]["num_experts"], g["config"]["num_experts_per_tok"],
+                                    g["config"]["moe_intermediate_size"],
+                                    g["config"]["hidden_size"])
+    assert c.I * c.H == g["params_per_expert"]["gate_proj"] == g["params_per_expert"]["up_proj"]
+    assert c.H * c.I == g["params_per_expert"]["down_proj"]
+    assert c.E * c.H == g["params_per_expert"]["gate"]
+    assert WORKLOADS["decode128_bf16"].E == c.E
+
+
+def test_generator_is_seeded_and_scaled():
+    cfg = WORKLOADS["tiny_f32"]
+    a, b = make_inputs(cfg), make_inputs(cfg)
+    for n in ("x", "w_router", "w_gate", "w_up", "w_down"):
+        assert (a[n] == b[n]).all()
+    assert abs(a["x"].std() - 1.0) < 0.05
+    assert abs(a["w_gate"].std() * math.sqrt(cfg.H) - 1.0) < 0.05
+    assert abs(a["w_down"].std() * math.sqrt(cfg.I) - 1.0) < 0.05
