@@ -29,9 +29,9 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
  *    row-major, 16-byte aligned. Weights use the nn.Linear [out, in] layout.
- *  - `dtype` (moe_config.dtype) is the element type of x, every weight, h,
- *    y_sorted and out. Logits, probabilities, weights and statistics are fp32;
- *    indices and counts are int32.
+ *  - `dtype` (moe_config.dtype) is the element type of x, every weight, h
+ *    and out. y_sorted (unweighted expert outputs), logits, probabilities,
+ *    weights and statistics are fp32; indices and counts are int32.
  *  - The library never allocates device memory, never synchronises the host
  *    with the device, and keeps no mutable global state: all work is enqueued
  *    on `stream` in call order. Scratch space is the caller's `workspace`,
@@ -78,7 +78,7 @@ typedef struct {
   int32_t intermediate;   /* I  (moe_intermediate_size) */
   int32_t norm_topk_prob; /* 1: renormalise the k weights (Qwen3); 0: use the
                              softmax probabilities as they are (Mixtral) */
-  moe_dtype dtype;        /* element type of x, weights, h, y_sorted, out */
+  moe_dtype dtype;        /* element type of x, weights, h, out */
 } moe_config;
 
 /* Load-balance outputs; every field may be NULL (then it is not written).
@@ -155,7 +155,7 @@ moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_
 
 /* Experts, second half: y_sorted[i, :] = W_down[e] h[i, :] for the rows of
  * every expert e.  h [T*k, I] dtype; w_down [E,H,I] dtype;
- * y_sorted [T*k, H] dtype out (fp32 accumulation, one rounding). */
+ * y_sorted [T*k, H] fp32 out (fp32 accumulation, not rounded to dtype). */
 moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
                            const void* w_down, void* y_sorted, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
@@ -171,7 +171,7 @@ moe_status moe_expert_swiglu(const moe_config* cfg, const void* x, const int32_t
 /* Combine: out[t, :] = sum_{j=0}^{k-1} topk_w[t,j] * y_sorted[pair_pos[t*k+j], :]
  * summed in fp32 in slot order j = 0..k-1 and rounded once to dtype; no
  * atomics. Replaces the index_add_ scatter of [QWEN3-READ] (forward code).
- *   y_sorted [T*k,H] dtype; pair_pos [T*k] int32; topk_w [T,k] fp32;
+ *   y_sorted [T*k,H] fp32; pair_pos [T*k] int32; topk_w [T,k] fp32;
  *   out [T,H] dtype. */
 moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_t* pair_pos,
                        const float* topk_w, void* out, hipStream_t stream);

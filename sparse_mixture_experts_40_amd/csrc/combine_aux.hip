@@ -1,0 +1,105 @@
+// combine_aux.hip — routing-weighted combine and load-balance statistics.
+//
+// Combine: [QWEN3-READ] "大模型-qwen3 MoE 详细解读" (cnblogs), forward code (each
+// expert output times its routing weight, added into the token's row) and §三
+// (inverse permutation back to token order). Here each token gathers its k
+// expert rows through pair_pos and sums them in slot order j = 0..k-1 in fp32,
+// one rounding to the output type: deterministic, no atomics.
+//
+// Statistics: [MOE-128x8] "MoE架构深度解析：128专家与8激活的智能路由" (csdn),
+// load-balancing section: f_e = n_e / (T*k), P_e = mean softmax probability,
+// aux = E * sum_e f_e P_e. Sums run in a fixed order.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k,
+                                                           const void* __restrict__ y,
+                                                           const int32_t* __restrict__ pair_pos,
+                                                           const float* __restrict__ topk_w,
+                                                           void* __restrict__ out) {
+  __shared__ int s_pos[16];
+  __shared__ float s_w[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < k) {
+    s_pos[tid] = pair_pos[(size_t)t * k + tid];
+    s_w[tid] = topk_w[(size_t)t * k + tid];
+  }
+  __syncthreads();
+  // y_sorted is fp32 for both element types; out is rounded once
+  const float* yf = static_cast<const float*>(y);
+  for (int c = tid; c < H / 4; c += kThreads) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(yf + (size_t)s_pos[j] * H + c * 4);
+      const float w = s_w[j];
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
+    if constexpr (BF16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + c * 4) =
+          make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + c * 4) = acc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void aux_kernel(int T, int E, int k,
+                                                       const int32_t* __restrict__ counts,
+                                                       const float* __restrict__ partials, int np,
+                                                       int32_t* __restrict__ c_out,
+                                                       float* __restrict__ f_out,
+                                                       float* __restrict__ p_out,
+                                                       float* __restrict__ aux_out) {
+  __shared__ double s_fp[kThreads];
+  const int e = threadIdx.x;
+  double fp = 0.0;
+  if (e < E) {
+    const int n = counts[e];
+    double s = 0.0;
+    for (int b = 0; b < np; ++b) s += (double)partials[(size_t)b * E + e];
+    const double f = (double)n / ((double)T * (double)k);
+    const double P = s / (double)T;
+    if (c_out) c_out[e] = n;
+    if (f_out) f_out[e] = (float)f;
+    if (p_out) p_out[e] = (float)P;
+    fp = f * P;
+  }
+  s_fp[e] = fp;
+  __syncthreads();
+  for (int d = kThreads / 2; d > 0; d >>= 1) {  // fixed-shape tree
+    if (e < d) s_fp[e] += s_fp[e + d];
+    __syncthreads();
+  }
+  if (e == 0 && aux_out) aux_out[0] = (float)((double)E * s_fp[0]);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
+                          const float* topk_w, void* out, hipStream_t s) {
+  if (c.dtype == MOE_DTYPE_BF16)
+    combine_kernel<true><<<c.num_tokens, kThreads, 0, s>>>(c.num_tokens, c.hidden, c.top_k, y,
+                                                           pair_pos, topk_w, out);
+  else
+    combine_kernel<false><<<c.num_tokens, kThreads, 0, s>>>(c.num_tokens, c.hidden, c.top_k, y,
+                                                            pair_pos, topk_w, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
+                      int n_partials, moe_aux_out out, hipStream_t s) {
+  aux_kernel<<<1, kThreads, 0, s>>>(c.num_tokens, c.num_experts, c.top_k, counts, prob_partials,
+                                    n_partials, out.counts, out.f, out.P, out.aux);
+  return hipGetLastError();
+}
+
+}  // namespace moe

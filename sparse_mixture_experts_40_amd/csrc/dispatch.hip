@@ -1,0 +1,136 @@
+// dispatch.hip — stable counting sort of the routing pairs by expert.
+//
+// Replaces the one-hot expert mask and the per-expert torch.where loop of
+// [QWEN3-READ] "大模型-qwen3 MoE 详细解读" (cnblogs), forward code, by the token
+// permutation (and its inverse) that its §三 describes for production kernels.
+//
+// Pairs p = t*k + j are cut into chunks of kChunk consecutive ids, one block
+// each:
+//   hist    : per-chunk LDS histogram (integer LDS atomics: exact, order-free)
+//   scan    : one block; per-expert totals, exclusive scan over experts, and
+//             the start of every (chunk, expert) run
+//   scatter : each chunk walks its pairs in ascending order, 256 at a time; a
+//             lane's rank among equal experts comes from 8 ballots (one per
+//             bit of the expert id), wave counts go through LDS, so pairs of an
+//             expert land in ascending pair order (a stable sort).
+// No device-to-host traffic; everything stays on the stream.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 2048;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int clamp_expert(int v, int E) { return v < 0 ? 0 : (v >= E ? E - 1 : v); }
+
+__global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(int P, int E,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 int32_t* __restrict__ hist) {
+  __shared__ int s_h[256];
+  const int tid = threadIdx.x;
+  s_h[tid] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk;
+  for (int i = tid; i < kChunk; i += kThreads) {
+    const int p = p0 + i;
+    if (p < P) atomicAdd(&s_h[clamp_expert(idx[p], E)], 1);
+  }
+  __syncthreads();
+  if (tid < E) hist[(size_t)blockIdx.x * E + tid] = s_h[tid];
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
+    int nchunks, int E, const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int s_c[256];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int b = 0; b < nchunks; ++b) tot += hist[(size_t)b * E + e];
+  s_c[e] = tot;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan over the 256 slots
+    const int add = (e >= d) ? s_c[e - d] : 0;
+    __syncthreads();
+    s_c[e] += add;
+    __syncthreads();
+  }
+  const int excl = s_c[e] - tot;
+  if (e < E) {
+    if (counts) counts[e] = tot;
+    if (offsets) offsets[e] = excl;
+    if (offsets && e == E - 1) offsets[E] = s_c[e];
+    if (base) {
+      int run = excl;
+      for (int b = 0; b < nchunks; ++b) {
+        base[(size_t)b * E + e] = run;
+        run += hist[(size_t)b * E + e];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
+    int P, int E, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  __shared__ int s_base[256];
+  __shared__ int s_wc[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < E) s_base[tid] = base[(size_t)blockIdx.x * E + tid];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
+  __syncthreads();
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  for (int it = 0; it < kChunk / kThreads; ++it) {
+    const int p = blockIdx.x * kChunk + it * kThreads + tid;
+    const bool valid = p < P;
+    const int v = valid ? clamp_expert(idx[p], E) : 0;
+    unsigned long long same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (v >> b) & 1;
+      const unsigned long long bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (valid && rank == 0) s_wc[wave][v] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = s_base[v] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wc[w][v];
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+    }
+    __syncthreads();
+    if (tid < E) {
+      s_base[tid] += s_wc[0][tid] + s_wc[1][tid] + s_wc[2][tid] + s_wc[3][tid];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int dispatch_num_chunks(const moe_config& c) {
+  const long P = (long)c.num_tokens * c.top_k;
+  return (int)((P + kChunk - 1) / kChunk);
+}
+
+hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                           int32_t* hist, int32_t* base, bool scatter, hipStream_t s) {
+  const int P = c.num_tokens * c.top_k, E = c.num_experts;
+  const int nch = dispatch_num_chunks(c);
+  dispatch_hist_kernel<<<nch, kThreads, 0, s>>>(P, E, topk_idx, hist);
+  dispatch_scan_kernel<<<1, kThreads, 0, s>>>(nch, E, hist, scatter ? base : nullptr, counts,
+                                              offsets);
+  if (scatter)
+    dispatch_scatter_kernel<<<nch, kThreads, 0, s>>>(P, E, topk_idx, base, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

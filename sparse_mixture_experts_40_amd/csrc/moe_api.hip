@@ -1,0 +1,236 @@
+// moe_api.hip — the C ABI of include/moe.h: argument checks, workspace
+// carving and the launch sequence on the caller's stream. No allocation, no
+// host synchronisation, no global state.
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Bump carver over the caller's workspace (base == nullptr: size only).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) & ~(kAlign - 1);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+size_t elem_bytes(const moe_config& c) { return c.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+moe_status check_config(const moe_config* cfg) {
+  if (!cfg) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config& c = *cfg;
+  if (c.num_tokens < 1 || c.hidden < 1 || c.num_experts < 1 || c.top_k < 1 ||
+      c.intermediate < 1 || c.top_k > c.num_experts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c.dtype != MOE_DTYPE_F32 && c.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.norm_topk_prob != 0 && c.norm_topk_prob != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.num_experts > 256 || c.top_k > 16) return MOE_ERR_UNSUPPORTED;
+  if (c.hidden % 64 != 0 || c.intermediate % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long P = (long long)c.num_tokens * c.top_k;
+  const long long wide = c.hidden > c.intermediate ? c.hidden : c.intermediate;
+  if (P >= (1LL << 31) || P * wide >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)c.num_experts * c.intermediate * c.hidden >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace regions. Each entry point carves the prefix it needs, in order.
+struct Layout {
+  int32_t* hist;
+  int32_t* base;
+  float* partials;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int32_t* idx;
+  float* w;
+  void* h;
+  void* y;
+  size_t dispatch_end, aux_end, layer_end;
+};
+
+Layout carve(const moe_config& c, void* ws) {
+  Carver cv(ws);
+  Layout L{};
+  const size_t P = (size_t)c.num_tokens * c.top_k, E = c.num_experts;
+  L.hist = cv.take<int32_t>((size_t)dispatch_num_chunks(c) * E);
+  L.base = cv.take<int32_t>((size_t)dispatch_num_chunks(c) * E);
+  L.dispatch_end = cv.off;
+  L.partials = cv.take<float>((size_t)router_num_blocks(c) * E);
+  L.counts = cv.take<int32_t>(E);
+  L.offsets = cv.take<int32_t>(E + 1);
+  L.idx = cv.take<int32_t>(P);
+  L.w = cv.take<float>(P);
+  L.aux_end = cv.off;
+  L.sorted_pair = cv.take<int32_t>(P);
+  L.pair_pos = cv.take<int32_t>(P);
+  L.h = cv.take<char>(P * c.intermediate * elem_bytes(c));
+  L.y = cv.take<float>(P * c.hidden);  // y_sorted is fp32
+  L.layer_end = cv.off;
+  return L;
+}
+
+// gate/up + down alone need only h
+size_t swiglu_bytes(const moe_config& c) {
+  Carver cv(nullptr);
+  cv.take<char>((size_t)c.num_tokens * c.top_k * c.intermediate * elem_bytes(c));
+  return cv.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return carve(*cfg, nullptr).layer_end;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_router,
+                           const float* logit_bias, float* logits, int32_t* topk_idx,
+                           float* topk_w, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (x ? !w_router : !logits) return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_router(*cfg, x, w_router, x ? logit_bias : nullptr, logits,
+                                logits != nullptr, topk_idx, topk_w, nullptr, true, stream));
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !expert_counts || !expert_offsets || !sorted_pair || !pair_pos)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.dispatch_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return launched(launch_dispatch(*cfg, topk_idx, expert_counts, expert_offsets, sorted_pair,
+                                  pair_pos, L.hist, L.base, true, stream));
+}
+
+moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_t* sorted_pair,
+                              const int32_t* expert_offsets, const void* w_gate,
+                              const void* w_up, void* h, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !sorted_pair || !expert_offsets || !w_gate || !w_up || !h)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_gate_up(*cfg, x, sorted_pair, expert_offsets, w_gate, w_up, h, stream));
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                           const void* w_down, void* y_sorted, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !w_down || !y_sorted) return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_down(*cfg, h, expert_offsets, w_down, y_sorted, stream));
+}
+
+moe_status moe_expert_swiglu(const moe_config* cfg, const void* x, const int32_t* sorted_pair,
+                             const int32_t* expert_offsets, const void* w_gate,
+                             const void* w_up, const void* w_down, void* y_sorted,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !sorted_pair || !expert_offsets || !w_gate || !w_up || !w_down || !y_sorted)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < swiglu_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  st = launched(launch_gate_up(*cfg, x, sorted_pair, expert_offsets, w_gate, w_up, workspace,
+                               stream));
+  if (st != MOE_OK) return st;
+  return launched(launch_down(*cfg, workspace, expert_offsets, w_down, y_sorted, stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_t* pair_pos,
+                       const float* topk_w, void* out, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!y_sorted || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_combine(*cfg, y_sorted, pair_pos, topk_w, out, stream));
+}
+
+moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
+                         moe_aux_out out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.aux_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!out.counts && !out.f && !out.P && !out.aux) return MOE_OK;
+  // per-block softmax sums from the logits (selection skipped)
+  st = launched(launch_router(*cfg, nullptr, nullptr, nullptr, const_cast<float*>(logits), false,
+                              L.idx, L.w, L.partials, false, stream));
+  if (st != MOE_OK) return st;
+  // expert counts from the given selection (histogram + scan only)
+  st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
+                                nullptr, false, stream));
+  if (st != MOE_OK) return st;
+  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg), out, stream));
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logit_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* out, float* router_logits,
+                             int32_t* topk_idx, float* topk_w, moe_aux_out aux,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_config& c = *cfg;
+  int32_t* idx = topk_idx ? topk_idx : L.idx;
+  float* w = topk_w ? topk_w : L.w;
+  const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
+
+  st = launched(launch_router(c, x, w_router, logit_bias, router_logits, router_logits != nullptr,
+                              idx, w, want_aux ? L.partials : nullptr, true, stream));
+  if (st != MOE_OK) return st;
+  st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
+                                L.base, true, stream));
+  if (st != MOE_OK) return st;
+  st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
+  if (st != MOE_OK) return st;
+  st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream));
+  if (st != MOE_OK) return st;
+  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
+  if (st != MOE_OK) return st;
+  if (want_aux)
+    st = launched(launch_aux(c, L.counts, L.partials, router_num_blocks(c), aux, stream));
+  return st;
+}
+
+}  // extern "C"

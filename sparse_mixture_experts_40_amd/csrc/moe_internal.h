@@ -1,0 +1,109 @@
+// moe_internal.h — shared device helpers and kernel-launcher declarations of
+// the gfx950 MoE library. Not part of the public ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its 16-bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite by contract).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// XCD-aware block order. Hardware block ids are dealt round-robin to the 8
+// XCDs (id b runs on XCD b % 8, each XCD with its own L2). Map the first
+// 8*floor(R/8) ids so that each XCD gets one contiguous range of logical tiles
+// (neighbouring tiles share operands in that XCD's L2); the tail is identity.
+// A bijection on [0, R).
+__device__ __forceinline__ int xcd_remap(int b, int R) {
+  const int full = R & ~7;
+  return b < full ? (b & 7) * (full >> 3) + (b >> 3) : b;
+}
+
+// Row-block tiling of the expert-grouped rows: expert e owns rows
+// [offsets[e], offsets[e+1]) and ceil(n_e / BM) row tiles.
+// row_tile_scan fills s_scan (2*E+2 ints of LDS): [0,E) inclusive scan of the
+// tile counts, [E+1, 2E+2) the offsets; returns the total number of row tiles.
+// Must be called by all threads of a block of at least E threads (E <= 256).
+template <int BM>
+__device__ int row_tile_scan(const int32_t* __restrict__ offsets, int E, int* s_scan) {
+  const int e = threadIdx.x;
+  for (int i = e; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  __syncthreads();
+  if (e < E) s_scan[e] = (s_scan[E + 2 + e] - s_scan[E + 1 + e] + BM - 1) / BM;
+  __syncthreads();
+  for (int d = 1; d < E; d <<= 1) {  // Hillis-Steele inclusive scan
+    const int add = (e < E && e >= d) ? s_scan[e - d] : 0;
+    __syncthreads();
+    if (e < E) s_scan[e] += add;
+    __syncthreads();
+  }
+  return s_scan[E - 1];
+}
+
+// (expert, first row, end row) of row tile `tile_id` < total.
+template <int BM>
+__device__ void row_tile_find(const int* s_scan, int E, int tile_id, int& expert, int& row0,
+                              int& row_end) {
+  int lo = 0, hi = E - 1;  // first expert whose inclusive tile count exceeds tile_id
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s_scan[mid] > tile_id) hi = mid; else lo = mid + 1;
+  }
+  expert = lo;
+  const int before = (lo == 0) ? 0 : s_scan[lo - 1];
+  row0 = s_scan[E + 1 + lo] + (tile_id - before) * BM;
+  row_end = s_scan[E + 2 + lo];
+}
+
+// ---- launchers (defined in the .hip files; all return hipGetLastError()) ----
+
+// Router: logits (MFMA for bf16, FMA for fp32) + softmax + top-k + weights.
+// x == nullptr: logits are read from `logits`. prob_partials (nullable):
+// [ceil(T/64), E] per-block sums of the full softmax. do_select == 0 skips the
+// top-k (only partials are produced).
+hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
+                         const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
+                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s);
+int router_num_blocks(const moe_config& c);
+
+// Dispatch: histogram per chunk, scan, stable scatter.
+int dispatch_num_chunks(const moe_config& c);
+hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                           int32_t* hist, int32_t* base, bool scatter, hipStream_t s);
+
+// Expert GEMMs.
+hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,
+                          const int32_t* offsets, const void* w_gate, const void* w_up, void* h,
+                          hipStream_t s);
+hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offsets,
+                       const void* w_down, void* y, hipStream_t s);
+
+// Combine and statistics.
+hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
+                          const float* topk_w, void* out, hipStream_t s);
+hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
+                      int n_partials, moe_aux_out out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,289 @@
+// router.hip — router linear + fp32 softmax + wavefront top-k + weights.
+//
+// [QWEN3-READ] "大模型-qwen3 MoE 详细解读" (cnblogs), forward code: gate linear
+// without bias, softmax over the experts in fp32, top-k, and (Qwen3 only)
+// division of the k weights by their sum. [LAB17] 第二阶段 实现流程 steps 1-3.
+//
+// One block of 256 threads (4 wave64) owns 64 tokens:
+//  1. logits tile [64 tokens x E] — bf16: MFMA 32x32x16 with the router rows
+//     as the A operand and the tokens as B, K staged through swizzled LDS;
+//     fp32: plain FMA dot products. (x == nullptr: the tile is read.)
+//  2. each wave takes 16 tokens; lanes hold experts e = lane + 64q. Softmax
+//     max/sum are xor-butterfly reductions (every lane ends with the same
+//     bits). Top-k is k rounds of a wave max over 64-bit keys
+//     (order-preserving fp32 bits, then 0xFFFF - e), so equal logits go to
+//     the lower expert index; -0.0 is folded into +0.0 first.
+//  3. per-block sums of the full softmax over the block's tokens (fixed order)
+//     for the load-balance statistic P_e.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTok = 64;       // tokens per block
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kBK = 64;        // K step (elements)
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;  // -0.0 -> +0.0
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(v, m, 64);
+    v = (o > v) ? o : v;
+  }
+  return v;
+}
+
+// swizzled [rows][64] bf16 tile: 16-byte chunk c of row r lives at chunk c ^ (r & 7)
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+
+// Logits tile by bf16 MFMA into s_log[t * ls + e] (+ bias).
+__device__ void router_logits_mfma(int T, int H, int E, int t0, const uint16_t* __restrict__ x,
+                                   const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+                                   char* smem, float* s_log, int ls) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int EP = (E + 31) & ~31;
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(smem);  // [64][64]
+  uint16_t* s_w = s_x + kTok * kBK;                     // [EP][64]
+  const int ntiles = (EP / 32) * 2;                     // (expert block, token block)
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+
+  uint4 rx[2], rw[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
+      rx[i] = make_uint4(0, 0, 0, 0);
+      if (t0 + row < T)
+        rx[i] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + row) * H + k0 + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
+      rw[i] = make_uint4(0, 0, 0, 0);
+      if (row < E) rw[i] = *reinterpret_cast<const uint4*>(wr + (size_t)row * H + k0 + ch * 8);
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
+      *reinterpret_cast<uint4*>(s_x + swz(row, ch)) = rx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
+      if (row < EP) *reinterpret_cast<uint4*>(s_w + swz(row, ch)) = rw[i];
+    }
+  };
+
+  const int nk = H / kBK;
+  gload(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();  // previous compute done with the tile
+    sstore();
+    __syncthreads();
+    if (kt + 1 < nk) gload((kt + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tile = q * 4 + wave;
+        if (tile < ntiles) {
+          const int eb = tile >> 1, tb = tile & 1;
+          const int er = eb * 32 + (lane & 31), tr = tb * 32 + (lane & 31);
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(s_x + swz(tr, ch));
+          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // tiles dead; s_log aliases them
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tile = q * 4 + wave;
+    if (tile < ntiles) {
+      const int eb = tile >> 1, tb = tile & 1;
+      const int t = tb * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = eb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (e < E) s_log[t * ls + e] = acc[q][r] + (bias ? bias[e] : 0.0f);
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void router_kernel(
+    int T, int H, int E, int k, int norm, const void* __restrict__ x, const void* __restrict__ wr,
+    const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partials,
+    int do_select) {
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kTok;
+  const int ls = ((E + 31) & ~31) + 1;
+  float* s_log = reinterpret_cast<float*>(smem);  // [64][ls]
+
+  if (logits_in) {
+    for (int i = tid; i < kTok * E; i += kThreads) {
+      const int t = i / E, e = i - t * E;
+      s_log[t * ls + e] = (t0 + t < T) ? logits_in[(size_t)(t0 + t) * E + e] : 0.0f;
+    }
+  } else if constexpr (BF16) {
+    router_logits_mfma(T, H, E, t0, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(wr), bias, smem, s_log, ls);
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    const float* wf = static_cast<const float*>(wr);
+    for (int i = tid; i < kTok * E; i += kThreads) {
+      const int t = i / E, e = i - t * E;
+      float s = 0.0f;
+      if (t0 + t < T) {
+        for (int h = 0; h < H; ++h) s = fmaf(xf[(size_t)(t0 + t) * H + h], wf[(size_t)e * H + h], s);
+        if (bias) s += bias[e];
+      }
+      s_log[t * ls + e] = s;
+    }
+  }
+  __syncthreads();
+
+  const int EQ = (E + 63) >> 6;  // <= 4 experts per lane
+  float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int tt = 0; tt < kTok / 4; ++tt) {
+    const int t = wave * (kTok / 4) + tt, gt = t0 + t;
+    if (gt >= T) break;  // wave-uniform
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = (q < EQ && e < E) ? s_log[t * ls + e] : -INFINITY;
+      if (logits_out && q < EQ && e < E) logits_out[(size_t)gt * E + e] = v[q];
+    }
+    const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    float ex[4], s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      ex[q] = (q < EQ && e < E) ? expf(v[q] - m) : 0.0f;
+      s += ex[q];
+    }
+    s = wave_sum(s);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pacc[q] += ex[q] * inv;
+
+    if (do_select) {
+      uint32_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        key[q] = (q < EQ && e < E) ? order_key(v[q]) : 0u;
+      }
+      int my_e = 0;
+      float my_p = 0.0f, psum = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned long long cand =
+              (static_cast<unsigned long long>(key[q]) << 32) | (0xFFFFu - (unsigned)(lane + 64 * q));
+          best = (key[q] != 0u && cand > best) ? cand : best;
+        }
+        best = wave_max_u64(best);
+        const int ej = 0xFFFF - static_cast<int>(best & 0xFFFFull);
+        if ((ej & 63) == lane) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == (ej >> 6)) key[q] = 0u;
+        }
+        const float pj = expf(key_value(static_cast<uint32_t>(best >> 32)) - m) * inv;
+        psum += pj;
+        if (lane == j) {
+          my_e = ej;
+          my_p = pj;
+        }
+      }
+      if (lane < k) {
+        topk_idx[(size_t)gt * k + lane] = my_e;
+        topk_w[(size_t)gt * k + lane] = norm ? my_p / psum : my_p;
+      }
+    }
+  }
+
+  if (partials) {
+    __syncthreads();  // every wave is done with s_log
+    float* s_part = reinterpret_cast<float*>(smem);  // [4][256]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      if (e < 256) s_part[wave * 256 + e] = pacc[q];
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads)
+      partials[(size_t)blockIdx.x * E + e] =
+          ((s_part[e] + s_part[256 + e]) + s_part[512 + e]) + s_part[768 + e];
+  }
+}
+
+}  // namespace
+
+int router_num_blocks(const moe_config& c) { return (c.num_tokens + kTok - 1) / kTok; }
+
+hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
+                         const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
+                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s) {
+  const int E = c.num_experts;
+  const int EP = (E + 31) & ~31;
+  size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
+  if (x && c.dtype == MOE_DTYPE_BF16) {
+    const size_t tiles = (size_t)(kTok + EP) * kBK * sizeof(uint16_t);
+    if (tiles > lds) lds = tiles;
+  }
+  if (lds < 4 * 256 * sizeof(float)) lds = 4 * 256 * sizeof(float);
+  const dim3 grid(router_num_blocks(c)), block(kThreads);
+  const float* lin = x ? nullptr : logits;
+  float* lout = (x && logits_out) ? logits : nullptr;
+  if (c.dtype == MOE_DTYPE_BF16)
+    router_kernel<true><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
+                                                 c.norm_topk_prob, x, w_router, bias, lin, lout,
+                                                 topk_idx, topk_w, prob_partials, do_select);
+  else
+    router_kernel<false><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
+                                                  c.norm_topk_prob, x, w_router, bias, lin, lout,
+                                                  topk_idx, topk_w, prob_partials, do_select);
+  return hipGetLastError();
+}
+
+}  // namespace moe

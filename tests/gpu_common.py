@@ -1,0 +1,105 @@
+"""Shared helpers of the GPU parity tests (inputs to the device, tolerances,
+sampled comparisons against the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from sparse_mixture_experts_40_amd import binding
+from sparse_mixture_experts_40_amd.inputs import as_f32
+
+# Tolerances of the block output: fp32 workloads max|d| <= 1e-4; bf16 workloads
+# (bf16 inputs, fp32 accumulation) max|d| <= 2e-2 * RMS(oracle output), on top
+# of the rounding of a bf16 output to its nearest value (at most half a bf16
+# ulp <= 2^-8 |ref|), which no bf16 output can avoid.
+F32_MAX_ABS = 1e-4
+BF16_REL_RMS = 2e-2
+BF16_HALF_ULP_REL = 2.0 ** -8
+# index mismatches are allowed only where the oracle's k-th and (k+1)-th
+# logits are closer than this
+TIE_GAP = 1e-3
+
+
+def dev(a):
+    return binding.to_device(a)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy()
+    return t.numpy()
+
+
+def kth_gap(logits_row: np.ndarray, k: int) -> float:
+    """Gap between the k-th and (k+1)-th largest logits (inf when k == E)."""
+    s = np.sort(logits_row.astype(np.float64))[::-1]
+    return float(s[k - 1] - s[k]) if k < len(s) else float("inf")
+
+
+def check_output(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out",
+                 bf16_rounded: bool = True):
+    """Element-wise tolerance check; returns (max|d|/RMS, RMS(d)/RMS)."""
+    d = np.abs(got.astype(np.float64) - ref)
+    rms = float(np.sqrt((ref ** 2).mean())) if ref.size else 0.0
+    if dtype == "f32":
+        assert d.max(initial=0.0) <= F32_MAX_ABS, f"{what}: max|d| {d.max():.3e} > {F32_MAX_ABS}"
+    else:
+        allow = BF16_REL_RMS * rms + (BF16_HALF_ULP_REL * np.abs(ref) if bf16_rounded else 0.0)
+        bad = d > allow
+        assert not bad.any(), (
+            f"{what}: {int(bad.sum())} elements over tolerance; max|d| {d.max():.3e}, "
+            f"RMS {rms:.3e}, worst excess {(d - allow).max():.3e}")
+    if not ref.size:
+        return 0.0, 0.0
+    return float(d.max() / rms), float(np.sqrt((d ** 2).mean()) / rms)
+
+
+def check_selection_row(lg, gpu_row, ref_row, k, token=None):
+    """A GPU selection that differs from the oracle's is valid only on near
+    ties (see compare_selection)."""
+    lg = np.asarray(lg, np.float64)
+    if set(gpu_row.tolist()) == set(ref_row.tolist()):
+        for j in np.where(ref_row != gpu_row)[0]:
+            assert abs(lg[gpu_row[j]] - lg[ref_row[j]]) < TIE_GAP, (token, j)
+        return
+    gap = kth_gap(lg, k)
+    assert gap < TIE_GAP, (f"token {token}: GPU experts {gpu_row} vs oracle {ref_row} with "
+                           f"k-th logit gap {gap:.2e}")
+    kth = np.sort(lg)[::-1][k - 1]
+    assert len(set(gpu_row.tolist())) == k
+    assert (lg[gpu_row] >= kth - TIE_GAP).all()
+
+
+def compare_selection(orc, cfg, inp, tokens, gpu_idx, gpu_w):
+    """Oracle forward of `tokens`, then the GPU's selection against it.
+
+    Equal expert sets are required, except on near ties: the oracle's k-th and
+    (k+1)-th logits closer than TIE_GAP (the GPU's set must then still be a
+    near-top-k: every chosen expert's oracle logit within TIE_GAP of the
+    oracle's k-th logit). Within an equal set, a different slot order is only
+    allowed between experts whose oracle logits are closer than TIE_GAP.
+    Weights are compared per expert. Returns (oracle result, mask of the tokens
+    whose expert set matches, so their outputs are comparable)."""
+    r = orc.forward_tokens(inp, cfg, tokens=tokens)
+    same_set = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(r["idx"], gpu_idx)],
+                        dtype=bool)
+    for i in np.where((r["idx"] != gpu_idx).any(1))[0]:
+        check_selection_row(r["logits"][i], gpu_idx[i], r["idx"][i], cfg.k, tokens[i])
+    order_g = np.argsort(gpu_idx[same_set], axis=1)
+    order_o = np.argsort(r["idx"][same_set], axis=1)
+    np.testing.assert_allclose(np.take_along_axis(gpu_w[same_set], order_g, 1),
+                               np.take_along_axis(r["w"][same_set], order_o, 1), rtol=0, atol=1e-4)
+    return r, same_set
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    pick = set([0, T - 1, T // 2]) | set(rng.choice(T, n - 3, replace=False).tolist())
+    return np.array(sorted(pick)[:n], dtype=np.int32)
+
+
+def x_f64(inp):
+    return as_f32(inp["x"]).astype(np.float64)

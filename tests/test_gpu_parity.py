@@ -1,0 +1,286 @@
+"""GPU parity of every stage and of the whole block against the CPU oracle, at
+sizes the oracle finishes in seconds (several tiles, ragged tails), plus edge
+cases and determinism. All calls go through the C ABI (libmoe.so)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_mixture_experts_40_amd import binding
+from sparse_mixture_experts_40_amd.configs import MoEConfig, WORKLOADS
+from sparse_mixture_experts_40_amd.inputs import make_inputs
+
+from gpu_common import check_output, check_selection_row, compare_selection, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    binding.load()
+    assert torch.cuda.is_available()
+    yield
+
+
+def _i32(t):
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.int32)).cuda()
+
+
+def _f32(t):
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).cuda()
+
+
+# ------------------------------------------------------------------ router
+
+
+ROUTER_SHAPES = [(1, 8, 2), (64, 8, 2), (100, 64, 8), (257, 128, 8), (130, 256, 16), (77, 40, 3),
+                 (33, 16, 16), (65, 1, 1), (50, 200, 1)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTER_SHAPES)
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("ties", [False, True])
+def test_router_topk_bitexact_on_oracle_logits(orc, T, E, k, norm, ties):
+    rng = np.random.default_rng(T * 1000 + E * 10 + k)
+    if ties:
+        vals = np.array([0.0, -0.0, 1.5, -1.5, 0.25, 3.0], np.float32)
+        lg = vals[rng.integers(0, len(vals), (T, E))]
+    else:
+        lg = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx_ref, w_ref, _ = orc.route(lg, k, norm)
+    cfg = MoEConfig("t", T=T, H=64, E=E, k=k, I=64, norm=norm, dtype="bf16")
+    c = binding.make_config(cfg)
+    g_lg = _f32(lg)
+    g_idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    binding.router_topk(c, None, None, None, g_lg, g_idx, g_w)
+    torch.cuda.synchronize()
+    assert (host(g_idx) == idx_ref).all()
+    np.testing.assert_allclose(host(g_w), w_ref, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,E,k,zipf", [(64, 128, 8, 2, 0.0), (300, 512, 64, 8, 0.0),
+                                          (129, 1024, 128, 8, 1.2), (70, 256, 256, 4, 0.0),
+                                          (5, 64, 40, 3, 1.2)])
+def test_router_from_x_matches_oracle(orc, dtype, T, H, E, k, zipf):
+    cfg = MoEConfig("t", T=T, H=H, E=E, k=k, I=64, norm=True, dtype=dtype, zipf_s=zipf)
+    inp = make_inputs(cfg, seed=2, weights=False)
+    lg_ref = orc.logits(inp["x"], inp["w_router"], inp["logit_bias"])
+    idx_ref, w_ref, _ = orc.route(lg_ref, k, True)
+    c = binding.make_config(cfg)
+    g_lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    g_idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    binding.router_topk(c, dev(inp["x"]), dev(inp["w_router"]), dev(inp["logit_bias"]), g_lg,
+                        g_idx, g_w)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(g_lg), lg_ref, rtol=0, atol=2e-5)
+    gi = host(g_idx)
+    for t in np.where((gi != idx_ref).any(1))[0]:
+        check_selection_row(lg_ref[t], gi[t], idx_ref[t], k, t)
+    same = (gi == idx_ref).all(1)
+    np.testing.assert_allclose(host(g_w)[same], w_ref[same], rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------- dispatch
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (1, 8, 2), (64, 8, 2), (1000, 64, 8),
+                                   (1031, 256, 16), (4096, 8, 2), (16384, 128, 8), (3, 200, 7)])
+def test_dispatch_bitexact(orc, T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    # distinct experts per token, skewed toward low ids
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    cfg = MoEConfig("t", T=T, H=64, E=E, k=k, I=64, norm=True, dtype="bf16")
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    g = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+    binding.dispatch(c, _i32(idx), *g, ws)
+    torch.cuda.synchronize()
+    for got, ref, name in zip(g, (counts, offsets, sp, pp), ("counts", "offsets", "sorted", "pos")):
+        assert (host(got) == ref).all(), name
+
+
+# ------------------------------------------------------------------ experts
+
+
+EXPERT_SHAPES = [  # (T, H, E, k, I)
+    (64, 128, 8, 2, 256),
+    (700, 512, 8, 2, 1024),
+    (300, 256, 64, 8, 128),
+    (41, 192, 40, 3, 320),
+    (9, 64, 4, 1, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,E,k,I", EXPERT_SHAPES)
+def test_expert_swiglu_matches_oracle(orc, dtype, T, H, E, k, I):
+    cfg = MoEConfig("t", T=T, H=H, E=E, k=k, I=I, norm=True, dtype=dtype)
+    inp = make_inputs(cfg, seed=4)
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    tok = sp // k
+    ex = np.repeat(np.arange(E, dtype=np.int32), counts)
+    y_ref = orc.expert_rows(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], tok, ex)
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    y = torch.empty(T * k, H, dtype=torch.float32, device="cuda")  # fp32 for both dtypes
+    binding.expert_swiglu(c, dev(inp["x"]), _i32(sp), _i32(offsets), dev(inp["w_gate"]),
+                          dev(inp["w_up"]), dev(inp["w_down"]), y, ws)
+    torch.cuda.synchronize()
+    check_output(host(y), y_ref, dtype, "y_sorted", bf16_rounded=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_matches_oracle(orc, dtype):
+    T, H, E, k = 300, 256, 16, 4
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    _, w_ref, _ = orc.route(lg, k, True, forced_idx=idx)
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    y32 = rng.standard_normal((T * k, H)).astype(np.float32)  # y_sorted is fp32
+    ref = orc.combine(w_ref.astype(np.float32), y32.astype(np.float64)[pp])
+    cfg = MoEConfig("t", T=T, H=H, E=E, k=k, I=64, norm=True, dtype=dtype)
+    c = binding.make_config(cfg)
+    out = torch.empty(T, H, dtype=binding.TORCH_DTYPE[dtype], device="cuda")
+    binding.combine(c, dev(y32), _i32(pp), _f32(w_ref), out)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    if dtype == "bf16":  # fp32 sum, one rounding to bf16: within half a bf16 ulp (+ fp32 sum)
+        assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+    else:
+        assert np.abs(got - ref).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------- aux
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1000, 128, 8), (77, 256, 16), (1, 4, 4)])
+def test_aux_stats_matches_oracle(orc, T, E, k):
+    rng = np.random.default_rng(E)
+    lg = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    idx, _, probs = orc.route(lg, k, True)
+    counts, _, _, _ = orc.dispatch(idx, E)
+    f, P, aux = orc.aux(counts, probs, k)
+    cfg = MoEConfig("t", T=T, H=64, E=E, k=k, I=64, norm=True, dtype="bf16")
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    g = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+             f=torch.empty(E, dtype=torch.float32, device="cuda"),
+             P=torch.empty(E, dtype=torch.float32, device="cuda"),
+             aux=torch.empty(1, dtype=torch.float32, device="cuda"))
+    binding.aux_stats(c, _f32(lg), _i32(idx), ws, **g)
+    torch.cuda.synchronize()
+    assert (host(g["counts"]) == counts).all()
+    np.testing.assert_allclose(host(g["f"]), f, rtol=1e-7)
+    np.testing.assert_allclose(host(g["P"]), P, rtol=2e-6, atol=1e-9)
+    assert host(g["aux"])[0] == pytest.approx(aux, rel=2e-6)
+
+
+# ---------------------------------------------------------------- end to end
+
+
+E2E = [
+    WORKLOADS["tiny_f32"],
+    MoEConfig("mixtral_like", T=700, H=512, E=8, k=2, I=1024, norm=False, dtype="bf16"),
+    MoEConfig("finegrained_like", T=1000, H=256, E=64, k=8, I=128, norm=True, dtype="bf16"),
+    MoEConfig("e128_like", T=2500, H=512, E=128, k=8, I=192, norm=True, dtype="bf16"),
+    MoEConfig("decode_like", T=64, H=512, E=128, k=8, I=256, norm=True, dtype="bf16",
+              zipf_s=1.2),
+    MoEConfig("e256_k16", T=300, H=128, E=256, k=16, I=64, norm=True, dtype="bf16"),
+    MoEConfig("odd_sizes", T=41, H=192, E=40, k=3, I=320, norm=False, dtype="bf16"),
+    MoEConfig("odd_sizes_f32", T=41, H=192, E=40, k=3, I=320, norm=True, dtype="f32"),
+    MoEConfig("single_token", T=1, H=256, E=16, k=4, I=128, norm=True, dtype="bf16"),
+    MoEConfig("k_equals_E", T=50, H=128, E=8, k=8, I=128, norm=True, dtype="bf16"),
+    MoEConfig("k1", T=130, H=128, E=8, k=1, I=128, norm=False, dtype="bf16"),
+]
+
+
+def _run_block(cfg, inp):
+    blk = binding.MoEBlock(cfg, inp)
+    x = dev(inp["x"])
+    blk.forward(x)
+    torch.cuda.synchronize()
+    return blk
+
+
+def check_block(orc, cfg, inp, blk, tokens):
+    """Block outputs of `tokens` against the oracle; statistics by their
+    definitions. Returns the number of near-tie selection mismatches."""
+    gi, gw = host(blk.topk_idx)[tokens], host(blk.topk_w)[tokens]
+    r, match = compare_selection(orc, cfg, inp, tokens, gi, gw)
+    mx, rm = check_output(host(blk.out)[tokens][match], r["out"][match], cfg.dtype)
+    print(f"{cfg.name}: max|d|/RMS {mx:.4f}  RMS(d)/RMS {rm:.5f}", flush=True)
+    np.testing.assert_allclose(host(blk.logits)[tokens], r["logits"], rtol=0, atol=2e-5)
+    # counts are the histogram of the selection; f = n / (T k)
+    counts = host(blk.counts)
+    assert (counts == np.bincount(host(blk.topk_idx).ravel(), minlength=cfg.E)).all()
+    assert counts.sum() == cfg.T * cfg.k
+    np.testing.assert_allclose(host(blk.f), counts / (cfg.T * cfg.k), rtol=1e-7)
+    return int((~match).sum())
+
+
+@pytest.mark.parametrize("cfg", E2E, ids=lambda c: c.name)
+def test_layer_forward_matches_oracle(orc, cfg):
+    inp = make_inputs(cfg, seed=0)
+    blk = _run_block(cfg, inp)
+    tokens = np.arange(cfg.T, dtype=np.int32)
+    nmis = check_block(orc, cfg, inp, blk, tokens)
+    # P and aux against the oracle's statistics (full softmax of its logits)
+    r = orc.forward_tokens(inp, cfg)
+    idx, _, probs = orc.route(r["logits"], cfg.k, cfg.norm)
+    counts, _, _, _ = orc.dispatch(idx, cfg.E)
+    f, P, aux = orc.aux(counts, probs, cfg.k)
+    np.testing.assert_allclose(host(blk.P), P, rtol=1e-5, atol=1e-8)
+    if nmis == 0:
+        assert (host(blk.counts) == counts).all()
+        assert host(blk.aux)[0] == pytest.approx(aux, rel=1e-5)
+    print(f"{cfg.name}: near-tie selection mismatches: {nmis}", flush=True)
+
+
+def test_all_tokens_to_one_expert(orc):
+    cfg = MoEConfig("hot", T=600, H=256, E=16, k=2, I=128, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=1)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[11] = 60.0  # expert 11 always first: 600 rows = several row tiles
+    inp["logit_bias"] = bias
+    blk = _run_block(cfg, inp)
+    assert (host(blk.topk_idx)[:, 0] == 11).all()
+    assert host(blk.counts)[11] == cfg.T
+    assert check_block(orc, cfg, inp, blk, np.arange(cfg.T, dtype=np.int32)) == 0
+
+
+def test_zero_router_ties_to_lowest_experts(orc):
+    cfg = MoEConfig("zero", T=200, H=128, E=32, k=4, I=64, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=3)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    blk = _run_block(cfg, inp)
+    assert (host(blk.topk_idx) == np.arange(4)).all()
+    np.testing.assert_allclose(host(blk.topk_w), 0.25, rtol=1e-7)
+    assert host(blk.counts).tolist() == [200] * 4 + [0] * 28
+    assert host(blk.aux)[0] == pytest.approx(1.0, rel=1e-6)
+    r = orc.forward_tokens(inp, cfg)
+    check_output(host(blk.out), r["out"], cfg.dtype)
+
+
+def test_deterministic_bitwise():
+    cfg = MoEConfig("det", T=1500, H=256, E=64, k=8, I=128, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=8)
+    blk = binding.MoEBlock(cfg, inp)
+    x = dev(inp["x"])
+    outs = []
+    for _ in range(3):
+        blk.forward(x)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (blk.out, blk.topk_idx, blk.topk_w, blk.logits,
+                                          blk.counts, blk.P, blk.aux)])
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t  # noqa: E731
+    for run in outs[1:]:
+        for a, b in zip(outs[0], run):
+            assert torch.equal(bits(a), bits(b))
