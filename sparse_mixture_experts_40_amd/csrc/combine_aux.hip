@@ -52,34 +52,45 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void aux_kernel(int T, int E, int k,
-                                                       const int32_t* __restrict__ counts,
-                                                       const float* __restrict__ partials, int np,
-                                                       int32_t* __restrict__ c_out,
-                                                       float* __restrict__ f_out,
-                                                       float* __restrict__ p_out,
-                                                       float* __restrict__ aux_out) {
-  __shared__ double s_fp[kThreads];
-  const int e = threadIdx.x;
-  double fp = 0.0;
-  if (e < E) {
+// One block per expert: P_e = (1/T) sum_b partials[b][e] (thread b takes the
+// fixed set b, b+256, ...; then a fixed-shape tree), f_e = n_e / (T k).
+__global__ __launch_bounds__(kThreads) void aux_expert_kernel(
+    int T, int E, int k, const int32_t* __restrict__ counts, const float* __restrict__ partials,
+    int np, int32_t* __restrict__ c_out, float* __restrict__ f_out, float* __restrict__ p_out,
+    double* __restrict__ fp_out) {
+  __shared__ double s[kThreads];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  double acc = 0.0;
+  for (int b = tid; b < np; b += kThreads) acc += (double)partials[(size_t)b * E + e];
+  s[tid] = acc;
+  __syncthreads();
+  for (int d = kThreads / 2; d > 0; d >>= 1) {
+    if (tid < d) s[tid] += s[tid + d];
+    __syncthreads();
+  }
+  if (tid == 0) {
     const int n = counts[e];
-    double s = 0.0;
-    for (int b = 0; b < np; ++b) s += (double)partials[(size_t)b * E + e];
     const double f = (double)n / ((double)T * (double)k);
-    const double P = s / (double)T;
+    const double P = s[0] / (double)T;
     if (c_out) c_out[e] = n;
     if (f_out) f_out[e] = (float)f;
     if (p_out) p_out[e] = (float)P;
-    fp = f * P;
+    fp_out[e] = f * P;
   }
-  s_fp[e] = fp;
+}
+
+// aux = E * sum_e f_e P_e (fixed-shape tree over the experts).
+__global__ __launch_bounds__(kThreads) void aux_final_kernel(int E, const double* __restrict__ fp,
+                                                             float* __restrict__ aux_out) {
+  __shared__ double s[kThreads];
+  const int e = threadIdx.x;
+  s[e] = (e < E) ? fp[e] : 0.0;
   __syncthreads();
-  for (int d = kThreads / 2; d > 0; d >>= 1) {  // fixed-shape tree
-    if (e < d) s_fp[e] += s_fp[e + d];
+  for (int d = kThreads / 2; d > 0; d >>= 1) {
+    if (e < d) s[e] += s[e + d];
     __syncthreads();
   }
-  if (e == 0 && aux_out) aux_out[0] = (float)((double)E * s_fp[0]);
+  if (e == 0) aux_out[0] = (float)((double)E * s[0]);
 }
 
 }  // namespace
@@ -96,9 +107,11 @@ hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pai
 }
 
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, moe_aux_out out, hipStream_t s) {
-  aux_kernel<<<1, kThreads, 0, s>>>(c.num_tokens, c.num_experts, c.top_k, counts, prob_partials,
-                                    n_partials, out.counts, out.f, out.P, out.aux);
+                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s) {
+  aux_expert_kernel<<<c.num_experts, kThreads, 0, s>>>(c.num_tokens, c.num_experts, c.top_k,
+                                                       counts, prob_partials, n_partials,
+                                                       out.counts, out.f, out.P, fp_scratch);
+  if (out.aux) aux_final_kernel<<<1, kThreads, 0, s>>>(c.num_experts, fp_scratch, out.aux);
   return hipGetLastError();
 }
 

@@ -47,8 +47,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
   __shared__ int s_c[256];
   const int e = threadIdx.x;
   int tot = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = 0; b < nchunks; ++b) tot += hist[(size_t)b * E + e];
+  }
   s_c[e] = tot;
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {  // inclusive scan over the 256 slots
@@ -64,6 +66,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
     if (offsets && e == E - 1) offsets[E] = s_c[e];
     if (base) {
       int run = excl;
+#pragma unroll 8
       for (int b = 0; b < nchunks; ++b) {
         base[(size_t)b * E + e] = run;
         run += hist[(size_t)b * E + e];

@@ -7,25 +7,20 @@
 // SwiGLU form down(silu(gate x) * up x).
 //
 // Rows are the expert-sorted routing pairs: expert e owns rows
-// [offsets[e], offsets[e+1]) (built by the dispatch). A block computes one
-// BM x BN tile of one expert; the tile is found on the device from `offsets`
-// (no host sync, no tile list): the grid is the worst case
-// (ceil(P/BM) + E row tiles) x (column tiles), and blocks past the last row
-// tile exit at once. Empty experts own no tiles, so their weights are never
-// read.
+// [offsets[e], offsets[e+1]) (built by the dispatch). The tile of a work item
+// is found on the device from `offsets` (no host sync, no tile list). Empty
+// experts own no tiles, so their weights are never read.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with the WEIGHT rows as the A operand
-// and the token rows as B, so D[n][m] puts 4 consecutive output columns of one
-// token row in each lane (8-byte stores). Both operands are K-contiguous; K is
-// staged 64 at a time through double-buffered, XOR-swizzled LDS (16-byte
-// chunk c of row r at chunk c ^ (r & 7): conflict-free ds_read_b128 /
-// ds_write_b128).
-//   gate/up: the B tile's first BN/2 rows are W_gate rows, the last BN/2 the
-//            W_up rows of the same columns, so each lane holds matching g and
-//            u; the epilogue writes h = silu(g) * u (fp32 math, one bf16
-//            rounding). The A rows are gathered through sorted_pair / k.
-//   down:    y_sorted = h W_down^T over contiguous h rows, stored in fp32
-//            (the combine adds the k rows of a token in fp32 and rounds once).
+// bf16 path (persistent, one 256-thread block per CU):
+//   tile  256 token rows x 256 weight rows; MFMA v_mfma_f32_32x32x16_bf16 with
+//         the WEIGHT rows as the A operand and the token rows as B, so D[n][m]
+//         puts 4 consecutive output columns of one token row in each lane;
+//   gate/up: the weight tile's first 128 rows are W_gate rows, the last 128
+//         the W_up rows of the same columns, so each lane holds matching g and
+//         u; the epilogue writes h = silu(g) * u (fp32 math, one bf16
+//         rounding). The token rows are gathered through sorted_pair / k;
+//   down: y_sorted = h W_down^T over contiguous h rows, stored in fp32 (the
+//         combine adds the k rows of a token in fp32 and rounds once).
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
 #include "moe_internal.h"
 
@@ -33,176 +28,306 @@ namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
-
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(n) for the small constant counts the pipeline needs
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a __syncthreads() fence
+// would drain the whole load pipeline). Each wave waits for its own LDS-DMA
+// loads with wait_vmcnt before arriving, so after the barrier every wave's
+// stage data is in LDS.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS row swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ f(r).
+// f makes the fragment reads (16 consecutive rows at one chunk per 256-byte
+// LDS cycle, or 8 rows per 128-byte cycle) conflict-free.
+template <int BK>
+__device__ __forceinline__ int swz_f(int r) {
+  if (BK == 64) return (r & 7) ^ ((r >> 3) & 1);               // 8 chunks per row
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);   // 4 chunks per row
+}
+
+// LDS-DMA of one K stage: this wave's BK/8 A and BK/8 B load instructions.
+// Lane l of an instruction lands at M0 + 16 l, i.e. the instruction fills
+// 1024 / (2 BK) consecutive tile rows; a_off / b_off already hold each lane's
+// source row and (swizzled) chunk.
+template <int BK, int BM, int NW>
+__device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* __restrict__ dB,
+                                          const char* abase, const char* bbase,
+                                          const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
+                                          int wave) {
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  constexpr int LA = BM * BK / (512 * NW), LB = 256 * BK / (512 * NW);  // per wave
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    __builtin_amdgcn_global_load_lds(abase + a_off[i] + kb,
+                                     (lds_void_t*)(dA + (wave * LA + i) * RPI * BK), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < LB; ++i)
+    __builtin_amdgcn_global_load_lds(bbase + b_off[i] + kb,
+                                     (lds_void_t*)(dB + (wave * LB + i) * RPI * BK), 16, 0, 0);
+}
+
+// Fragments of k step kk of a stage: 4 weight blocks (A operand), 4 token
+// blocks (B operand), 16 bytes per lane each.
+template <int BK, int MB, int NB>
+__device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
+                                           const uint16_t* __restrict__ sB, int kk,
+                                           bf16x8_t (&fa)[NB], bf16x8_t (&fb)[MB],
+                                           const int (&wrow)[NB], int trow0, int lane, int sw) {
+  const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    fa[nb] = *reinterpret_cast<const bf16x8_t*>(sB + wrow[nb] * BK + pc);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    fb[mb] = *reinterpret_cast<const bf16x8_t*>(sA + (trow0 + mb * 32) * BK + pc);
+}
+
+// One K stage of the pipeline: start the loads of stage (dA, dB), multiply
+// stage (cA, cB), wait for stage (nA, nB) and read its first fragments.
+// Half of the last k step's MFMAs are issued after the stage barrier, so the
+// MFMA pipe stays busy while the wave waits at the barrier and while the next
+// stage's first fragments arrive from LDS. (On the last stage the "next"
+// fragments are stale LDS data that is never used.)
+// The distinct __restrict__ pointers give the LDS accesses disjoint alias
+// scopes, so the compiler does not drain the in-flight LDS-DMA loads before
+// every fragment read; the explicit wait_vmcnt + lds_barrier order them.
+template <int BK, int BM, int NW, int MB, int NB>
+__device__ __forceinline__ void gemm_step(
+    uint16_t* __restrict__ dA, uint16_t* __restrict__ dB, bool issue_next, const char* abase,
+    const char* bbase, const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
+    const uint16_t* __restrict__ cA, const uint16_t* __restrict__ cB,
+    const uint16_t* __restrict__ nA, const uint16_t* __restrict__ nB, int vm_allow,
+    f32x16_t (&acc)[NB][MB], bf16x8_t (&fa)[2][NB], bf16x8_t (&fb)[2][MB],
+    const int (&wrow)[NB], int trow0, int lane, int sw, int wave) {
+  constexpr int KK = BK / 16;
+  constexpr int L = (KK - 1) & 1;  // fragment buffer of the last k step
+  constexpr int NH = NB / 2;       // last k step: blocks [0, NH) before the barrier
+  if (issue_next) dma_stage<BK, BM, NW>(dA, dB, abase, bbase, a_off, b_off, kb, wave);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + 1 < KK)
+      stage_frag<BK, MB, NB>(cA, cB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wrow, trow0,
+                             lane, sw);
+    const int nbe = (kk + 1 < KK) ? NB : NH;
+#pragma unroll
+    for (int nb = 0; nb < nbe; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][nb], fb[kk & 1][mb],
+                                                              acc[nb][mb], 0, 0, 0);
+  }
+  // interleave the next k step's fragment reads with the MFMAs
+  constexpr int NR = NB + MB, PER = (NB * MB + NR - 1) / NR;
+#pragma unroll
+  for (int kk = 0; kk + 1 < KK; ++kk)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  __builtin_amdgcn_sched_group_barrier(0x008, NH * MB, 0);
+  wait_vmcnt(vm_allow);
+  lds_barrier();
+  stage_frag<BK, MB, NB>(nA, nB, 0, fa[0], fb[0], wrow, trow0, lane, sw);
+#pragma unroll
+  for (int nb = NH; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[L][nb], fb[L][mb], acc[nb][mb], 0,
+                                                            0, 0);
+#pragma unroll
+  for (int i = 0; i < (NB - NH) * MB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
+// Persistent grouped GEMM: NW waves per block (2 x NW/2), OCC blocks per CU.
+//   tile: BM token rows x 256 weight rows, K staged BK at a time through NST
+//         LDS stages (NST - 1 stages of loads in flight under the MFMAs);
+//   wave: (BM/2) x (512/NW) = MB x NB blocks of v_mfma_f32_32x32x16_bf16 with
+//         fp32 accumulators; with 8 waves, two waves share each SIMD, so one
+//         wave's loads, LDS reads and barrier waits overlap the other's MFMAs;
+//   fragments of the next 16-wide k step are read while the MFMAs of the
+//         current one issue; the first fragments of the next stage are read
+//         right after the stage barrier, while deferred MFMAs keep the pipe busy;
+//   tiles: each XCD (hardware block b runs on XCD b % 8) walks one contiguous
+//         range of tiles; inside an expert the order is column tile major,
+//         row tile minor, so concurrent blocks share weight tiles in L2.
+// Rows past an expert's end and columns past N are clamped to valid memory on
+// load and never stored.
+template <bool GATEUP, int BM, int BK, int NST, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
     int n_tiles_n) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M;  // token rows per wave
-  constexpr int WTN = BN / WAVES_N;  // weight rows per wave
-  constexpr int MBW = WTM / 32, NBW = WTN / 32;
-  constexpr int ACH = BM * 8 / NT;  // 16-byte chunks per thread per K step
-  constexpr int BCH = BN * 8 / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile / thread mismatch");
-  static_assert(!GATEUP || NBW % 2 == 0, "gate/up needs paired blocks");
-  constexpr int NCOL = GATEUP ? BN / 2 : BN;  // output columns per block
-
-  __shared__ __align__(16) uint16_t s_a[2][BM * kBK];
-  __shared__ __align__(16) uint16_t s_b[2][BN * kBK];
+  constexpr int BN = 256;
+  constexpr int WN = NW / 2;                  // waves along the weight rows
+  constexpr int MB = BM / 64;                 // token blocks of 32 rows per wave
+  constexpr int NB = BN / (WN * 32);          // weight blocks of 32 rows per wave
+  constexpr int NCOL = GATEUP ? BN / 2 : BN;  // output columns per tile
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;               // tile rows per load instruction
+  constexpr int LA = BM * BK / (512 * NW);    // A load instructions per wave per stage
+  constexpr int LB = BN * BK / (512 * NW);    // B load instructions per wave per stage
+  constexpr int STAGE = (BM + BN) * BK;       // elements per stage
+  static_assert(BK / 16 == 1 || (BK / 16) % 2 == 0, "fragment double buffer parity");
+  static_assert(NB % 2 == 0 && LA >= 1 && LB >= 1, "tile / wave mismatch");
+  __shared__ __align__(1024) uint16_t smem[NST * STAGE];
   __shared__ int s_scan[2 * 256 + 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  const int n_real = row_tile_scan<BM>(offsets, E, s_scan) * n_tiles_n;
-  if ((int)blockIdx.x >= n_real) return;  // uniform: beyond the last tile
-  const int L = xcd_remap(blockIdx.x, n_real);
-  const int m_lin = L / n_tiles_n, n_tile = L - m_lin * n_tiles_n;
-  int expert, row0, row_end;
-  row_tile_find<BM>(s_scan, E, m_lin, expert, row0, row_end);
-  const int n0 = n_tile * NCOL;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int R = row_tile_scan<BM>(offsets, E, s_scan) * n_tiles_n;
+  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3;
+  const int chunk = (R + 7) >> 3;
+  const int nk = K / BK;
 
-  // per-thread source rows (nullptr: zero fill)
-  const uint16_t* a_src[ACH];
+  const int sw = swz_f<BK>(lane & 31);  // swizzle of every fragment row of this lane
+  int wrow[NB];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int r = (tid >> 3) + (NT / 8) * i;
-    const int gi = row0 + r;
-    a_src[i] = nullptr;
-    if (gi < row_end) {
+  for (int nb = 0; nb < NB; ++nb)
+    wrow[nb] = GATEUP ? ((nb / (NB / 2)) * 128 + wn * (NB / 2) * 32 + (nb % (NB / 2)) * 32 +
+                         (lane & 31))
+                      : (wn * NB * 32 + nb * 32 + (lane & 31));
+  const int trow0 = wm * (BM / 2) + (lane & 31);
+
+  for (int t = blockIdx.x >> 3; t < chunk; t += nper) {
+    const int L = xcd * chunk + t;
+    if (L >= R) break;
+    // expert e owns tiles [ntn * S[e-1], ntn * S[e]); column major inside
+    int expert, row0, row_end;
+    row_tile_find<BM>(s_scan, E, L / n_tiles_n, expert, row0, row_end);
+    const int s_prev = expert ? s_scan[expert - 1] : 0;
+    const int mt = s_scan[expert] - s_prev;
+    const int local = L - n_tiles_n * s_prev;
+    const int n_tile = local / mt, m_tile = local - n_tile * mt;
+    row0 = s_scan[E + 1 + expert] + m_tile * BM;
+    const int n0 = n_tile * NCOL;
+
+    // per-lane source byte offsets of this wave's LA A and LB B loads
+    uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int r = (wave * LA + i) * RPI + lane / CPR;  // tile row written by this lane
+      const int lc = (lane % CPR) ^ swz_f<BK>(r);       // logical chunk for its slot
+      int gi = row0 + r;
+      gi = gi < row_end ? gi : row_end - 1;
       const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
-      a_src[i] = act + (size_t)arow * K + (tid & 7) * 8;
+      a_off[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)lc * 8u) * 2u;
     }
-  }
-  const uint16_t* b_src[BCH];
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int r = (tid >> 3) + (NT / 8) * i;
-    int n;
-    const uint16_t* w;
-    if (GATEUP) {
-      n = n0 + (r < BN / 2 ? r : r - BN / 2);
-      w = (r < BN / 2) ? w0 : w1;
-    } else {
-      n = n0 + r;
-      w = w0;
+    for (int i = 0; i < LB; ++i) {
+      const int r = (wave * LB + i) * RPI + lane / CPR;
+      const int lc = (lane % CPR) ^ swz_f<BK>(r);
+      int n = n0 + (GATEUP ? (r & 127) : r);
+      n = n < N_out ? n : N_out - 1;
+      b_off[i] = (((uint32_t)expert * (uint32_t)N_out + (uint32_t)n) * (uint32_t)K +
+                  (uint32_t)lc * 8u) * 2u;
     }
-    b_src[i] = (n < N_out) ? w + ((size_t)expert * N_out + n) * K + (tid & 7) * 8 : nullptr;
-  }
+    const char* abase = reinterpret_cast<const char*>(act);
+    // B rows [0, 128) of a gate/up tile come from W_gate, [128, 256) from W_up
+    const char* bbase = reinterpret_cast<const char*>((GATEUP && wave >= NW / 2) ? w1 : w0);
 
-  f32x16_t acc[NBW][MBW];
+    f32x16_t acc[NB][MB];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+    bf16x8_t fa[2][NB], fb[2][MB];
 
-  uint4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int r = (tid >> 3) + (NT / 8) * i;
-      *reinterpret_cast<uint4*>(&s_a[buf][swz(r, tid & 7)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int r = (tid >> 3) + (NT / 8) * i;
-      *reinterpret_cast<uint4*>(&s_b[buf][swz(r, tid & 7)]) = rb[i];
-    }
-  };
+    // prologue: NST - 1 stages in flight, first fragments of stage 0
+    for (int st = 0; st < NST - 1 && st < nk; ++st)
+      dma_stage<BK, BM, NW>(smem + st * STAGE, smem + st * STAGE + BM * BK, abase, bbase, a_off,
+                            b_off, (uint32_t)(st * BK) * 2u, wave);
+    wait_vmcnt((LA + LB) * ((nk - 1 < NST - 2 ? nk - 1 : NST - 2)));
+    lds_barrier();
+    stage_frag<BK, MB, NB>(smem, smem + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
 
-  // weight row (within the B tile) of this lane for wave-local block nb
-  auto wrow = [&](int nb) {
-    if (GATEUP) {
-      const int half = nb < NBW / 2 ? 0 : BN / 2;
-      const int nbl = nb < NBW / 2 ? nb : nb - NBW / 2;
-      return half + wn * (WTN / 2) + nbl * 32 + (lane & 31);
+    for (int kt = 0; kt < nk; ++kt) {
+      uint16_t* dA = smem + ((kt + NST - 1) % NST) * STAGE;
+      const uint16_t* cA = smem + (kt % NST) * STAGE;
+      const uint16_t* nA = smem + ((kt + 1) % NST) * STAGE;
+      const int last = (kt + NST - 1 < nk - 1) ? kt + NST - 1 : nk - 1;
+      const int ahead = last - (kt + 1);  // stages still loading after stage kt+1
+      gemm_step<BK, BM, NW, MB, NB>(dA, dA + BM * BK, kt + NST - 1 < nk, abase, bbase, a_off,
+                                    b_off, (uint32_t)((kt + NST - 1) * BK) * 2u, cA,
+                                    cA + BM * BK, nA, nA + BM * BK,
+                                    ahead > 0 ? (LA + LB) * ahead : 0, acc, fa, fb, wrow, trow0,
+                                    lane, sw, wave);
     }
-    return wn * WTN + nb * 32 + (lane & 31);
-  };
+    __syncthreads();  // every wave done with the LDS stages before the next tile's loads
 
-  const int nk = K / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t af[NBW], bfr[MBW];
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = row0 + trow0 + mb * 32;
+      if (row >= row_end) continue;
+      if (GATEUP) {
+        uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)row * N_out;
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-        af[nb] = *reinterpret_cast<const bf16x8_t*>(&s_b[cur][swz(wrow(nb), ch)]);
+        for (int nb = 0; nb < NB / 2; ++nb) {
 #pragma unroll
-      for (int mb = 0; mb < MBW; ++mb)
-        bfr[mb] = *reinterpret_cast<const bf16x8_t*>(
-            &s_a[cur][swz(wm * WTM + mb * 32 + (lane & 31), ch)]);
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * (NB / 2) * 32 + nb * 32 + q * 8 + (lane >> 5) * 4;
+            if (col < N_out) {
+              float hv[4];
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
-#pragma unroll
-  for (int mb = 0; mb < MBW; ++mb) {
-    const int row = row0 + wm * WTM + mb * 32 + (lane & 31);
-    if (row >= row_end) continue;
-    if (GATEUP) {
-      uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)row * N_out;
-#pragma unroll
-      for (int nb = 0; nb < NBW / 2; ++nb) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * (WTN / 2) + nb * 32 + q * 8 + (lane >> 5) * 4;
-          if (col < N_out) {
-            float hv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              hv[j] = silu(acc[nb][mb][q * 4 + j]) * acc[nb + NBW / 2][mb][q * 4 + j];
-            *reinterpret_cast<uint2*>(orow + col) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+              for (int j = 0; j < 4; ++j)
+                hv[j] = silu(acc[nb][mb][q * 4 + j]) * acc[nb + NB / 2][mb][q * 4 + j];
+              *reinterpret_cast<uint2*>(orow + col) =
+                  make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            }
           }
         }
-      }
-    } else {
-      float* orow = static_cast<float*>(out) + (size_t)row * N_out;
+      } else {
+        float* orow = static_cast<float*>(out) + (size_t)row * N_out;
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * WTN + nb * 32 + q * 8 + (lane >> 5) * 4;
-          if (col < N_out)
-            *reinterpret_cast<float4*>(orow + col) =
-                make_float4(acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1],
-                            acc[nb][mb][q * 4 + 2], acc[nb][mb][q * 4 + 3]);
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * NB * 32 + nb * 32 + q * 8 + (lane >> 5) * 4;
+            if (col < N_out)
+              *reinterpret_cast<float4*>(orow + col) =
+                  make_float4(acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1],
+                              acc[nb][mb][q * 4 + 2], acc[nb][mb][q * 4 + 3]);
+          }
         }
       }
     }
   }
 }
+
+#ifndef MOE_GEMM_NW
+#define MOE_GEMM_NW 8
+#endif
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+// tile height, K step, LDS stages, waves per block, blocks per CU
+constexpr int kGemmBM = 256, kGemmBK = MOE_GEMM_BK, kGemmStages = MOE_GEMM_BK == 64 ? 2 : 4,
+              kGemmWaves = MOE_GEMM_NW, kGemmOcc = 1;
 
 // ---- fp32 path ------------------------------------------------------------
 
@@ -258,13 +383,15 @@ __global__ __launch_bounds__(256) void down_f32_kernel(int E, int H, int I,
   }
 }
 
-// bf16 tile shapes
-constexpr int GU_BM = 128, GU_BN = 128, GU_WM = 2, GU_WN = 2;
-constexpr int DN_BM = 128, DN_BN = 128, DN_WM = 2, DN_WN = 2;
-
-int grid_for(int P, int E, int BM, int n_tiles_n) {
-  const long mt = (long)(P + BM - 1) / BM + (E < P ? E : P);
-  return (int)(mt * n_tiles_n);
+// Number of CUs, rounded to a multiple of 8 (the persistent grid is a
+// multiple of it).
+int persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return (cus + 7) & ~7;
 }
 
 }  // namespace
@@ -280,9 +407,9 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
         static_cast<float*>(h));
     return hipGetLastError();
   }
-  const int ntn = (c.intermediate + GU_BN / 2 - 1) / (GU_BN / 2);
-  const int grid = grid_for(P, c.num_experts, GU_BM, ntn);
-  grouped_gemm_bf16_kernel<GU_BM, GU_BN, GU_WM, GU_WN, true><<<grid, 64 * GU_WM * GU_WN, 0, s>>>(
+  const int ntn = (c.intermediate + 127) / 128;
+  grouped_gemm_bf16_kernel<true, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
+      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
       c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
       sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
       static_cast<const uint16_t*>(w_up), h, ntn);
@@ -298,9 +425,9 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
         static_cast<const float*>(w_down), static_cast<float*>(y));
     return hipGetLastError();
   }
-  const int ntn = (c.hidden + DN_BN - 1) / DN_BN;
-  const int grid = grid_for(P, c.num_experts, DN_BM, ntn);
-  grouped_gemm_bf16_kernel<DN_BM, DN_BN, DN_WM, DN_WN, false><<<grid, 64 * DN_WM * DN_WN, 0, s>>>(
+  const int ntn = (c.hidden + 255) / 256;
+  grouped_gemm_bf16_kernel<false, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
+      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
       c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h), nullptr,
       offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn);
   return hipGetLastError();

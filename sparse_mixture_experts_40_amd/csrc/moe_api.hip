@@ -51,6 +51,7 @@ struct Layout {
   int32_t* hist;
   int32_t* base;
   float* partials;
+  double* fp;
   int32_t* counts;
   int32_t* offsets;
   int32_t* sorted_pair;
@@ -70,6 +71,7 @@ Layout carve(const moe_config& c, void* ws) {
   L.base = cv.take<int32_t>((size_t)dispatch_num_chunks(c) * E);
   L.dispatch_end = cv.off;
   L.partials = cv.take<float>((size_t)router_num_blocks(c) * E);
+  L.fp = cv.take<double>(E);
   L.counts = cv.take<int32_t>(E);
   L.offsets = cv.take<int32_t>(E + 1);
   L.idx = cv.take<int32_t>(P);
@@ -198,7 +200,7 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
   st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
                                 nullptr, false, stream));
   if (st != MOE_OK) return st;
-  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg), out, stream));
+  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg), L.fp, out, stream));
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
@@ -229,7 +231,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
   if (st != MOE_OK) return st;
   if (want_aux)
-    st = launched(launch_aux(c, L.counts, L.partials, router_num_blocks(c), aux, stream));
+    st = launched(launch_aux(c, L.counts, L.partials, router_num_blocks(c), L.fp, aux, stream));
   return st;
 }
 

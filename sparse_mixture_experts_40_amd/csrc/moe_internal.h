@@ -103,7 +103,8 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
 // Combine and statistics.
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s);
+// fp_scratch: E doubles of workspace (per-expert f_e * P_e).
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, moe_aux_out out, hipStream_t s);
+                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s);
 
 }  // namespace moe
