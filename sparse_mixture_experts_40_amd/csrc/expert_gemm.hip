@@ -329,6 +329,198 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
 constexpr int kGemmBM = 256, kGemmBK = MOE_GEMM_BK, kGemmStages = MOE_GEMM_BK == 64 ? 2 : 4,
               kGemmWaves = MOE_GEMM_NW, kGemmOcc = 1;
 
+// ---- bf16 decode path (few rows per expert: weight streaming) -------------
+//
+// Work item = (touched expert e, chunk c of 32 output columns): gate/up reads
+// 32 W_gate + 32 W_up rows, down reads 64 W_down rows, each exactly once; the
+// expert's token rows (n_e <= 64 per pass, padded to 32-row MFMA blocks) are
+// read from L2. K is split over the 4 waves (fixed reduction order through
+// LDS, so the result is deterministic). Weights go straight from HBM into
+// MFMA operand registers, two groups of 4 k steps in flight per wave.
+// Experts with no rows own no work items and read no weight bytes.
+constexpr int kDecG = 4;  // k steps (16 wide) per load group
+
+// Loads of one group of kDecG k steps: NB weight fragments and NTB token
+// fragments per step, 16 bytes per lane each.
+template <int NB, int NTB>
+__device__ __forceinline__ void dec_load(int g, const uint16_t* const (&wrow)[NB],
+                                         const uint16_t* const (&trow)[2],
+                                         bf16x8_t (&wf)[kDecG][NB], bf16x8_t (&tf)[kDecG][2]) {
+#pragma unroll
+  for (int s = 0; s < kDecG; ++s) {
+    const int k = (g * kDecG + s) * 16;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wf[s][nb] = *reinterpret_cast<const bf16x8_t*>(wrow[nb] + k);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) tf[s][tb] = *reinterpret_cast<const bf16x8_t*>(trow[tb] + k);
+  }
+}
+
+template <int NB, int NTB>
+__device__ __forceinline__ void dec_mfma(const bf16x8_t (&wf)[kDecG][NB],
+                                         const bf16x8_t (&tf)[kDecG][2], f32x16_t (&acc)[NB][2]) {
+#pragma unroll
+  for (int s = 0; s < kDecG; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s][nb], tf[s][tb], acc[nb][tb],
+                                                              0, 0, 0);
+}
+
+// This wave's K range: groups of kDecG k steps, two groups of loads in flight
+// (static buffers A / B, so no register copies between groups).
+template <int NB, int NTB>
+__device__ __forceinline__ void dec_kloop(int ng, const uint16_t* const (&wrow)[NB],
+                                          const uint16_t* const (&trow)[2],
+                                          f32x16_t (&acc)[NB][2]) {
+  bf16x8_t wa[kDecG][NB], ta[kDecG][2], wb[kDecG][NB], tb_[kDecG][2];
+  dec_load<NB, NTB>(0, wrow, trow, wa, ta);
+  int g = 0;
+  constexpr int NL = kDecG * (NB + NTB), NM = kDecG * NB * NTB;
+  for (; g + 2 < ng; g += 2) {  // no conditional loads inside: exact vmcnt waits
+    dec_load<NB, NTB>(g + 1, wrow, trow, wb, tb_);
+    dec_mfma<NB, NTB>(wa, ta, acc);
+    dec_load<NB, NTB>(g + 2, wrow, trow, wa, ta);
+    dec_mfma<NB, NTB>(wb, tb_, acc);
+    // keep each group's loads ahead of the previous group's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+  if (g + 1 < ng) {
+    dec_load<NB, NTB>(g + 1, wrow, trow, wb, tb_);
+    dec_mfma<NB, NTB>(wa, ta, acc);
+    dec_mfma<NB, NTB>(wb, tb_, acc);
+  } else {
+    dec_mfma<NB, NTB>(wa, ta, acc);
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
+    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
+    int n_chunks) {
+  constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
+  __shared__ int s_scan[2 * 256 + 2];
+  __shared__ __align__(16) float s_part[4][NB][2][16][64];  // [wave][nb][tb][r][lane]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // s_scan[e]: inclusive count of experts with rows; offsets in s_scan[E+1..]
+  for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  __syncthreads();
+  if (tid < E) s_scan[tid] = (s_scan[E + 2 + tid] > s_scan[E + 1 + tid]) ? 1 : 0;
+  __syncthreads();
+  for (int d = 1; d < E; d <<= 1) {
+    const int add = (tid < E && tid >= d) ? s_scan[tid - d] : 0;
+    __syncthreads();
+    if (tid < E) s_scan[tid] += add;
+    __syncthreads();
+  }
+  const int items = s_scan[E - 1] * n_chunks;
+  const int kw = K / 4;  // this wave's K range [wave*kw, wave*kw + kw)
+  const int nsteps = kw / 16;
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int rank = it / n_chunks, c = it - rank * n_chunks;
+    int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
+    }
+    const int e = lo;
+    const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
+    // weight rows of this lane (A operand): block nb, row lane & 31
+    const uint16_t* wrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int n = GATEUP ? c * 32 + (lane & 31) : c * 64 + nb * 32 + (lane & 31);
+      n = n < N_out ? n : N_out - 1;
+      const uint16_t* wm = (GATEUP && nb == 1) ? w1 : w0;
+      wrow[nb] = wm + ((size_t)e * N_out + n) * K + wave * kw + (lane >> 5) * 8;
+    }
+    for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
+      const uint16_t* trow[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        int gi = p0 + tb * 32 + (lane & 31);
+        gi = gi < r1 ? gi : r1 - 1;
+        const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
+        trow[tb] = act + (size_t)arow * K + wave * kw + (lane >> 5) * 8;
+      }
+      const int ntb = (r1 - p0) > 32 ? 2 : 1;
+      f32x16_t acc[NB][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
+      const int ng = nsteps / kDecG;
+      if (ntb > 1)
+        dec_kloop<NB, 2>(ng, wrow, trow, acc);
+      else
+        dec_kloop<NB, 1>(ng, wrow, trow, acc);
+      // split-K reduction over the 4 waves in fixed order, then the epilogue
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
+      __syncthreads();
+      {
+        const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, lane, half of r)
+        const int row = p0 + tb * 32 + (lane & 31);
+        if (tb < ntb && row < r1) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = half * 2 + qq;  // group of 4 consecutive columns
+            float v[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int r = q * 4 + j;
+                v[nb][j] = ((s_part[0][nb][tb][r][lane] + s_part[1][nb][tb][r][lane]) +
+                            s_part[2][nb][tb][r][lane]) + s_part[3][nb][tb][r][lane];
+              }
+            const int n_in = q * 8 + (lane >> 5) * 4;  // column inside a 32-wide block
+            if (GATEUP) {
+              const int col = c * 32 + n_in;
+              if (col < N_out) {
+                float hv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hv[j] = silu(v[0][j]) * v[1][j];
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)row * N_out + col) =
+                    make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+              }
+            } else {
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                const int col = c * 64 + nb * 32 + n_in;
+                if (col < N_out)
+                  *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)row * N_out + col) =
+                      make_float4(v[nb][0], v[nb][1], v[nb][2], v[nb][3]);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();  // s_part is reused by the next pass / item
+    }
+  }
+}
+
+// The decode kernels take the block when the average expert has few rows.
+bool use_decode_path(const moe_config& c) {
+  return (long)c.num_tokens * c.top_k <= 16L * c.num_experts && c.hidden % 256 == 0 &&
+         c.intermediate % 256 == 0;
+}
+
 // ---- fp32 path ------------------------------------------------------------
 
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int i) {
@@ -407,6 +599,14 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
         static_cast<float*>(h));
     return hipGetLastError();
   }
+  if (use_decode_path(c)) {
+    const int nch = (c.intermediate + 31) / 32;
+    decode_gemm_bf16_kernel<true><<<persistent_grid(), 256, 0, s>>>(
+        c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
+        sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
+        static_cast<const uint16_t*>(w_up), h, nch);
+    return hipGetLastError();
+  }
   const int ntn = (c.intermediate + 127) / 128;
   grouped_gemm_bf16_kernel<true, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
       <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
@@ -423,6 +623,13 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
     down_f32_kernel<<<P, 256, c.intermediate * sizeof(float), s>>>(
         c.num_experts, c.hidden, c.intermediate, static_cast<const float*>(h), offsets,
         static_cast<const float*>(w_down), static_cast<float*>(y));
+    return hipGetLastError();
+  }
+  if (use_decode_path(c)) {
+    const int nch = (c.hidden + 63) / 64;
+    decode_gemm_bf16_kernel<false><<<persistent_grid(), 256, 0, s>>>(
+        c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
+        nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch);
     return hipGetLastError();
   }
   const int ntn = (c.hidden + 255) / 256;

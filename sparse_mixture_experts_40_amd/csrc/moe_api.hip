@@ -58,6 +58,8 @@ struct Layout {
   int32_t* pair_pos;
   int32_t* idx;
   float* w;
+  float* rpart;   // split-K router partials [splits, T, E]
+  float* rlogits; // split-K router logits [T, E]
   void* h;
   void* y;
   size_t dispatch_end, aux_end, layer_end;
@@ -70,13 +72,16 @@ Layout carve(const moe_config& c, void* ws) {
   L.hist = cv.take<int32_t>((size_t)dispatch_num_chunks(c) * E);
   L.base = cv.take<int32_t>((size_t)dispatch_num_chunks(c) * E);
   L.dispatch_end = cv.off;
-  L.partials = cv.take<float>((size_t)router_num_blocks(c) * E);
+  L.partials = cv.take<float>((size_t)router_num_blocks(c, true) * E);  // the larger count
   L.fp = cv.take<double>(E);
   L.counts = cv.take<int32_t>(E);
   L.offsets = cv.take<int32_t>(E + 1);
   L.idx = cv.take<int32_t>(P);
   L.w = cv.take<float>(P);
   L.aux_end = cv.off;
+  const int ks = router_k_splits(c);
+  L.rpart = ks > 1 ? cv.take<float>((size_t)ks * c.num_tokens * E) : nullptr;
+  L.rlogits = ks > 1 ? cv.take<float>((size_t)c.num_tokens * E) : nullptr;
   L.sorted_pair = cv.take<int32_t>(P);
   L.pair_pos = cv.take<int32_t>(P);
   L.h = cv.take<char>(P * c.intermediate * elem_bytes(c));
@@ -200,7 +205,8 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
   st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
                                 nullptr, false, stream));
   if (st != MOE_OK) return st;
-  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg), L.fp, out, stream));
+  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg, true), L.fp, out,
+                             stream));
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
@@ -218,8 +224,13 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   float* w = topk_w ? topk_w : L.w;
   const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
 
-  st = launched(launch_router(c, x, w_router, logit_bias, router_logits, router_logits != nullptr,
-                              idx, w, want_aux ? L.partials : nullptr, true, stream));
+  if (router_k_splits(c) > 1)
+    st = launched(launch_router_split(c, x, w_router, logit_bias, L.rlogits, router_logits,
+                                      L.rpart, idx, w, want_aux ? L.partials : nullptr, stream));
+  else
+    st = launched(launch_router(c, x, w_router, logit_bias, router_logits,
+                                router_logits != nullptr, idx, w,
+                                want_aux ? L.partials : nullptr, true, stream));
   if (st != MOE_OK) return st;
   st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
                                 L.base, true, stream));
@@ -231,7 +242,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
   if (st != MOE_OK) return st;
   if (want_aux)
-    st = launched(launch_aux(c, L.counts, L.partials, router_num_blocks(c), L.fp, aux, stream));
+    st = launched(launch_aux(c, L.counts, L.partials,
+                             router_num_blocks(c, router_k_splits(c) > 1), L.fp, aux, stream));
   return st;
 }
 

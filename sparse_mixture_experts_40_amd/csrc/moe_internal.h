@@ -80,12 +80,20 @@ __device__ void row_tile_find(const int* s_scan, int E, int tile_id, int& expert
 
 // Router: logits (MFMA for bf16, FMA for fp32) + softmax + top-k + weights.
 // x == nullptr: logits are read from `logits`. prob_partials (nullable):
-// [ceil(T/64), E] per-block sums of the full softmax. do_select == 0 skips the
-// top-k (only partials are produced).
+// [router_num_blocks(c, x == nullptr), E] per-block sums of the full softmax.
+// do_select == 0 skips the top-k (only partials are produced).
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
                          float* topk_w, float* prob_partials, bool do_select, hipStream_t s);
-int router_num_blocks(const moe_config& c);
+int router_num_blocks(const moe_config& c, bool from_logits);
+// Split-K router for small token counts (bf16): K splits (1 = not worth it),
+// and the launch sequence partial logits -> fixed-order sum (+ bias) ->
+// softmax / top-k. part: [splits, T, E] fp32, logits_ws: [T, E] fp32 scratch.
+int router_k_splits(const moe_config& c);
+hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
+                               const float* bias, float* logits_ws, float* logits_out,
+                               float* part, int32_t* topk_idx, float* topk_w,
+                               float* prob_partials, hipStream_t s);
 
 // Dispatch: histogram per chunk, scan, stable scatter.
 int dispatch_num_chunks(const moe_config& c);

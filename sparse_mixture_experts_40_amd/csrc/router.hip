@@ -8,9 +8,9 @@
 //  1. logits tile [64 tokens x E] — bf16: MFMA 32x32x16 with the router rows
 //     as the A operand and the tokens as B, K staged through swizzled LDS;
 //     fp32: plain FMA dot products. (x == nullptr: the tile is read.)
-//  2. each wave takes 16 tokens; lanes hold experts e = lane + 64q. Softmax
-//     max/sum are xor-butterfly reductions (every lane ends with the same
-//     bits). Top-k is k rounds of a wave max over 64-bit keys
+//  2. each wave takes 16 tokens, 4 at a time (their reductions interleave);
+//     lanes hold experts e = lane + 64q. Softmax max/sum are xor-butterfly
+//     reductions (every lane ends with the same bits). Top-k is k rounds of a wave max over 64-bit keys
 //     (order-preserving fp32 bits, then 0xFFFF - e), so equal logits go to
 //     the lower expert index; -0.0 is folded into +0.0 first.
 //  3. per-block sums of the full softmax over the block's tokens (fixed order)
@@ -36,32 +36,38 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+constexpr int kNT = 4;  // tokens reduced together per wave
+
+__device__ __forceinline__ void wave_max_n(float (&v)[kNT]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  for (int msk = 32; msk >= 1; msk >>= 1)
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) v[u] = fmaxf(v[u], __shfl_xor(v[u], msk, 64));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ void wave_sum_n(float (&v)[kNT]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  for (int msk = 32; msk >= 1; msk >>= 1)
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) v[u] += __shfl_xor(v[u], msk, 64);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+__device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[kNT]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const unsigned long long o = __shfl_xor(v, m, 64);
-    v = (o > v) ? o : v;
-  }
-  return v;
+  for (int msk = 32; msk >= 1; msk >>= 1)
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) {
+      const unsigned long long o = __shfl_xor(v[u], msk, 64);
+      v[u] = (o > v[u]) ? o : v[u];
+    }
 }
 
 // swizzled [rows][64] bf16 tile: 16-byte chunk c of row r lives at chunk c ^ (r & 7)
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
 
 // Logits tile by bf16 MFMA into s_log[t * ls + e] (+ bias).
-__device__ void router_logits_mfma(int T, int H, int E, int t0, const uint16_t* __restrict__ x,
+__device__ void router_logits_mfma(int T, int H, int E, int t0, int kbeg, int kend,
+                                   const uint16_t* __restrict__ x,
                                    const uint16_t* __restrict__ wr, const float* __restrict__ bias,
                                    char* smem, float* s_log, int ls) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,13 +111,13 @@ __device__ void router_logits_mfma(int T, int H, int E, int t0, const uint16_t* 
     }
   };
 
-  const int nk = H / kBK;
-  gload(0);
+  const int nk = (kend - kbeg) / kBK;
+  gload(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();  // previous compute done with the tile
     sstore();
     __syncthreads();
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * kBK);
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int ch = kk * 2 + (lane >> 5);
@@ -149,20 +155,20 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     int T, int H, int E, int k, int norm, const void* __restrict__ x, const void* __restrict__ wr,
     const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partials,
-    int do_select) {
+    int do_select, int tpb) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kTok;
+  const int t0 = blockIdx.x * tpb;  // tpb = 64 when the logits are computed here
   const int ls = ((E + 31) & ~31) + 1;
   float* s_log = reinterpret_cast<float*>(smem);  // [64][ls]
 
   if (logits_in) {
-    for (int i = tid; i < kTok * E; i += kThreads) {
+    for (int i = tid; i < tpb * E; i += kThreads) {
       const int t = i / E, e = i - t * E;
       s_log[t * ls + e] = (t0 + t < T) ? logits_in[(size_t)(t0 + t) * E + e] : 0.0f;
     }
   } else if constexpr (BF16) {
-    router_logits_mfma(T, H, E, t0, static_cast<const uint16_t*>(x),
+    router_logits_mfma(T, H, E, t0, 0, H, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(wr), bias, smem, s_log, ls);
   } else {
     const float* xf = static_cast<const float*>(x);
@@ -181,63 +187,97 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
   const int EQ = (E + 63) >> 6;  // <= 4 experts per lane
   float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int tt = 0; tt < kTok / 4; ++tt) {
-    const int t = wave * (kTok / 4) + tt, gt = t0 + t;
-    if (gt >= T) break;  // wave-uniform
-    float v[4];
+  // kNT tokens at a time per wave: their cross-lane reductions are independent
+  // chains, so the shuffle latencies overlap.
+  for (int tt = 0; tt < tpb / 4; tt += kNT) {
+    const int tb0 = wave * (tpb / 4) + tt;
+    if (t0 + tb0 >= T) break;  // wave-uniform
+    bool ok[kNT];
+    float v[kNT][4], m[kNT], ex[kNT][4], ssum[kNT], inv[kNT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = (q < EQ && e < E) ? s_log[t * ls + e] : -INFINITY;
-      if (logits_out && q < EQ && e < E) logits_out[(size_t)gt * E + e] = v[q];
-    }
-    const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    float ex[4], s = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      ex[q] = (q < EQ && e < E) ? expf(v[q] - m) : 0.0f;
-      s += ex[q];
-    }
-    s = wave_sum(s);
-    const float inv = 1.0f / s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pacc[q] += ex[q] * inv;
-
-    if (do_select) {
-      uint32_t key[4];
+    for (int u = 0; u < kNT; ++u) {
+      const int t = tb0 + u, gt = t0 + t;
+      ok[u] = gt < T;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        key[q] = (q < EQ && e < E) ? order_key(v[q]) : 0u;
+        v[u][q] = (q < EQ && e < E) ? s_log[t * ls + e] : -INFINITY;
+        if (logits_out && ok[u] && q < EQ && e < E) logits_out[(size_t)gt * E + e] = v[u][q];
       }
-      int my_e = 0;
-      float my_p = 0.0f, psum = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        unsigned long long best = 0ull;
+      m[u] = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
+    }
+    wave_max_n(m);
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) {
+      ssum[u] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        ex[u][q] = (q < EQ && e < E) ? expf(v[u][q] - m[u]) : 0.0f;
+        ssum[u] += ex[u][q];
+      }
+    }
+    wave_sum_n(ssum);
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) {
+      inv[u] = 1.0f / ssum[u];
+      if (ok[u]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pacc[q] += ex[u][q] * inv[u];
+      }
+    }
+
+    if (do_select) {
+      uint32_t key[kNT][4];
+      int my_e[kNT];
+      float my_p[kNT], psum[kNT];
+#pragma unroll
+      for (int u = 0; u < kNT; ++u) {
+        my_e[u] = 0;
+        my_p[u] = 0.0f;
+        psum[u] = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const unsigned long long cand =
-              (static_cast<unsigned long long>(key[q]) << 32) | (0xFFFFu - (unsigned)(lane + 64 * q));
-          best = (key[q] != 0u && cand > best) ? cand : best;
-        }
-        best = wave_max_u64(best);
-        const int ej = 0xFFFF - static_cast<int>(best & 0xFFFFull);
-        if ((ej & 63) == lane) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (q == (ej >> 6)) key[q] = 0u;
-        }
-        const float pj = expf(key_value(static_cast<uint32_t>(best >> 32)) - m) * inv;
-        psum += pj;
-        if (lane == j) {
-          my_e = ej;
-          my_p = pj;
+          const int e = lane + 64 * q;
+          key[u][q] = (q < EQ && e < E) ? order_key(v[u][q]) : 0u;
         }
       }
-      if (lane < k) {
-        topk_idx[(size_t)gt * k + lane] = my_e;
-        topk_w[(size_t)gt * k + lane] = norm ? my_p / psum : my_p;
+      for (int j = 0; j < k; ++j) {
+        unsigned long long best[kNT];
+#pragma unroll
+        for (int u = 0; u < kNT; ++u) {
+          best[u] = 0ull;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const unsigned long long cand = (static_cast<unsigned long long>(key[u][q]) << 32) |
+                                            (0xFFFFu - (unsigned)(lane + 64 * q));
+            best[u] = (key[u][q] != 0u && cand > best[u]) ? cand : best[u];
+          }
+        }
+        wave_max_u64_n(best);
+#pragma unroll
+        for (int u = 0; u < kNT; ++u) {
+          const int ej = 0xFFFF - static_cast<int>(best[u] & 0xFFFFull);
+          if ((ej & 63) == lane) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (q == (ej >> 6)) key[u][q] = 0u;
+          }
+          const float pj = expf(key_value(static_cast<uint32_t>(best[u] >> 32)) - m[u]) * inv[u];
+          psum[u] += pj;
+          if (lane == j) {
+            my_e[u] = ej;
+            my_p[u] = pj;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kNT; ++u) {
+        const int gt = t0 + tb0 + u;
+        if (ok[u] && lane < k) {
+          topk_idx[(size_t)gt * k + lane] = my_e[u];
+          topk_w[(size_t)gt * k + lane] = norm ? my_p[u] / psum[u] : my_p[u];
+        }
       }
     }
   }
@@ -257,9 +297,84 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   }
 }
 
+// Split-K router logits for small token counts (a single 64-token block
+// would stream the whole router matrix through one CU): block (tile, ks)
+// computes the partial logits of its 64 tokens over K range ks, written to
+// part[ks][t][e]; router_reduce_kernel sums the partials in ks order and adds
+// the bias, then the usual router_kernel runs on the summed logits.
+__global__ __launch_bounds__(kThreads) void router_partial_kernel(
+    int T, int H, int E, int kchunk, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wr, float* __restrict__ part) {
+  extern __shared__ __align__(16) char smem[];
+  const int t0 = blockIdx.x * kTok, ks = blockIdx.y;
+  const int ls = ((E + 31) & ~31) + 1;
+  float* s_log = reinterpret_cast<float*>(smem);
+  router_logits_mfma(T, H, E, t0, ks * kchunk, ks * kchunk + kchunk, x, wr, nullptr, smem, s_log,
+                     ls);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTok * E; i += kThreads) {
+    const int t = i / E, e = i - t * E;
+    if (t0 + t < T) part[((size_t)ks * T + t0 + t) * E + e] = s_log[t * ls + e];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void router_reduce_kernel(int T, int E, int nsplit,
+                                                                 const float* __restrict__ part,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ logits,
+                                                                 float* __restrict__ logits_out) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= T * E) return;
+  float s = 0.0f;
+  for (int ks = 0; ks < nsplit; ++ks) s += part[(size_t)ks * T * E + i];
+  if (bias) s += bias[i % E];
+  logits[i] = s;
+  if (logits_out) logits_out[i] = s;
+}
+
 }  // namespace
 
-int router_num_blocks(const moe_config& c) { return (c.num_tokens + kTok - 1) / kTok; }
+// Tokens per router block: 64 when the block computes its logits (one MFMA
+// tile); 16 when it starts from logits and T is small (more waves share the
+// top-k work).
+int router_tpb(const moe_config& c, bool from_logits) {
+  return (from_logits && c.num_tokens <= 4096) ? 16 : kTok;
+}
+
+int router_num_blocks(const moe_config& c, bool from_logits) {
+  const int tpb = router_tpb(c, from_logits);
+  return (c.num_tokens + tpb - 1) / tpb;
+}
+
+int router_k_splits(const moe_config& c) {
+  if (c.dtype != MOE_DTYPE_BF16) return 1;
+  // Split only grids below one block per CU: above that the fused kernel (logits
+  // and top-k in one pass) is faster than split + reduce + a top-k pass.
+  int ks = 1;
+  while (router_num_blocks(c, false) * ks * 2 <= 256 && c.hidden % (ks * 2 * kBK) == 0 &&
+         c.hidden / (ks * 2) >= 256)
+    ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
+                               const float* bias, float* logits_ws, float* logits_out,
+                               float* part, int32_t* topk_idx, float* topk_w,
+                               float* prob_partials, hipStream_t s) {
+  const int ks = router_k_splits(c), E = c.num_experts;
+  const int EP = (E + 31) & ~31;
+  size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
+  const size_t tiles = (size_t)(kTok + EP) * kBK * sizeof(uint16_t);
+  if (tiles > lds) lds = tiles;
+  router_partial_kernel<<<dim3(router_num_blocks(c, false), ks), kThreads, lds, s>>>(
+      c.num_tokens, c.hidden, E, c.hidden / ks, static_cast<const uint16_t*>(x),
+      static_cast<const uint16_t*>(w_router), part);
+  const int n = c.num_tokens * E;
+  router_reduce_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(
+      c.num_tokens, E, ks, part, bias, logits_ws, logits_out);
+  return launch_router(c, nullptr, nullptr, nullptr, logits_ws, false, topk_idx, topk_w,
+                       prob_partials, true, s);
+}
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
@@ -272,17 +387,19 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
     if (tiles > lds) lds = tiles;
   }
   if (lds < 4 * 256 * sizeof(float)) lds = 4 * 256 * sizeof(float);
-  const dim3 grid(router_num_blocks(c)), block(kThreads);
+  const bool from_logits = (x == nullptr);
+  const int tpb = router_tpb(c, from_logits);
+  const dim3 grid(router_num_blocks(c, from_logits)), block(kThreads);
   const float* lin = x ? nullptr : logits;
   float* lout = (x && logits_out) ? logits : nullptr;
   if (c.dtype == MOE_DTYPE_BF16)
     router_kernel<true><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
                                                  c.norm_topk_prob, x, w_router, bias, lin, lout,
-                                                 topk_idx, topk_w, prob_partials, do_select);
+                                                 topk_idx, topk_w, prob_partials, do_select, tpb);
   else
     router_kernel<false><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
                                                   c.norm_topk_prob, x, w_router, bias, lin, lout,
-                                                  topk_idx, topk_w, prob_partials, do_select);
+                                                  topk_idx, topk_w, prob_partials, do_select, tpb);
   return hipGetLastError();
 }
 

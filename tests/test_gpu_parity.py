@@ -109,6 +109,9 @@ def test_dispatch_bitexact(orc, T, E, k):
 
 EXPERT_SHAPES = [  # (T, H, E, k, I)
     (64, 128, 8, 2, 256),
+    # weight-streaming (decode) kernels: few rows per expert, H and I multiples of 256
+    (40, 512, 16, 4, 512),
+    (7, 1024, 64, 8, 256),
     (700, 512, 8, 2, 1024),
     (300, 256, 64, 8, 128),
     (41, 192, 40, 3, 320),
@@ -199,6 +202,8 @@ E2E = [
     MoEConfig("single_token", T=1, H=256, E=16, k=4, I=128, norm=True, dtype="bf16"),
     MoEConfig("k_equals_E", T=50, H=128, E=8, k=8, I=128, norm=True, dtype="bf16"),
     MoEConfig("k1", T=130, H=128, E=8, k=1, I=128, norm=False, dtype="bf16"),
+    MoEConfig("decode_skewed", T=48, H=768, E=64, k=6, I=512, norm=True, dtype="bf16",
+              zipf_s=1.5),
 ]
 
 
@@ -253,6 +258,19 @@ def test_all_tokens_to_one_expert(orc):
     blk = _run_block(cfg, inp)
     assert (host(blk.topk_idx)[:, 0] == 11).all()
     assert host(blk.counts)[11] == cfg.T
+    assert check_block(orc, cfg, inp, blk, np.arange(cfg.T, dtype=np.int32)) == 0
+
+
+def test_decode_path_hot_expert_multi_pass(orc):
+    """Weight-streaming kernels with one expert holding more than 64 rows
+    (several token passes) and a ragged last pass."""
+    cfg = MoEConfig("hot_decode", T=100, H=512, E=8, k=1, I=256, norm=False, dtype="bf16")
+    inp = make_inputs(cfg, seed=6)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[5] = 60.0
+    inp["logit_bias"] = bias
+    blk = _run_block(cfg, inp)
+    assert host(blk.counts)[5] == cfg.T
     assert check_block(orc, cfg, inp, blk, np.arange(cfg.T, dtype=np.int32)) == 0
 
 
