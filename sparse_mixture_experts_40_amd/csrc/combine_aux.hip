@@ -17,14 +17,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k,
+// One block per token. KC > 0 is the exact k at compile time, so all k row
+// loads of a column chunk are issued before the first multiply (k loads in
+// flight per lane); KC == 0 is the runtime-k form. Either way the sum runs in
+// slot order j = 0..k-1.
+template <bool BF16, int KC>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k_rt,
                                                            const void* __restrict__ y,
                                                            const int32_t* __restrict__ pair_pos,
                                                            const float* __restrict__ topk_w,
                                                            void* __restrict__ out) {
   __shared__ int s_pos[16];
   __shared__ float s_w[16];
+  const int k = KC > 0 ? KC : k_rt;
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) {
     s_pos[tid] = pair_pos[(size_t)t * k + tid];
@@ -35,13 +40,28 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k,
   const float* yf = static_cast<const float*>(y);
   for (int c = tid; c < H / 4; c += kThreads) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(yf + (size_t)s_pos[j] * H + c * 4);
-      const float w = s_w[j];
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+    if constexpr (KC > 0) {
+      float4 v[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        v[j] = *reinterpret_cast<const float4*>(yf + (size_t)s_pos[j] * H + c * 4);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float w = s_w[j];
+        acc.x = fmaf(w, v[j].x, acc.x);
+        acc.y = fmaf(w, v[j].y, acc.y);
+        acc.z = fmaf(w, v[j].z, acc.z);
+        acc.w = fmaf(w, v[j].w, acc.w);
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(yf + (size_t)s_pos[j] * H + c * 4);
+        const float w = s_w[j];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+      }
     }
     if constexpr (BF16) {
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + c * 4) =
@@ -95,14 +115,26 @@ __global__ __launch_bounds__(kThreads) void aux_final_kernel(int E, const double
 
 }  // namespace
 
+template <bool BF16>
+void combine_launch(const moe_config& c, const void* y, const int32_t* pair_pos,
+                    const float* topk_w, void* out, hipStream_t s) {
+  const dim3 g(c.num_tokens), b(kThreads);
+  const int T = c.num_tokens, H = c.hidden, k = c.top_k;
+  switch (k) {
+    case 1: combine_kernel<BF16, 1><<<g, b, 0, s>>>(T, H, k, y, pair_pos, topk_w, out); break;
+    case 2: combine_kernel<BF16, 2><<<g, b, 0, s>>>(T, H, k, y, pair_pos, topk_w, out); break;
+    case 4: combine_kernel<BF16, 4><<<g, b, 0, s>>>(T, H, k, y, pair_pos, topk_w, out); break;
+    case 8: combine_kernel<BF16, 8><<<g, b, 0, s>>>(T, H, k, y, pair_pos, topk_w, out); break;
+    default: combine_kernel<BF16, 0><<<g, b, 0, s>>>(T, H, k, y, pair_pos, topk_w, out); break;
+  }
+}
+
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s) {
   if (c.dtype == MOE_DTYPE_BF16)
-    combine_kernel<true><<<c.num_tokens, kThreads, 0, s>>>(c.num_tokens, c.hidden, c.top_k, y,
-                                                           pair_pos, topk_w, out);
+    combine_launch<true>(c, y, pair_pos, topk_w, out, s);
   else
-    combine_kernel<false><<<c.num_tokens, kThreads, 0, s>>>(c.num_tokens, c.hidden, c.top_k, y,
-                                                            pair_pos, topk_w, out);
+    combine_launch<false>(c, y, pair_pos, topk_w, out, s);
   return hipGetLastError();
 }
 
