@@ -28,7 +28,11 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g); the reciprocal is the hardware approximation
+// (about 1 ulp of fp32), far below the bf16 rounding of h that follows.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -160,6 +164,48 @@ __device__ __forceinline__ void gemm_step(
   }
 }
 
+// Location and per-lane load offsets of tile L (column tile major inside an
+// expert: expert e owns tiles [ntn * S[e-1], ntn * S[e])).
+struct GemmTile {
+  int row0, row_end, n0;
+};
+
+template <bool GATEUP, int BM, int BK, int NW, int NCOL, int LA, int LB>
+__device__ __forceinline__ void tile_setup(int L, int n_tiles_n, int E, int K, int N_out,
+                                           int k_top, const int* s_scan,
+                                           const int32_t* __restrict__ sorted_pair, int wave,
+                                           int lane, GemmTile& tl, uint32_t (&a_off)[LA],
+                                           uint32_t (&b_off)[LB]) {
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  int expert, row0, row_end;
+  row_tile_find<BM>(s_scan, E, L / n_tiles_n, expert, row0, row_end);
+  const int s_prev = expert ? s_scan[expert - 1] : 0;
+  const int mt = s_scan[expert] - s_prev;
+  const int local = L - n_tiles_n * s_prev;
+  const int n_tile = local / mt, m_tile = local - n_tile * mt;
+  tl.row0 = s_scan[E + 1 + expert] + m_tile * BM;
+  tl.row_end = row_end;
+  tl.n0 = n_tile * NCOL;
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = (wave * LA + i) * RPI + lane / CPR;  // tile row written by this lane
+    const int lc = (lane % CPR) ^ swz_f<BK>(r);       // logical chunk for its slot
+    int gi = tl.row0 + r;
+    gi = gi < row_end ? gi : row_end - 1;
+    const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
+    a_off[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)lc * 8u) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wave * LB + i) * RPI + lane / CPR;
+    const int lc = (lane % CPR) ^ swz_f<BK>(r);
+    int n = tl.n0 + (GATEUP ? (r & 127) : r);
+    n = n < N_out ? n : N_out - 1;
+    b_off[i] = (((uint32_t)expert * (uint32_t)N_out + (uint32_t)n) * (uint32_t)K +
+                (uint32_t)lc * 8u) * 2u;
+  }
+}
+
 // Persistent grouped GEMM: NW waves per block (2 x NW/2), OCC blocks per CU.
 //   tile: BM token rows x 256 weight rows, K staged BK at a time through NST
 //         LDS stages (NST - 1 stages of loads in flight under the MFMAs);
@@ -211,42 +257,38 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                       : (wn * NB * 32 + nb * 32 + (lane & 31));
   const int trow0 = wm * (BM / 2) + (lane & 31);
 
-  for (int t = blockIdx.x >> 3; t < chunk; t += nper) {
-    const int L = xcd * chunk + t;
-    if (L >= R) break;
-    // expert e owns tiles [ntn * S[e-1], ntn * S[e]); column major inside
-    int expert, row0, row_end;
-    row_tile_find<BM>(s_scan, E, L / n_tiles_n, expert, row0, row_end);
-    const int s_prev = expert ? s_scan[expert - 1] : 0;
-    const int mt = s_scan[expert] - s_prev;
-    const int local = L - n_tiles_n * s_prev;
-    const int n_tile = local / mt, m_tile = local - n_tile * mt;
-    row0 = s_scan[E + 1 + expert] + m_tile * BM;
-    const int n0 = n_tile * NCOL;
+  const char* abase = reinterpret_cast<const char*>(act);
+  // B rows [0, 128) of a gate/up tile come from W_gate, [128, 256) from W_up
+  const char* bbase = reinterpret_cast<const char*>((GATEUP && wave >= NW / 2) ? w1 : w0);
+  // With two stages and an even number of K stages, the last K stage of a tile
+  // computes from buffer 1 while buffer 0 is free: the next tile's first stage
+  // is loaded there during that step, and its latency hides behind the
+  // epilogue (no pipeline drain between tiles).
+  const bool can_prefetch = (NST == 2) && (nk % 2 == 0);
 
-    // per-lane source byte offsets of this wave's LA A and LB B loads
-    uint32_t a_off[LA], b_off[LB];
+  int t = blockIdx.x >> 3;
+  bool have = t < chunk && xcd * chunk + t < R;
+  GemmTile cur;
+  uint32_t a_off[LA], b_off[LB];
+  if (have)
+    tile_setup<GATEUP, BM, BK, NW, NCOL, LA, LB>(xcd * chunk + t, n_tiles_n, E, K, N_out, k_top,
+                                                 s_scan, sorted_pair, wave, lane, cur, a_off,
+                                                 b_off);
+  bool staged = false;  // first stage of `cur` already loaded by the previous tile
+  while (have) {
+    const int tn = t + nper;
+    const bool have_n = tn < chunk && xcd * chunk + tn < R;
+    GemmTile nxt{};
+    uint32_t a_offn[LA], b_offn[LB];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = (wave * LA + i) * RPI + lane / CPR;  // tile row written by this lane
-      const int lc = (lane % CPR) ^ swz_f<BK>(r);       // logical chunk for its slot
-      int gi = row0 + r;
-      gi = gi < row_end ? gi : row_end - 1;
-      const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
-      a_off[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)lc * 8u) * 2u;
-    }
+    for (int i = 0; i < LA; ++i) a_offn[i] = 0u;
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = (wave * LB + i) * RPI + lane / CPR;
-      const int lc = (lane % CPR) ^ swz_f<BK>(r);
-      int n = n0 + (GATEUP ? (r & 127) : r);
-      n = n < N_out ? n : N_out - 1;
-      b_off[i] = (((uint32_t)expert * (uint32_t)N_out + (uint32_t)n) * (uint32_t)K +
-                  (uint32_t)lc * 8u) * 2u;
-    }
-    const char* abase = reinterpret_cast<const char*>(act);
-    // B rows [0, 128) of a gate/up tile come from W_gate, [128, 256) from W_up
-    const char* bbase = reinterpret_cast<const char*>((GATEUP && wave >= NW / 2) ? w1 : w0);
+    for (int i = 0; i < LB; ++i) b_offn[i] = 0u;
+    if (have_n)
+      tile_setup<GATEUP, BM, BK, NW, NCOL, LA, LB>(xcd * chunk + tn, n_tiles_n, E, K, N_out,
+                                                   k_top, s_scan, sorted_pair, wave, lane, nxt,
+                                                   a_offn, b_offn);
+    const bool prefetch = can_prefetch && have_n;
 
     f32x16_t acc[NB][MB];
 #pragma unroll
@@ -257,15 +299,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
     bf16x8_t fa[2][NB], fb[2][MB];
 
-    // prologue: NST - 1 stages in flight, first fragments of stage 0
-    for (int st = 0; st < NST - 1 && st < nk; ++st)
-      dma_stage<BK, BM, NW>(smem + st * STAGE, smem + st * STAGE + BM * BK, abase, bbase, a_off,
-                            b_off, (uint32_t)(st * BK) * 2u, wave);
-    wait_vmcnt((LA + LB) * ((nk - 1 < NST - 2 ? nk - 1 : NST - 2)));
+    // prologue: NST - 1 stages in flight (unless prefetched), first fragments
+    if (!staged) {
+      for (int st = 0; st < NST - 1 && st < nk; ++st)
+        dma_stage<BK, BM, NW>(smem + st * STAGE, smem + st * STAGE + BM * BK, abase, bbase, a_off,
+                              b_off, (uint32_t)(st * BK) * 2u, wave);
+      wait_vmcnt((LA + LB) * ((nk - 1 < NST - 2 ? nk - 1 : NST - 2)));
+    } else {
+      wait_vmcnt(0);
+    }
     lds_barrier();
     stage_frag<BK, MB, NB>(smem, smem + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
 
-    for (int kt = 0; kt < nk; ++kt) {
+    const int nk_main = prefetch ? nk - 1 : nk;
+    for (int kt = 0; kt < nk_main; ++kt) {
       uint16_t* dA = smem + ((kt + NST - 1) % NST) * STAGE;
       const uint16_t* cA = smem + (kt % NST) * STAGE;
       const uint16_t* nA = smem + ((kt + 1) % NST) * STAGE;
@@ -277,7 +324,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                                     ahead > 0 ? (LA + LB) * ahead : 0, acc, fa, fb, wrow, trow0,
                                     lane, sw, wave);
     }
-    __syncthreads();  // every wave done with the LDS stages before the next tile's loads
+    if (prefetch) {
+      // last K stage (buffer 1) while the next tile's stage 0 loads into buffer 0;
+      // the fragments read after its barrier are stale and unused
+      gemm_step<BK, BM, NW, MB, NB>(smem, smem + BM * BK, true, abase, bbase, a_offn, b_offn, 0u,
+                                    smem + STAGE, smem + STAGE + BM * BK, smem, smem + BM * BK,
+                                    LA + LB, acc, fa, fb, wrow, trow0, lane, sw, wave);
+    }
+    // No barrier here: the epilogue touches no LDS, and the next tile's first
+    // LDS writes are ordered by the barriers of its prologue and first step.
+    const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
 
     // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
 #pragma unroll
@@ -316,6 +372,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
         }
       }
     }
+
+    staged = prefetch;
+    cur = nxt;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) a_off[i] = a_offn[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) b_off[i] = b_offn[i];
+    t = tn;
+    have = have_n;
   }
 }
 
