@@ -67,28 +67,33 @@ __device__ __forceinline__ int swz_f(int r) {
   return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);   // 4 chunks per row
 }
 
-// LDS-DMA of one K stage: this wave's BK/8 A and BK/8 B load instructions.
-// Lane l of an instruction lands at M0 + 16 l, i.e. the instruction fills
-// 1024 / (2 BK) consecutive tile rows; a_off / b_off already hold each lane's
-// source row and (swizzled) chunk.
+// LDS-DMA of one K stage: this wave's BK/8 A and BK/8 B load instructions
+// (buffer_load_dwordx4 ... lds). Lane l of an instruction lands at M0 + 16 l,
+// i.e. the instruction fills 1024 / (2 BK) consecutive tile rows; a_off / b_off
+// hold each lane's source row and (swizzled) chunk, the K offset of the stage
+// is the scalar offset. Buffer (MUBUF) rather than global (FLAT-encoded) loads:
+// an outstanding FLAT load may count against both the vector-memory and the
+// LDS counter, which makes the compiler wait for every LDS read in full
+// (lgkmcnt(0)) while stage loads are in flight; with buffer loads it waits
+// only for the fragments it needs.
 template <int BK, int BM, int NW>
 __device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* __restrict__ dB,
-                                          const char* abase, const char* bbase,
+                                          __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
                                           int wave) {
   constexpr int CPR = BK / 8, RPI = 64 / CPR;
   constexpr int LA = BM * BK / (512 * NW), LB = 256 * BK / (512 * NW);  // per wave
 #pragma unroll
   for (int i = 0; i < LA; ++i)
-    __builtin_amdgcn_global_load_lds(abase + a_off[i] + kb,
-                                     (lds_void_t*)(dA + (wave * LA + i) * RPI * BK), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dA + (wave * LA + i) * RPI * BK), 16,
+                                             a_off[i], kb, 0, 0);
 #pragma unroll
   for (int i = 0; i < LB; ++i)
-    __builtin_amdgcn_global_load_lds(bbase + b_off[i] + kb,
-                                     (lds_void_t*)(dB + (wave * LB + i) * RPI * BK), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dB + (wave * LB + i) * RPI * BK), 16,
+                                             b_off[i], kb, 0, 0);
 }
 
-// Fragments of k step kk of a stage: 4 weight blocks (A operand), 4 token
+// Fragments of k step kk of a stage: NB weight blocks (A operand), MB token
 // blocks (B operand), 16 bytes per lane each.
 template <int BK, int MB, int NB>
 __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
@@ -115,8 +120,9 @@ __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
 // every fragment read; the explicit wait_vmcnt + lds_barrier order them.
 template <int BK, int BM, int NW, int MB, int NB>
 __device__ __forceinline__ void gemm_step(
-    uint16_t* __restrict__ dA, uint16_t* __restrict__ dB, bool issue_next, const char* abase,
-    const char* bbase, const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
+    uint16_t* __restrict__ dA, uint16_t* __restrict__ dB, bool issue_next,
+    __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase, const uint32_t* a_off,
+    const uint32_t* b_off, uint32_t kb,
     const uint16_t* __restrict__ cA, const uint16_t* __restrict__ cB,
     const uint16_t* __restrict__ nA, const uint16_t* __restrict__ nB, int vm_allow,
     f32x16_t (&acc)[NB][MB], bf16x8_t (&fa)[2][NB], bf16x8_t (&fb)[2][MB],
@@ -138,15 +144,14 @@ __device__ __forceinline__ void gemm_step(
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][nb], fb[kk & 1][mb],
                                                               acc[nb][mb], 0, 0, 0);
   }
-  // interleave the next k step's fragment reads with the MFMAs
-  constexpr int NR = NB + MB, PER = (NB * MB + NR - 1) / NR;
+  // per k step: first all fragment reads of the next k step, then this step's
+  // MFMAs, so each read has a whole step of MFMAs to land before its use
+  constexpr int NR = NB + MB;
 #pragma unroll
-  for (int kk = 0; kk + 1 < KK; ++kk)
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+  for (int kk = 0; kk + 1 < KK; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);
+  }
   __builtin_amdgcn_sched_group_barrier(0x008, NH * MB, 0);
   wait_vmcnt(vm_allow);
   lds_barrier();
@@ -167,7 +172,7 @@ __device__ __forceinline__ void gemm_step(
 // Location and per-lane load offsets of tile L (column tile major inside an
 // expert: expert e owns tiles [ntn * S[e-1], ntn * S[e])).
 struct GemmTile {
-  int row0, row_end, n0;
+  int row0, row_end, n0, expert;
 };
 
 template <bool GATEUP, int BM, int BK, int NW, int NCOL, int LA, int LB>
@@ -186,6 +191,7 @@ __device__ __forceinline__ void tile_setup(int L, int n_tiles_n, int E, int K, i
   tl.row0 = s_scan[E + 1 + expert] + m_tile * BM;
   tl.row_end = row_end;
   tl.n0 = n_tile * NCOL;
+  tl.expert = expert;
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int r = (wave * LA + i) * RPI + lane / CPR;  // tile row written by this lane
@@ -201,9 +207,14 @@ __device__ __forceinline__ void tile_setup(int L, int n_tiles_n, int E, int K, i
     const int lc = (lane % CPR) ^ swz_f<BK>(r);
     int n = tl.n0 + (GATEUP ? (r & 127) : r);
     n = n < N_out ? n : N_out - 1;
-    b_off[i] = (((uint32_t)expert * (uint32_t)N_out + (uint32_t)n) * (uint32_t)K +
-                (uint32_t)lc * 8u) * 2u;
+    b_off[i] = ((uint32_t)n * (uint32_t)K + (uint32_t)lc * 8u) * 2u;
   }
+}
+
+// Buffer descriptor of a byte range (raw addressing, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
 // Persistent grouped GEMM: NW waves per block (2 x NW/2), OCC blocks per CU.
@@ -241,7 +252,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
   __shared__ __align__(1024) uint16_t smem[NST * STAGE];
   __shared__ int s_scan[2 * 256 + 2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave & 1, wn = wave >> 1;
   const int R = row_tile_scan<BM>(offsets, E, s_scan) * n_tiles_n;
   const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3;
@@ -257,9 +269,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                       : (wn * NB * 32 + nb * 32 + (lane & 31));
   const int trow0 = wm * (BM / 2) + (lane & 31);
 
-  const char* abase = reinterpret_cast<const char*>(act);
+  // A operand: the activation rows (x for gate/up, h for down); offsets stay
+  // below 2^32 bytes (checked on the host)
+  const __amdgpu_buffer_rsrc_t abase = make_rsrc(act, 0xFFFFFFFFu);
   // B rows [0, 128) of a gate/up tile come from W_gate, [128, 256) from W_up
-  const char* bbase = reinterpret_cast<const char*>((GATEUP && wave >= NW / 2) ? w1 : w0);
+  const uint16_t* wsel = (GATEUP && wave >= NW / 2) ? w1 : w0;
+  const uint32_t wbytes = (uint32_t)N_out * (uint32_t)K * 2u;  // one expert's matrix
   // With two stages and an even number of K stages, the last K stage of a tile
   // computes from buffer 1 while buffer 0 is free: the next tile's first stage
   // is loaded there during that step, and its latency hides behind the
@@ -289,6 +304,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                                                    k_top, s_scan, sorted_pair, wave, lane, nxt,
                                                    a_offn, b_offn);
     const bool prefetch = can_prefetch && have_n;
+    const __amdgpu_buffer_rsrc_t bbase =
+        make_rsrc(wsel + (size_t)__builtin_amdgcn_readfirstlane(cur.expert) * N_out * K, wbytes);
+    const __amdgpu_buffer_rsrc_t bbase_n =
+        make_rsrc(wsel + (size_t)__builtin_amdgcn_readfirstlane(have_n ? nxt.expert : 0) * N_out * K,
+                  wbytes);
 
     f32x16_t acc[NB][MB];
 #pragma unroll
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     if (prefetch) {
       // last K stage (buffer 1) while the next tile's stage 0 loads into buffer 0;
       // the fragments read after its barrier are stale and unused
-      gemm_step<BK, BM, NW, MB, NB>(smem, smem + BM * BK, true, abase, bbase, a_offn, b_offn, 0u,
+      gemm_step<BK, BM, NW, MB, NB>(smem, smem + BM * BK, true, abase, bbase_n, a_offn, b_offn, 0u,
                                     smem + STAGE, smem + STAGE + BM * BK, smem, smem + BM * BK,
                                     LA + LB, acc, fa, fb, wrow, trow0, lane, sw, wave);
     }

@@ -58,6 +58,8 @@ def test_workspace_size(lib):
     ((4, 64, 64, 17, 64, 1, 1), 2),   # k > 16
     ((4, 96, 8, 2, 64, 1, 1), 2),     # H % 64
     ((4, 64, 8, 2, 100, 1, 1), 2),    # I % 64
+    ((1, 65536, 2, 1, 32768, 1, 1), 2),     # H*I >= 2^31 (32-bit per-expert offsets)
+    ((1 << 20, 4096, 8, 2, 1024, 1, 1), 2),  # T*k*max(H,I) >= 2^31
 ])
 def test_config_validation_returns_status(lib, fields, status):
     c = binding.moe_config(*fields)
