@@ -36,15 +36,42 @@ __device__ __forceinline__ float silu(float g) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt vmcnt(n) for the small constant counts the pipeline needs
+// s_waitcnt vmcnt(n) for the counts the pipelines need (n <= 32; larger
+// counts wait for everything, which is always safe)
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
     case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
     case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
     case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
     case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
     case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
+    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+    case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+    case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
     case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
+    case 26: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+    case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
+    case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+    case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
@@ -356,11 +383,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
 
     // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
+    if constexpr (GATEUP) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = row0 + trow0 + mb * 32;
       if (row >= row_end) continue;
-      if (GATEUP) {
+      {
         uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)row * N_out;
 #pragma unroll
         for (int nb = 0; nb < NB / 2; ++nb) {
@@ -377,19 +405,41 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
             }
           }
         }
-      } else {
-        float* orow = static_cast<float*>(out) + (size_t)row * N_out;
+      }
+    }
+    } else {
+      // down: the fp32 tile goes through the LDS stage computed last (free
+      // now: its reads completed before the last stage barrier) in MB passes
+      // of 64 rows x 256 columns, so that each store instruction writes one
+      // contiguous 1 KB row. 16-byte chunk c of slab row s sits at chunk
+      // c ^ (s & 15): conflict-free for the column writes (16 rows, one chunk)
+      // and the row reads (one row, 16 chunks).
+      static_assert(BN * 64 * 4 <= STAGE * 2, "slab must fit in one stage");
+      float* slab = reinterpret_cast<float*>(smem + ((nk - 1) % NST) * STAGE);
+      const int srow_w = wm * 32 + (lane & 31);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * NB * 32 + nb * 32 + q * 8 + (lane >> 5) * 4;
-            if (col < N_out)
-              *reinterpret_cast<float4*>(orow + col) =
-                  make_float4(acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1],
-                              acc[nb][mb][q * 4 + 2], acc[nb][mb][q * 4 + 3]);
+            const int chunk = (wn * NB * 32 + nb * 32 + q * 8 + (lane >> 5) * 4) >> 2;
+            *reinterpret_cast<float4*>(slab + srow_w * BN + ((chunk ^ (srow_w & 15)) << 2)) =
+                make_float4(acc[nb][mb][q * 4 + 0], acc[nb][mb][q * 4 + 1],
+                            acc[nb][mb][q * 4 + 2], acc[nb][mb][q * 4 + 3]);
           }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < 64 / NW; ++i) {
+          const int sr = wave * (64 / NW) + i;                  // slab row
+          const int row = row0 + (sr >> 5) * 128 + mb * 32 + (sr & 31);
+          const float4 v =
+              *reinterpret_cast<const float4*>(slab + sr * BN + ((lane ^ (sr & 15)) << 2));
+          const int col = n0 + lane * 4;
+          if (row < row_end && col < N_out)
+            *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)row * N_out + col) = v;
         }
+        lds_barrier();
       }
     }
 
