@@ -151,6 +151,67 @@ int orc_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32
   return 0;
 }
 
+/* Expert capacity, [MOE-128x8] 容量因子设计: capacity = (tokens per batch /
+ * experts) x capacity factor. With k slots per token the per-expert load the
+ * factor applies to is T*k/E, so C = ceil(T * k * cf / E) (k = 1 is the
+ * page's formula). */
+int orc_capacity(int T, int E, int k, double cf) {
+  if (T < 1 || E < 1 || k < 1 || !(cf > 0.0)) return -1;
+  double c = ceil((double)T * (double)k * cf / (double)E);
+  if (c < 1.0) c = 1.0;
+  if (c > (double)T * k) c = (double)T * k;
+  return (int)c;
+}
+
+/* Capacity-limited dispatch, [QWEN3-ROUTE] §四 (inference routing with
+ * capacity: the tokens are taken in order, and an expert accepts a token while
+ * the number it has accepted is below its capacity):
+ *   walk the pairs p = t*k + j in increasing order; p is kept iff fewer than
+ *   `capacity` earlier pairs went to the same expert;
+ *   counts[e] = pairs routed to e (before the limit);
+ *   offsets = exclusive prefix sum of the kept counts;
+ *   sorted_pair = the kept pair ids grouped by expert, ascending inside a
+ *   group; pair_pos[p] = its position, or -1 for a dropped pair;
+ *   *dropped = number of dropped pairs. */
+int orc_dispatch_capacity(int T, int E, int k, int capacity, const int32_t* idx,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                          int32_t* pair_pos, int32_t* dropped) {
+  if (T < 0 || E < 1 || k < 1 || capacity < 1 || !idx || !counts || !offsets || !sorted_pair ||
+      !pair_pos || !dropped)
+    return -1;
+  const long P = (long)T * k;
+  int32_t* accepted = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (!accepted) return -1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  *dropped = 0;
+  for (long p = 0; p < P; ++p) { /* the walk: keep or drop, in pair order */
+    const int e = idx[p];
+    if (e < 0 || e >= E) {
+      free(accepted);
+      return -1;
+    }
+    counts[e] += 1;
+    if (accepted[e] < capacity) {
+      accepted[e] += 1;
+      pair_pos[p] = 0; /* kept: position filled in below */
+    } else {
+      pair_pos[p] = -1;
+      *dropped += 1;
+    }
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + accepted[e];
+  for (int e = 0; e < E; ++e) accepted[e] = offsets[e]; /* next free slot */
+  for (long p = 0; p < P; ++p) {
+    if (pair_pos[p] < 0) continue;
+    const int32_t pos = accepted[idx[p]]++;
+    sorted_pair[pos] = (int32_t)p;
+    pair_pos[p] = pos;
+  }
+  free(accepted);
+  return 0;
+}
+
 /* One expert MLP per requested row, [MOE-128x8] gate_proj / up_proj / down_proj
  * with the SwiGLU form down(silu(gate x) * up x), no biases:
  *   g_i = sum_h Wg[e,i,h] x[t,h],  u_i = sum_h Wu[e,i,h] x[t,h]
@@ -196,20 +257,31 @@ int orc_expert_rows(int H, int I, int dtype, const void* x, const void* wg, cons
 }
 
 /* Routing-weighted combine, [QWEN3-READ] forward code (expert output times its
- * routing weight, accumulated into the token's row):
- *   out[t,:] = sum_{j=0..k-1} w[t,j] * y_pair[t*k+j, :]   (slot order, double) */
-int orc_combine(int T, int H, int k, const double* w, const double* y_pair, double* out) {
+ * routing weight, accumulated into the token's row), over the kept slots:
+ *   out[t,:] = sum_{j : keep[t,j]} w[t,j] * y_pair[t*k+j, :]  (slot order, double)
+ * keep (nullable: all kept) marks the slots that a capacity limit did not drop;
+ * a dropped slot contributes nothing. */
+int orc_combine_kept(int T, int H, int k, const double* w, const double* y_pair,
+                     const int8_t* keep, double* out) {
   if (T < 0 || H < 1 || k < 1 || !w || !y_pair || !out) return -1;
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < T; ++t) {
     for (int h = 0; h < H; ++h) {
       double s = 0.0;
-      for (int j = 0; j < k; ++j)
+      for (int j = 0; j < k; ++j) {
+        if (keep && !keep[(size_t)t * k + j]) continue;
         s += w[(size_t)t * k + j] * y_pair[((size_t)t * k + j) * H + h];
+      }
       out[(size_t)t * H + h] = s;
     }
   }
   return 0;
+}
+
+/* All slots kept:
+ *   out[t,:] = sum_{j=0..k-1} w[t,j] * y_pair[t*k+j, :]   (slot order, double) */
+int orc_combine(int T, int H, int k, const double* w, const double* y_pair, double* out) {
+  return orc_combine_kept(T, H, k, w, y_pair, NULL, out);
 }
 
 /* Load-balance statistics, [MOE-128x8] load-balancing section, n = E:
@@ -235,11 +307,13 @@ int orc_aux(int T, int E, int k, const int32_t* counts, const double* probs, dou
  * NULL): logits -> route -> experts -> combine, [QWEN3-READ] forward code.
  * n = number of listed tokens. Outputs are per listed token:
  *   logits [n,E] fp32, idx [n,k], w [n,k], out [n,H] double.
- * forced_idx [n,k] (nullable) replaces the selection. */
+ * forced_idx [n,k] (nullable) replaces the selection; keep [n,k] (nullable)
+ * marks the slots a capacity limit kept (the others contribute nothing). */
 int orc_forward_tokens(int T, int H, int E, int k, int I, int norm, int dtype, const void* x,
                        const void* wr, const float* bias, const void* wg, const void* wu,
                        const void* wd, int n, const int32_t* tokens, const int32_t* forced_idx,
-                       int round_h, float* logits, int32_t* idx, double* w, double* out) {
+                       const int8_t* keep, int round_h, float* logits, int32_t* idx, double* w,
+                       double* out) {
   if (T < 1 || n < 0 || !logits || !idx || !w || !out) return -1;
   const size_t rowb = (size_t)H * (dtype == 0 ? 4 : 2);
   /* gather the listed rows of x so the steps below see a dense [n,H] block */
@@ -262,7 +336,7 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int norm, int dtype, c
       ex[r * k + j] = idx[r * k + j];
     }
   if (orc_expert_rows(H, I, dtype, xs, wg, wu, wd, n * k, tok, ex, round_h, y)) goto done;
-  if (orc_combine(n, H, k, w, y, out)) goto done;
+  if (orc_combine_kept(n, H, k, w, y, keep, out)) goto done;
   rc = 0;
 done:
   free(xs);

@@ -47,11 +47,15 @@ def _load():
         lib.orc_dispatch.argtypes = [i, i, i, P, P, P, P, P]
         lib.orc_expert_rows.argtypes = [i, i, i, P, P, P, P, i, P, P, i, P]
         lib.orc_combine.argtypes = [i, i, i, P, P, P]
+        lib.orc_combine_kept.argtypes = [i, i, i, P, P, P, P]
+        lib.orc_capacity.argtypes = [i, i, i, ctypes.c_double]
+        lib.orc_dispatch_capacity.argtypes = [i, i, i, i, P, P, P, P, P, P]
         lib.orc_aux.argtypes = [i, i, i, P, P, P, P, P]
-        lib.orc_forward_tokens.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P, i,
+        lib.orc_forward_tokens.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P, P, i,
                                            P, P, P, P]
         for f in (lib.orc_logits, lib.orc_route, lib.orc_dispatch, lib.orc_expert_rows,
-                  lib.orc_combine, lib.orc_aux, lib.orc_forward_tokens):
+                  lib.orc_combine, lib.orc_combine_kept, lib.orc_capacity,
+                  lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -122,6 +126,29 @@ def dispatch(idx: np.ndarray, E: int):
     return counts, offsets, sp, pp
 
 
+def capacity(T: int, E: int, k: int, cf: float) -> int:
+    """Expert capacity ceil(T*k*cf/E) (at least 1, at most T*k)."""
+    c = _load().orc_capacity(T, E, k, float(cf))
+    _check(0 if c > 0 else -1, "capacity")
+    return c
+
+
+def dispatch_capacity(idx: np.ndarray, E: int, cap: int):
+    """Capacity-limited dispatch. Returns (counts [E] before the limit,
+    offsets [E+1] of the kept pairs, sorted_pair [P] (first offsets[E] valid),
+    pair_pos [P] (-1 = dropped), dropped)."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.full(T * k, -1, np.int32)
+    pp = np.empty(T * k, np.int32)
+    dropped = np.zeros(1, np.int32)
+    _check(_load().orc_dispatch_capacity(T, E, k, int(cap), _p(idx), _p(counts), _p(offsets),
+                                         _p(sp), _p(pp), _p(dropped)), "dispatch_capacity")
+    return counts, offsets, sp, pp, int(dropped[0])
+
+
 def expert_rows(x, w_gate, w_up, w_down, tok, ex, round_h: bool = False) -> np.ndarray:
     """SwiGLU expert output (float64 [n,H]) for rows (token tok[r], expert ex[r])."""
     x, w_gate, w_up, w_down = _c(x), _c(w_gate), _c(w_up), _c(w_down)
@@ -138,14 +165,19 @@ def expert_rows(x, w_gate, w_up, w_down, tok, ex, round_h: bool = False) -> np.n
     return y
 
 
-def combine(w: np.ndarray, y_pair: np.ndarray) -> np.ndarray:
-    """out[t] = sum_j w[t,j] * y_pair[t*k+j] (float64)."""
+def combine(w: np.ndarray, y_pair: np.ndarray, keep: np.ndarray | None = None) -> np.ndarray:
+    """out[t] = sum_j w[t,j] * y_pair[t*k+j] over the kept slots (float64)."""
     w = _c(w, np.float64)
     y_pair = _c(y_pair, np.float64)
     T, k = w.shape
     H = y_pair.shape[1]
     out = np.empty((T, H), np.float64)
-    _check(_load().orc_combine(T, H, k, _p(w), _p(y_pair), _p(out)), "combine")
+    if keep is None:
+        _check(_load().orc_combine(T, H, k, _p(w), _p(y_pair), _p(out)), "combine")
+    else:
+        keep = _c(keep, np.int8)
+        _check(_load().orc_combine_kept(T, H, k, _p(w), _p(y_pair), _p(keep), _p(out)),
+               "combine")
     return out
 
 
@@ -161,8 +193,10 @@ def aux(counts: np.ndarray, probs: np.ndarray, k: int):
     return f, P, float(a[0])
 
 
-def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool = False):
-    """Block forward for the listed tokens (all when None).
+def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool = False,
+                   keep=None):
+    """Block forward for the listed tokens (all when None); keep [n,k] (None:
+    all kept) marks the slots a capacity limit kept.
 
     inp: dict with x, w_router, w_gate, w_up, w_down, logit_bias (None or
     float32 [E]); cfg: an object with T, H, E, k, I, norm.
@@ -176,6 +210,7 @@ def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool =
     tokens = _c(tokens, np.int32)
     n = tokens.shape[0]
     forced_idx = _c(forced_idx, np.int32)
+    keep = _c(keep, np.int8)
     k = cfg.k
     lg = np.empty((n, cfg.E), np.float32)
     idx = np.empty((n, k), np.int32)
@@ -183,6 +218,7 @@ def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool =
     out = np.empty((n, H), np.float64)
     _check(_load().orc_forward_tokens(T, H, cfg.E, k, cfg.I, int(bool(cfg.norm)),
                                       _dtype_code(x), _p(x), _p(wr), _p(bias), _p(wg), _p(wu),
-                                      _p(wd), n, _p(tokens), _p(forced_idx), int(round_h),
+                                      _p(wd), n, _p(tokens), _p(forced_idx), _p(keep),
+                                      int(round_h),
                                       _p(lg), _p(idx), _p(w), _p(out)), "forward_tokens")
     return {"logits": lg, "idx": idx, "w": w, "out": out}

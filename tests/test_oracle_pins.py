@@ -163,6 +163,95 @@ def test_dispatch_matches_stable_sort(orc, seed):
         assert (flat[grp] == e).all() and (np.diff(grp) > 0).all()
 
 
+def _capacity_by_flatnonzero(idx, E, cap):
+    """Kept pairs of each expert = its first `cap` pair ids (numpy
+    flatnonzero gives them ascending): a characterisation independent of the
+    oracle's sequential walk."""
+    flat = idx.ravel()
+    kept = [np.flatnonzero(flat == e)[:cap] for e in range(E)]
+    offsets = np.concatenate([[0], np.cumsum([len(g) for g in kept])]).astype(np.int32)
+    sp = np.concatenate(kept).astype(np.int32) if flat.size else np.zeros(0, np.int32)
+    pp = np.full(flat.size, -1, np.int32)
+    pp[sp] = np.arange(sp.size, dtype=np.int32)
+    return offsets, sp, pp
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_capacity_dispatch_keeps_first_pairs_of_each_expert(orc, seed):
+    rng = _rng(260 + seed)
+    E = int(rng.integers(1, 24))
+    k = int(rng.integers(1, min(E, 6) + 1))
+    T = int(rng.integers(1, 200))
+    # skewed: low expert ids are popular, so a tight capacity drops pairs
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(
+        np.int32)
+    cap = int(rng.integers(1, max(2, T * k // E + 2)))
+    counts, offsets, sp, pp, dropped = orc.dispatch_capacity(idx, E, cap)
+    ref_off, ref_sp, ref_pp = _capacity_by_flatnonzero(idx, E, cap)
+    assert (counts == np.bincount(idx.ravel(), minlength=E)).all()  # before the limit
+    assert (offsets == ref_off).all()
+    assert (sp[: offsets[E]] == ref_sp).all()
+    assert (pp == ref_pp).all()
+    assert dropped == int(np.maximum(counts - cap, 0).sum()) == int((pp < 0).sum())
+
+
+def test_capacity_limits(orc):
+    rng = _rng(270)
+    E, k, T = 12, 3, 150
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    # a capacity at least the largest load drops nothing: the dropless dispatch
+    c2, o2, sp2, pp2, d2 = orc.dispatch_capacity(idx, E, int(counts.max()))
+    assert d2 == 0 and (o2 == offsets).all() and (sp2 == sp).all() and (pp2 == pp).all()
+    # capacity 1: every touched expert keeps exactly its lowest pair id
+    _, o1, sp1, pp1, d1 = orc.dispatch_capacity(idx, E, 1)
+    flat = idx.ravel()
+    touched = np.flatnonzero(counts)
+    assert (sp1[: o1[E]] == [np.flatnonzero(flat == e)[0] for e in touched]).all()
+    assert d1 == T * k - len(touched)
+
+
+def test_capacity_formula(orc):
+    # [MOE-128x8] 容量因子设计: (tokens / experts) x factor, per routed slot
+    assert orc.capacity(16384, 128, 8, 1.25) == 1280
+    assert orc.capacity(16384, 128, 8, 1.0) == 1024
+    assert orc.capacity(1000, 8, 1, 1.25) == 157   # k = 1: the page's formula, 156.25 rounded up
+    assert orc.capacity(64, 128, 8, 1.25) == 5     # 5.0 exactly
+    assert orc.capacity(3, 128, 1, 1.0) == 1       # never below one
+
+
+def test_combine_kept_masks_slots(orc):
+    rng = _rng(280)
+    T, k, H = 9, 3, 5
+    w = rng.random((T, k))
+    y = rng.standard_normal((T * k, H))
+    keep = rng.random((T, k)) < 0.6
+    out = orc.combine(w, y, keep)
+    ref = np.einsum("tj,tjh->th", w * keep, y.reshape(T, k, H))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+    assert (orc.combine(w, y, np.zeros((T, k), bool)) == 0.0).all()
+    np.testing.assert_array_equal(orc.combine(w, y, np.ones((T, k), bool)), orc.combine(w, y))
+
+
+def test_forward_keep_mask(orc):
+    cfg = MoEConfig("keep", T=12, H=64, E=6, k=3, I=64, norm=True, dtype="f32")
+    inp = make_inputs(cfg)
+    full = orc.forward_tokens(inp, cfg)
+    same = orc.forward_tokens(inp, cfg, keep=np.ones((cfg.T, cfg.k), np.int8))
+    np.testing.assert_array_equal(full["out"], same["out"])
+    keep = np.zeros((cfg.T, cfg.k), np.int8)
+    keep[:, 0] = 1  # only the top slot: w_0 * MLP_{e_0}(x)
+    top = orc.forward_tokens(inp, cfg, keep=keep)
+    x = as_f32(inp["x"]).astype(np.float64)
+    for t in range(cfg.T):
+        e = full["idx"][t, 0]
+        mlp = _swiglu_np(x[t:t + 1], *(as_f32(inp[n][e]).astype(np.float64)
+                                      for n in ("w_gate", "w_up", "w_down")))
+        np.testing.assert_allclose(top["out"][t], full["w"][t, 0] * mlp[0], rtol=1e-10,
+                                   atol=1e-12)
+
+
 # --------------------------------------------------------------------- expert
 
 
