@@ -1,6 +1,7 @@
 """Benchmark of the MoE block forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--capacity-factor CF]   # capacity-limited dispatch, C = ceil(T*k*CF/E)
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
 
 A step is one moe_layer_forward (router, dispatch, gate/up GEMM, down GEMM,
@@ -75,21 +76,21 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gate_up_algorithmic(cfg, counts: np.ndarray):
-    """Algorithmic FLOPs and bytes of one gate/up launch: 2 GEMMs of
-    2*H*I FLOP per routed pair; bytes = gate+up weights of the touched experts
-    + the x rows read + h written."""
+def gate_up_algorithmic(cfg, counts: np.ndarray, rows: int):
+    """Algorithmic FLOPs and bytes of one gate/up launch over `rows` routed
+    (kept) pairs: 2 GEMMs of 2*H*I FLOP per pair; bytes = gate+up weights of
+    the touched experts + the x rows read + h written."""
     eb = 2 if cfg.dtype == "bf16" else 4
     touched = int((counts > 0).sum())
-    flops = 4.0 * cfg.H * cfg.I * cfg.P
-    bytes_ = touched * 2.0 * cfg.I * cfg.H * eb + cfg.T * cfg.H * eb + cfg.P * cfg.I * eb
+    flops = 4.0 * cfg.H * cfg.I * rows
+    bytes_ = touched * 2.0 * cfg.I * cfg.H * eb + cfg.T * cfg.H * eb + rows * cfg.I * eb
     return flops, bytes_, touched
 
 
-def layer_algorithmic(cfg, counts: np.ndarray):
+def layer_algorithmic(cfg, counts: np.ndarray, rows: int):
     eb = 2 if cfg.dtype == "bf16" else 4
     touched = int((counts > 0).sum())
-    flops = cfg.T * (2.0 * cfg.H * cfg.E + 6.0 * cfg.H * cfg.I * cfg.k)
+    flops = cfg.T * 2.0 * cfg.H * cfg.E + 6.0 * cfg.H * cfg.I * rows
     bytes_ = touched * 3.0 * cfg.H * cfg.I * eb + cfg.E * cfg.H * eb + 2.0 * cfg.T * cfg.H * eb
     return flops, bytes_
 
@@ -133,6 +134,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="> 0: capacity-limited dispatch with C = ceil(T*k*CF/E)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times: the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -168,7 +171,9 @@ def main():
     t0 = time.perf_counter()
     inp = make_inputs(cfg)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
-    blk = binding.MoEBlock(cfg, inp)
+    cap = binding.capacity(binding.make_config(cfg), args.capacity_factor) \
+        if args.capacity_factor > 0 else 0
+    blk = binding.MoEBlock(cfg, inp, capacity=cap)
     x = binding.to_device(inp["x"])
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
@@ -201,7 +206,10 @@ def main():
     pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     h = torch.empty(T * k, cfg.I, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
     binding.router_topk(c, x, blk.w_router, blk.logit_bias, None, idx, wts)
-    binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+    if cap:
+        binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
+    else:
+        binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
     for _ in range(2):
         binding.expert_gate_up(c, x, sp, offsets, blk.w_gate, blk.w_up, h)
     torch.cuda.synchronize()
@@ -212,12 +220,13 @@ def main():
     torch.cuda.synchronize()
     gu_ms = ev0.elapsed_time(ev1) / args.steps
     cnt = counts.cpu().numpy()
-    gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt)
-    lflops, lbytes = layer_algorithmic(cfg, cnt)
+    rows = int(offsets[E].item())  # kept pairs (all of them without a capacity)
+    gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt, rows)
+    lflops, lbytes = layer_algorithmic(cfg, cnt, rows)
     log(f"gate/up kernel: {gu_ms:.4f} ms/launch, touched experts {touched}/{E}")
 
     decode = cfg.P <= 4 * cfg.E  # weight-streaming regime: bound by HBM
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name) if not cap else None
     if decode:
         achieved = gbytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -238,6 +247,9 @@ def main():
     roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
 
     value = T / (ms_step * 1e-3)
+    if cap:
+        line_cap = {"capacity_factor": args.capacity_factor, "capacity": cap,
+                    "dropped_pairs": int(blk.dropped.item()), "kept_pairs": rows}
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -250,6 +262,8 @@ def main():
                   "hbm_gbs_min_bytes": lbytes / (ms_step * 1e-3) / 1e9,
                   "touched_experts": touched, "wall_ms_per_step": wall * 1e3 / args.steps},
     }
+    if cap:
+        line["config"].update(line_cap)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

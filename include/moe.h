@@ -140,6 +140,37 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t*
                         int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Expert capacity for a capacity factor cf: ceil(T*k*cf / E), at least 1 and
+ * at most T*k. [MOE-128x8] 容量因子设计 gives capacity = (tokens per batch /
+ * experts) x factor (factor 1.0 - 1.25); with k slots per token the per-expert
+ * load the factor scales is T*k/E (k = 1 is the page's formula).
+ * Host-only and pure; returns 0 if `cfg` is invalid or cf <= 0. */
+int32_t moe_capacity(const moe_config* cfg, float capacity_factor);
+
+/* Capacity-limited dispatch. [QWEN3-ROUTE] §四 (inference routing with expert
+ * capacities: the tokens are taken in order and an expert accepts a token
+ * while it has accepted fewer than its capacity). Pair p = t*k + j of expert e
+ * is kept iff fewer than `capacity` pairs of e have a smaller pair id, i.e.
+ * each expert keeps its first `capacity` pairs in pair order.
+ *   capacity       >= 1 (see moe_capacity).
+ *   expert_counts  [E]   int32 out: pairs routed to e, BEFORE the limit.
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of the kept counts
+ *                  min(n_e, capacity); [E] = number of kept pairs.
+ *   sorted_pair    [T*k] int32 out: the kept pair ids grouped by expert,
+ *                  ascending inside a group; entries past offsets[E] are not
+ *                  written.
+ *   pair_pos       [T*k] int32 out: position of each kept pair in
+ *                  sorted_pair, -1 for a dropped pair.
+ *   dropped        [1] int32 out (may be NULL): number of dropped pairs.
+ * The expert and combine entry points take these arrays unchanged: the
+ * experts see only the kept rows, and a dropped slot adds nothing to its
+ * token's output (its routing weight is not redistributed). */
+moe_status moe_dispatch_capacity(const moe_config* cfg, const int32_t* topk_idx,
+                                 int32_t capacity, int32_t* expert_counts,
+                                 int32_t* expert_offsets, int32_t* sorted_pair,
+                                 int32_t* pair_pos, int32_t* dropped, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* Experts, first half: for every sorted row i of expert e (offsets[e] <= i <
  * offsets[e+1]) with token t = sorted_pair[i] / k:
  *     h[i, :] = silu(W_gate[e] x_t) * (W_up[e] x_t),  silu(z) = z / (1 + e^-z)
@@ -171,6 +202,7 @@ moe_status moe_expert_swiglu(const moe_config* cfg, const void* x, const int32_t
 /* Combine: out[t, :] = sum_{j=0}^{k-1} topk_w[t,j] * y_sorted[pair_pos[t*k+j], :]
  * summed in fp32 in slot order j = 0..k-1 and rounded once to dtype; no
  * atomics. Replaces the index_add_ scatter of [QWEN3-READ] (forward code).
+ * A slot with pair_pos < 0 (dropped by moe_dispatch_capacity) adds nothing.
  *   y_sorted [T*k,H] fp32; pair_pos [T*k] int32; topk_w [T,k] fp32;
  *   out [T,H] dtype. */
 moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_t* pair_pos,
@@ -182,6 +214,13 @@ moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_
 moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
                          moe_aux_out out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Options of moe_layer_forward_ex. Zero-initialised = the plain forward. */
+typedef struct {
+  int32_t capacity; /* 0: dropless. > 0: capacity-limited dispatch with this
+                       capacity (moe_dispatch_capacity; see moe_capacity) */
+  int32_t* dropped; /* [1] int32 out or NULL: pairs dropped by the capacity */
+} moe_options;
 
 /* The whole block: router -> dispatch -> experts -> combine -> statistics,
  * all on `stream`, with no host synchronisation.
@@ -196,6 +235,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                              const void* w_down, void* out, float* router_logits,
                              int32_t* topk_idx, float* topk_w, moe_aux_out aux,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_layer_forward with options (opt may be NULL: all defaults). With a
+ * capacity the dispatch is moe_dispatch_capacity's; the statistics count the
+ * routed pairs (before the limit). */
+moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, const void* x,
+                                const void* w_router, const float* logit_bias,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                void* out, float* router_logits, int32_t* topk_idx,
+                                float* topk_w, moe_aux_out aux, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -22,8 +22,9 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # public entry points of include/moe.h
 EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_dispatch",
-           "moe_expert_gate_up", "moe_expert_down", "moe_expert_swiglu", "moe_combine",
-           "moe_aux_stats", "moe_layer_forward")
+           "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
+           "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_layer_forward",
+           "moe_layer_forward_ex")
 
 
 class moe_config(ctypes.Structure):
@@ -31,6 +32,10 @@ class moe_config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class moe_options(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p)]
 
 
 class moe_aux_out(ctypes.Structure):
@@ -54,15 +59,19 @@ def load(path: str = LIB_PATH):
     st = ctypes.c_int
     lib.moe_workspace_size.argtypes, lib.moe_workspace_size.restype = [C], S
     lib.moe_status_string.argtypes, lib.moe_status_string.restype = [st], ctypes.c_char_p
+    lib.moe_capacity.argtypes, lib.moe_capacity.restype = [C, ctypes.c_float], ctypes.c_int32
     sig = {
         "moe_router_topk": [C, V, V, V, V, V, V, V],
         "moe_dispatch": [C, V, V, V, V, V, V, S, V],
+        "moe_dispatch_capacity": [C, V, ctypes.c_int32, V, V, V, V, V, V, S, V],
         "moe_expert_gate_up": [C, V, V, V, V, V, V, V, S, V],
         "moe_expert_down": [C, V, V, V, V, V, S, V],
         "moe_expert_swiglu": [C, V, V, V, V, V, V, V, V, S, V],
         "moe_combine": [C, V, V, V, V, V],
         "moe_aux_stats": [C, V, V, moe_aux_out, V, S, V],
         "moe_layer_forward": [C, V, V, V, V, V, V, V, V, V, V, moe_aux_out, V, S, V],
+        "moe_layer_forward_ex": [C, ctypes.POINTER(moe_options), V, V, V, V, V, V, V, V, V, V,
+                                 moe_aux_out, V, S, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -121,6 +130,21 @@ def dispatch(c: moe_config, topk_idx, counts, offsets, sorted_pair, pair_pos, ws
                                _stream()), "moe_dispatch")
 
 
+def capacity(c: moe_config, capacity_factor: float) -> int:
+    n = int(load().moe_capacity(ctypes.byref(c), float(capacity_factor)))
+    if n <= 0:
+        raise ValueError("invalid configuration or capacity factor")
+    return n
+
+
+def dispatch_capacity(c: moe_config, topk_idx, cap: int, counts, offsets, sorted_pair, pair_pos,
+                      ws, dropped=None):
+    _check(load().moe_dispatch_capacity(ctypes.byref(c), _ptr(topk_idx), int(cap), _ptr(counts),
+                                        _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
+                                        _ptr(dropped), _ptr(ws), ws.numel(), _stream()),
+           "moe_dispatch_capacity")
+
+
 def expert_gate_up(c: moe_config, x, sorted_pair, offsets, w_gate, w_up, h, ws=None):
     _check(load().moe_expert_gate_up(ctypes.byref(c), _ptr(x), _ptr(sorted_pair), _ptr(offsets),
                                      _ptr(w_gate), _ptr(w_up), _ptr(h), _ptr(ws),
@@ -165,6 +189,17 @@ def layer_forward(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, 
            "moe_layer_forward")
 
 
+def layer_forward_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, w_gate,
+                     w_up, w_down, out, ws, router_logits=None, topk_idx=None, topk_w=None,
+                     counts=None, f=None, P=None, aux=None):
+    _check(load().moe_layer_forward_ex(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
+                                       _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate),
+                                       _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(router_logits),
+                                       _ptr(topk_idx), _ptr(topk_w), _aux(counts, f, P, aux),
+                                       _ptr(ws), ws.numel(), _stream()),
+           "moe_layer_forward_ex")
+
+
 def to_device(a, device="cuda") -> torch.Tensor:
     """numpy input array (float32, or uint16 bf16 bits) -> GPU tensor of the
     matching torch dtype (bf16 bits are reinterpreted, not converted)."""
@@ -180,9 +215,12 @@ class MoEBlock:
     """Device-resident block: holds the weights and a workspace, runs the
     whole forward with one library call per step."""
 
-    def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda"):
+    def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0):
+        """capacity > 0: capacity-limited dispatch (see moe_capacity)."""
         self.cfg = cfg
         self.c = make_config(cfg)
+        self.dropped = torch.zeros(1, dtype=torch.int32, device=device)
+        self.opts = moe_options(int(capacity), _ptr(self.dropped)) if capacity else None
         self.w_router = to_device(inputs["w_router"], device)
         self.w_gate = to_device(inputs["w_gate"], device)
         self.w_up = to_device(inputs["w_up"], device)
@@ -203,10 +241,10 @@ class MoEBlock:
         """outputs=False: only `out` (logits, selection and statistics stay in
         the workspace / are not computed)."""
         if outputs:
-            layer_forward(self.c, x, self.w_router, self.logit_bias, self.w_gate, self.w_up,
-                          self.w_down, self.out, self.ws, self.logits, self.topk_idx, self.topk_w,
-                          self.counts, self.f, self.P, self.aux)
+            layer_forward_ex(self.c, self.opts, x, self.w_router, self.logit_bias, self.w_gate,
+                             self.w_up, self.w_down, self.out, self.ws, self.logits,
+                             self.topk_idx, self.topk_w, self.counts, self.f, self.P, self.aux)
         else:
-            layer_forward(self.c, x, self.w_router, self.logit_bias, self.w_gate, self.w_up,
-                          self.w_down, self.out, self.ws)
+            layer_forward_ex(self.c, self.opts, x, self.w_router, self.logit_bias, self.w_gate,
+                             self.w_up, self.w_down, self.out, self.ws)
         return self.out

@@ -31,9 +31,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k_r
   __shared__ float s_w[16];
   const int k = KC > 0 ? KC : k_rt;
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < k) {
-    s_pos[tid] = pair_pos[(size_t)t * k + tid];
-    s_w[tid] = topk_w[(size_t)t * k + tid];
+  if (tid < k) {  // a slot dropped by a capacity limit (pair_pos < 0) adds 0 * row 0
+    const int pos = pair_pos[(size_t)t * k + tid];
+    s_pos[tid] = pos < 0 ? 0 : pos;
+    s_w[tid] = pos < 0 ? 0.0f : topk_w[(size_t)t * k + tid];
   }
   __syncthreads();
   // y_sorted is fp32 for both element types; out is rounded once

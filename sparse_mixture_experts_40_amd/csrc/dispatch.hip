@@ -7,12 +7,18 @@
 // Pairs p = t*k + j are cut into chunks of kChunk consecutive ids, one block
 // each:
 //   hist    : per-chunk LDS histogram (integer LDS atomics: exact, order-free)
-//   scan    : one block; per-expert totals, exclusive scan over experts, and
-//             the start of every (chunk, expert) run
+//   scan    : one block; per-expert totals, kept counts min(total, capacity),
+//             exclusive scan of the kept counts, and the rank inside its expert
+//             of the first pair of every (chunk, expert) run
 //   scatter : each chunk walks its pairs in ascending order, 256 at a time; a
 //             lane's rank among equal experts comes from 8 ballots (one per
 //             bit of the expert id), wave counts go through LDS, so pairs of an
 //             expert land in ascending pair order (a stable sort).
+// Capacity ([MOE-128x8] 容量因子设计; [QWEN3-ROUTE] §四, tokens taken in order,
+// an expert accepts while below its capacity): the pair of rank r inside its
+// expert is kept iff r < capacity, i.e. each expert keeps its first
+// `capacity` pairs in pair order; a dropped pair gets pair_pos = -1. A
+// capacity of 0 keeps every pair.
 // No device-to-host traffic; everything stays on the stream.
 #include "moe_internal.h"
 
@@ -42,46 +48,56 @@ __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(int P, int E,
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
-    int nchunks, int E, const int32_t* __restrict__ hist, int32_t* __restrict__ base,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    int nchunks, int E, int cap, const int32_t* __restrict__ hist, int32_t* __restrict__ rank0,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dropped) {
   __shared__ int s_c[256];
+  __shared__ int s_drop;
   const int e = threadIdx.x;
+  if (e == 0) s_drop = 0;
   int tot = 0;
   if (e < E) {
 #pragma unroll 8
     for (int b = 0; b < nchunks; ++b) tot += hist[(size_t)b * E + e];
   }
-  s_c[e] = tot;
+  const int kept = (cap > 0 && tot > cap) ? cap : tot;
+  s_c[e] = kept;
   __syncthreads();
+  if (kept < tot) atomicAdd(&s_drop, tot - kept);  // integer: exact, order-free
   for (int d = 1; d < 256; d <<= 1) {  // inclusive scan over the 256 slots
     const int add = (e >= d) ? s_c[e - d] : 0;
     __syncthreads();
     s_c[e] += add;
     __syncthreads();
   }
-  const int excl = s_c[e] - tot;
+  const int excl = s_c[e] - kept;
   if (e < E) {
     if (counts) counts[e] = tot;
     if (offsets) offsets[e] = excl;
     if (offsets && e == E - 1) offsets[E] = s_c[e];
-    if (base) {
-      int run = excl;
+    if (rank0) {
+      int run = 0;
 #pragma unroll 8
       for (int b = 0; b < nchunks; ++b) {
-        base[(size_t)b * E + e] = run;
+        rank0[(size_t)b * E + e] = run;
         run += hist[(size_t)b * E + e];
       }
     }
   }
+  if (dropped && e == 0) *dropped = s_drop;
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
-    int P, int E, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
-    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
-  __shared__ int s_base[256];
+    int P, int E, int cap, const int32_t* __restrict__ idx, const int32_t* __restrict__ rank0,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int s_rank[256];  // rank inside its expert of this chunk's next pair
+  __shared__ int s_off[256];
   __shared__ int s_wc[4][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < E) s_base[tid] = base[(size_t)blockIdx.x * E + tid];
+  if (tid < E) {
+    s_rank[tid] = rank0[(size_t)blockIdx.x * E + tid];
+    s_off[tid] = offsets[tid];
+  }
 #pragma unroll
   for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
   __syncthreads();
@@ -101,14 +117,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     if (valid && rank == 0) s_wc[wave][v] = __popcll(same);
     __syncthreads();
     if (valid) {
-      int pos = s_base[v] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_wc[w][v];
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
+      int r = s_rank[v] + rank;
+      for (int w = 0; w < wave; ++w) r += s_wc[w][v];
+      if (cap <= 0 || r < cap) {
+        const int pos = s_off[v] + r;
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      } else {
+        pair_pos[p] = -1;
+      }
     }
     __syncthreads();
     if (tid < E) {
-      s_base[tid] += s_wc[0][tid] + s_wc[1][tid] + s_wc[2][tid] + s_wc[3][tid];
+      s_rank[tid] += s_wc[0][tid] + s_wc[1][tid] + s_wc[2][tid] + s_wc[3][tid];
 #pragma unroll
       for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
     }
@@ -125,14 +146,16 @@ int dispatch_num_chunks(const moe_config& c) {
 
 hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                           int32_t* hist, int32_t* base, bool scatter, hipStream_t s) {
+                           int32_t* hist, int32_t* rank0, bool scatter, int capacity,
+                           int32_t* dropped, hipStream_t s) {
   const int P = c.num_tokens * c.top_k, E = c.num_experts;
   const int nch = dispatch_num_chunks(c);
   dispatch_hist_kernel<<<nch, kThreads, 0, s>>>(P, E, topk_idx, hist);
-  dispatch_scan_kernel<<<1, kThreads, 0, s>>>(nch, E, hist, scatter ? base : nullptr, counts,
-                                              offsets);
+  dispatch_scan_kernel<<<1, kThreads, 0, s>>>(nch, E, capacity, hist, scatter ? rank0 : nullptr,
+                                              counts, offsets, dropped);
   if (scatter)
-    dispatch_scatter_kernel<<<nch, kThreads, 0, s>>>(P, E, topk_idx, base, sorted_pair, pair_pos);
+    dispatch_scatter_kernel<<<nch, kThreads, 0, s>>>(P, E, capacity, topk_idx, rank0, offsets,
+                                                     sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

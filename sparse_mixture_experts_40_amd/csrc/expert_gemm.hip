@@ -676,6 +676,9 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(int E, int H, int I, i
                                                           float* __restrict__ h) {
   extern __shared__ float s_x[];
   const int i = blockIdx.x;
+  // one block per possible row: rows past offsets[E] (pairs dropped by a
+  // capacity limit) have no sorted_pair entry and are skipped
+  if (i >= offsets[E]) return;
   const int e = expert_of_row(offsets, E, i);
   const int t = sorted_pair[i] / k_top;
   for (int c = threadIdx.x; c < H; c += blockDim.x) s_x[c] = x[(size_t)t * H + c];
@@ -699,6 +702,7 @@ __global__ __launch_bounds__(256) void down_f32_kernel(int E, int H, int I,
                                                        float* __restrict__ y) {
   extern __shared__ float s_h[];
   const int i = blockIdx.x;
+  if (i >= offsets[E]) return;  // no row (see gate_up_f32_kernel)
   const int e = expert_of_row(offsets, E, i);
   for (int c = threadIdx.x; c < I; c += blockDim.x) s_h[c] = h[(size_t)i * I + c];
   __syncthreads();

@@ -3,6 +3,8 @@
 // host synchronisation, no global state.
 #include <string.h>
 
+#include <cmath>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -140,7 +142,32 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t*
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.dispatch_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return launched(launch_dispatch(*cfg, topk_idx, expert_counts, expert_offsets, sorted_pair,
-                                  pair_pos, L.hist, L.base, true, stream));
+                                  pair_pos, L.hist, L.base, true, 0, nullptr, stream));
+}
+
+int32_t moe_capacity(const moe_config* cfg, float capacity_factor) {
+  if (check_config(cfg) != MOE_OK || !(capacity_factor > 0.0f)) return 0;
+  const double pairs = (double)cfg->num_tokens * (double)cfg->top_k;
+  double c = ceil(pairs * (double)capacity_factor / (double)cfg->num_experts);
+  if (c < 1.0) c = 1.0;
+  if (c > pairs) c = pairs;
+  return (int32_t)c;
+}
+
+moe_status moe_dispatch_capacity(const moe_config* cfg, const int32_t* topk_idx,
+                                 int32_t capacity, int32_t* expert_counts,
+                                 int32_t* expert_offsets, int32_t* sorted_pair,
+                                 int32_t* pair_pos, int32_t* dropped, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !expert_counts || !expert_offsets || !sorted_pair || !pair_pos ||
+      capacity < 1)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.dispatch_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return launched(launch_dispatch(*cfg, topk_idx, expert_counts, expert_offsets, sorted_pair,
+                                  pair_pos, L.hist, L.base, true, capacity, dropped, stream));
 }
 
 moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_t* sorted_pair,
@@ -205,20 +232,24 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
   if (st != MOE_OK) return st;
   // expert counts from the given selection (histogram + scan only)
   st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
-                                nullptr, false, stream));
+                                nullptr, false, 0, nullptr, stream));
   if (st != MOE_OK) return st;
   return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg, true), L.fp, out,
                              stream));
 }
 
-moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
-                             const float* logit_bias, const void* w_gate, const void* w_up,
-                             const void* w_down, void* out, float* router_logits,
-                             int32_t* topk_idx, float* topk_w, moe_aux_out aux,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, const void* x,
+                                const void* w_router, const float* logit_bias,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                void* out, float* router_logits, int32_t* topk_idx,
+                                float* topk_w, moe_aux_out aux, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_options none{};
+  const moe_options& o = opt ? *opt : none;
+  if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const moe_config& c = *cfg;
@@ -235,7 +266,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                                 want_aux ? L.partials : nullptr, true, stream));
   if (st != MOE_OK) return st;
   st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
-                                L.base, true, stream));
+                                L.base, true, o.capacity, o.dropped, stream));
   if (st != MOE_OK) return st;
   st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
   if (st != MOE_OK) return st;
@@ -247,6 +278,16 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
     st = launched(launch_aux(c, L.counts, L.partials,
                              router_num_blocks(c, router_k_splits(c) > 1), L.fp, aux, stream));
   return st;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logit_bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* out, float* router_logits,
+                             int32_t* topk_idx, float* topk_w, moe_aux_out aux,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return moe_layer_forward_ex(cfg, nullptr, x, w_router, logit_bias, w_gate, w_up, w_down, out,
+                              router_logits, topk_idx, topk_w, aux, workspace, workspace_bytes,
+                              stream);
 }
 
 }  // extern "C"

@@ -95,11 +95,15 @@ hipError_t launch_router_split(const moe_config& c, const void* x, const void* w
                                float* part, int32_t* topk_idx, float* topk_w,
                                float* prob_partials, hipStream_t s);
 
-// Dispatch: histogram per chunk, scan, stable scatter.
+// Dispatch: histogram per chunk, scan, stable scatter. capacity 0 keeps every
+// pair; > 0 keeps the first `capacity` pairs of each expert (pair_pos = -1 for
+// the others, their number in *dropped if non-null). counts are before the
+// limit, offsets cover the kept pairs.
 int dispatch_num_chunks(const moe_config& c);
 hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                           int32_t* hist, int32_t* base, bool scatter, hipStream_t s);
+                           int32_t* hist, int32_t* rank0, bool scatter, int capacity,
+                           int32_t* dropped, hipStream_t s);
 
 // Expert GEMMs.
 hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,

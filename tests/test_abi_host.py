@@ -85,3 +85,26 @@ def test_null_pointers_and_small_workspace_rejected(lib):
     assert lib.moe_layer_forward(ctypes.byref(c), d, d, None, None, d, d, d, None, None, None,
                                  aux, d, ws, None) == 1
     assert lib.moe_expert_swiglu(ctypes.byref(c), d, d, d, d, d, d, d, d, 0, None) == 3
+
+
+def test_capacity_helper_and_validation(lib, orc):
+    for name in ("prefill128_bf16", "decode128_bf16", "mixtral_bf16", "tiny_f32"):
+        cfg = WORKLOADS[name]
+        c = binding.make_config(cfg)
+        for cf in (0.25, 1.0, 1.1, 1.25, 1000.0):
+            assert binding.capacity(c, cf) == orc.capacity(cfg.T, cfg.E, cfg.k, cf)
+        assert lib.moe_capacity(ctypes.byref(c), 0.0) == 0
+        assert lib.moe_capacity(ctypes.byref(c), -1.0) == 0
+    c = binding.make_config(WORKLOADS["tiny_f32"])
+    d = ctypes.c_void_p(16)
+    ws = ctypes.c_void_p(256)
+    big = 1 << 30
+    # capacity must be >= 1; null outputs rejected (dropped may be NULL)
+    assert lib.moe_dispatch_capacity(ctypes.byref(c), d, 0, d, d, d, d, None, ws, big, None) == 1
+    assert lib.moe_dispatch_capacity(ctypes.byref(c), d, 4, None, d, d, d, None, ws, big, None) == 1
+    assert lib.moe_dispatch_capacity(ctypes.byref(c), d, 4, d, d, d, d, None, None, 0, None) == 3
+    # forward_ex: a negative capacity is an argument error
+    opt = binding.moe_options(-1, None)
+    r = lib.moe_layer_forward_ex(ctypes.byref(c), ctypes.byref(opt), d, d, None, d, d, d, d,
+                                 None, None, None, binding.moe_aux_out(), ws, big, None)
+    assert r == 1
