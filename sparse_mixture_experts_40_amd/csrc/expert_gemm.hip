@@ -120,20 +120,25 @@ __device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* _
                                              b_off[i], kb, 0, 0);
 }
 
-// Fragments of k step kk of a stage: NB weight blocks (A operand), MB token
-// blocks (B operand), 16 bytes per lane each.
-template <int BK, int MB, int NB>
+// Fragments of k step kk of a stage: NB weight blocks (A operand) and the MBV
+// active token blocks (B operand) of this wave, 16 bytes per lane each. Token
+// block mb of a wave covers tile rows trow0 + 64 mb (the two row halves of
+// the waves interleave in 32-row blocks). A wave with no active block reads
+// nothing.
+template <int BK, int MB, int NB, int MBV>
 __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
                                            const uint16_t* __restrict__ sB, int kk,
                                            bf16x8_t (&fa)[NB], bf16x8_t (&fb)[MB],
                                            const int (&wrow)[NB], int trow0, int lane, int sw) {
-  const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
+  if constexpr (MBV > 0) {
+    const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    fa[nb] = *reinterpret_cast<const bf16x8_t*>(sB + wrow[nb] * BK + pc);
+    for (int nb = 0; nb < NB; ++nb)
+      fa[nb] = *reinterpret_cast<const bf16x8_t*>(sB + wrow[nb] * BK + pc);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    fb[mb] = *reinterpret_cast<const bf16x8_t*>(sA + (trow0 + mb * 32) * BK + pc);
+    for (int mb = 0; mb < MBV; ++mb)
+      fb[mb] = *reinterpret_cast<const bf16x8_t*>(sA + (trow0 + mb * 64) * BK + pc);
+  }
 }
 
 // One K stage of the pipeline: start the loads of stage (dA, dB), multiply
@@ -145,7 +150,7 @@ __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
 // The distinct __restrict__ pointers give the LDS accesses disjoint alias
 // scopes, so the compiler does not drain the in-flight LDS-DMA loads before
 // every fragment read; the explicit wait_vmcnt + lds_barrier order them.
-template <int BK, int BM, int NW, int MB, int NB>
+template <int BK, int BM, int NW, int MB, int NB, int MBV>
 __device__ __forceinline__ void gemm_step(
     uint16_t* __restrict__ dA, uint16_t* __restrict__ dB, bool issue_next,
     __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase, const uint32_t* a_off,
@@ -161,38 +166,81 @@ __device__ __forceinline__ void gemm_step(
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (kk + 1 < KK)
-      stage_frag<BK, MB, NB>(cA, cB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wrow, trow0,
-                             lane, sw);
+      stage_frag<BK, MB, NB, MBV>(cA, cB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wrow,
+                                  trow0, lane, sw);
     const int nbe = (kk + 1 < KK) ? NB : NH;
 #pragma unroll
     for (int nb = 0; nb < nbe; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MBV; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][nb], fb[kk & 1][mb],
                                                               acc[nb][mb], 0, 0, 0);
   }
   // per k step: first all fragment reads of the next k step, then this step's
   // MFMAs, so each read has a whole step of MFMAs to land before its use
-  constexpr int NR = NB + MB;
+  if constexpr (MBV > 0) {
+    constexpr int NR = NB + MBV;
 #pragma unroll
-  for (int kk = 0; kk + 1 < KK; ++kk) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NB * MB, 0);
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NB * MBV, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NH * MBV, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NH * MB, 0);
   wait_vmcnt(vm_allow);
   lds_barrier();
-  stage_frag<BK, MB, NB>(nA, nB, 0, fa[0], fb[0], wrow, trow0, lane, sw);
+  stage_frag<BK, MB, NB, MBV>(nA, nB, 0, fa[0], fb[0], wrow, trow0, lane, sw);
 #pragma unroll
   for (int nb = NH; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MBV; ++mb)
       acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[L][nb], fb[L][mb], acc[nb][mb], 0,
                                                             0, 0);
+  if constexpr (MBV > 0) {
 #pragma unroll
-  for (int i = 0; i < (NB - NH) * MB; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int i = 0; i < (NB - NH) * MBV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
+}
+
+// The K loop of one tile for a wave with MBV active token blocks: first
+// fragments, the steps, and (prefetch) the last step that loads the next
+// tile's first stage into buffer 0. Waves without active blocks still issue
+// their loads and take every barrier.
+template <int BK, int BM, int NST, int NW, int MB, int NB, int MBV>
+__device__ __forceinline__ void tile_k(uint16_t* smem, int nk, bool prefetch,
+                                       __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase,
+                                       __amdgpu_buffer_rsrc_t bbase_n, const uint32_t* a_off,
+                                       const uint32_t* b_off, const uint32_t* a_offn,
+                                       const uint32_t* b_offn, f32x16_t (&acc)[NB][MB],
+                                       const int (&wrow)[NB], int trow0, int lane, int sw,
+                                       int wave) {
+  constexpr int LA = BM * BK / (512 * NW), LB = 256 * BK / (512 * NW);
+  constexpr int STAGE = (BM + 256) * BK;
+  bf16x8_t fa[2][NB], fb[2][MB];
+  stage_frag<BK, MB, NB, MBV>(smem, smem + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
+  const int nk_main = prefetch ? nk - 1 : nk;
+  for (int kt = 0; kt < nk_main; ++kt) {
+    uint16_t* dA = smem + ((kt + NST - 1) % NST) * STAGE;
+    const uint16_t* cA = smem + (kt % NST) * STAGE;
+    const uint16_t* nA = smem + ((kt + 1) % NST) * STAGE;
+    const int last = (kt + NST - 1 < nk - 1) ? kt + NST - 1 : nk - 1;
+    const int ahead = last - (kt + 1);  // stages still loading after stage kt+1
+    gemm_step<BK, BM, NW, MB, NB, MBV>(dA, dA + BM * BK, kt + NST - 1 < nk, abase, bbase, a_off,
+                                       b_off, (uint32_t)((kt + NST - 1) * BK) * 2u, cA,
+                                       cA + BM * BK, nA, nA + BM * BK,
+                                       ahead > 0 ? (LA + LB) * ahead : 0, acc, fa, fb, wrow,
+                                       trow0, lane, sw, wave);
+  }
+  if (prefetch) {
+    // last K stage (buffer 1) while the next tile's stage 0 loads into buffer 0;
+    // the fragments read after its barrier are stale and unused
+    gemm_step<BK, BM, NW, MB, NB, MBV>(smem, smem + BM * BK, true, abase, bbase_n, a_offn, b_offn,
+                                       0u, smem + STAGE, smem + STAGE + BM * BK, smem,
+                                       smem + BM * BK, LA + LB, acc, fa, fb, wrow, trow0, lane,
+                                       sw, wave);
   }
 }
 
@@ -294,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     wrow[nb] = GATEUP ? ((nb / (NB / 2)) * 128 + wn * (NB / 2) * 32 + (nb % (NB / 2)) * 32 +
                          (lane & 31))
                       : (wn * NB * 32 + nb * 32 + (lane & 31));
-  const int trow0 = wm * (BM / 2) + (lane & 31);
+  const int trow0 = wm * 32 + (lane & 31);  // token block mb: tile rows trow0 + 64 mb
 
   // A operand: the activation rows (x for gate/up, h for down); offsets stay
   // below 2^32 bytes (checked on the host)
@@ -344,9 +392,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
-    bf16x8_t fa[2][NB], fb[2][MB];
-
-    // prologue: NST - 1 stages in flight (unless prefetched), first fragments
+    // prologue: NST - 1 stages in flight (unless prefetched)
     if (!staged) {
       for (int st = 0; st < NST - 1 && st < nk; ++st)
         dma_stage<BK, BM, NW>(smem + st * STAGE, smem + st * STAGE + BM * BK, abase, bbase, a_off,
@@ -356,37 +402,40 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       wait_vmcnt(0);
     }
     lds_barrier();
-    stage_frag<BK, MB, NB>(smem, smem + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
 
-    const int nk_main = prefetch ? nk - 1 : nk;
-    for (int kt = 0; kt < nk_main; ++kt) {
-      uint16_t* dA = smem + ((kt + NST - 1) % NST) * STAGE;
-      const uint16_t* cA = smem + (kt % NST) * STAGE;
-      const uint16_t* nA = smem + ((kt + 1) % NST) * STAGE;
-      const int last = (kt + NST - 1 < nk - 1) ? kt + NST - 1 : nk - 1;
-      const int ahead = last - (kt + 1);  // stages still loading after stage kt+1
-      gemm_step<BK, BM, NW, MB, NB>(dA, dA + BM * BK, kt + NST - 1 < nk, abase, bbase, a_off,
-                                    b_off, (uint32_t)((kt + NST - 1) * BK) * 2u, cA,
-                                    cA + BM * BK, nA, nA + BM * BK,
-                                    ahead > 0 ? (LA + LB) * ahead : 0, acc, fa, fb, wrow, trow0,
-                                    lane, sw, wave);
-    }
-    if (prefetch) {
-      // last K stage (buffer 1) while the next tile's stage 0 loads into buffer 0;
-      // the fragments read after its barrier are stale and unused
-      gemm_step<BK, BM, NW, MB, NB>(smem, smem + BM * BK, true, abase, bbase_n, a_offn, b_offn, 0u,
-                                    smem + STAGE, smem + STAGE + BM * BK, smem, smem + BM * BK,
-                                    LA + LB, acc, fa, fb, wrow, trow0, lane, sw, wave);
-    }
-    // No barrier here: the epilogue touches no LDS, and the next tile's first
-    // LDS writes are ordered by the barriers of its prologue and first step.
+    // token blocks of this wave with at least one row of the expert: the
+    // MFMAs (and fragment reads) of the others are skipped, so the last,
+    // partly filled tile of an expert costs in proportion to its rows
+    const int live = min(BM, cur.row_end - cur.row0) - wm * 32;
+    const int mbv = live <= 0 ? 0 : min(MB, (live + 63) / 64);
+    if (mbv >= MB)
+      tile_k<BK, BM, NST, NW, MB, NB, MB>(smem, nk, prefetch, abase, bbase, bbase_n, a_off,
+                                          b_off, a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
+    else if (mbv == 3)
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 3 ? 3 : MB)>(smem, nk, prefetch, abase, bbase,
+                                                         bbase_n, a_off, b_off, a_offn, b_offn,
+                                                         acc, wrow, trow0, lane, sw, wave);
+    else if (mbv == 2)
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 2 ? 2 : MB)>(smem, nk, prefetch, abase, bbase,
+                                                         bbase_n, a_off, b_off, a_offn, b_offn,
+                                                         acc, wrow, trow0, lane, sw, wave);
+    else if (mbv == 1)
+      tile_k<BK, BM, NST, NW, MB, NB, 1>(smem, nk, prefetch, abase, bbase, bbase_n, a_off, b_off,
+                                         a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
+    else
+      tile_k<BK, BM, NST, NW, MB, NB, 0>(smem, nk, prefetch, abase, bbase, bbase_n, a_off, b_off,
+                                         a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
+    // No barrier here: the only LDS the epilogue touches is the stage computed
+    // last (its reads finished before the last stage barrier), and the next
+    // tile's first LDS writes are ordered by the barriers of its prologue and
+    // first step.
     const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
 
     // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
     if constexpr (GATEUP) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int row = row0 + trow0 + mb * 32;
+      const int row = row0 + trow0 + mb * 64;
       if (row >= row_end) continue;
       {
         uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)row * N_out;
@@ -432,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 64 / NW; ++i) {
           const int sr = wave * (64 / NW) + i;                  // slab row
-          const int row = row0 + (sr >> 5) * 128 + mb * 32 + (sr & 31);
+          const int row = row0 + mb * 64 + sr;  // slab row sr = 32 wm + m
           const float4 v =
               *reinterpret_cast<const float4*>(slab + sr * BN + ((lane ^ (sr & 15)) << 2));
           const int col = n0 + lane * 4;
