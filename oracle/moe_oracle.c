@@ -76,8 +76,21 @@ int orc_logits(int T, int H, int E, int dtype, const void* x, const void* wr,
  * forced_idx (nullable): use these experts instead of selecting (weights are
  * computed the same way from them).
  * probs (nullable) receives the full softmax [T,E]. */
+int orc_route_sel(int T, int E, int k, int norm, const float* logits, const float* sel_bias,
+                  const int32_t* forced_idx, int32_t* idx, double* w, double* probs);
+
 int orc_route(int T, int E, int k, int norm, const float* logits, const int32_t* forced_idx,
               int32_t* idx, double* w, double* probs) {
+  return orc_route_sel(T, E, k, norm, logits, NULL, forced_idx, idx, w, probs);
+}
+
+/* orc_route with a selection-only bias, [LAB17] (DeepSeek-V3's balancing
+ * without an auxiliary loss: a per-expert bias moves the routing decision, the
+ * model's own scores keep the weights): the k experts are chosen by the fp32
+ * key l[t,e] + sel_bias[e] (descending, ties to the lower index), the weights
+ * and probs come from the softmax of the unbiased l. sel_bias NULL: no bias. */
+int orc_route_sel(int T, int E, int k, int norm, const float* logits, const float* sel_bias,
+                  const int32_t* forced_idx, int32_t* idx, double* w, double* probs) {
   if (T < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
   int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
@@ -98,15 +111,21 @@ int orc_route(int T, int E, int k, int norm, const float* logits, const int32_t*
         if (sel[j] < 0 || sel[j] >= E) bad = 1;
       }
     } else {
-      /* k passes of "largest remaining logit, lowest index on ties" */
+      /* k passes of "largest remaining key, lowest index on ties"; the key is
+       * the fp32 logit, plus the selection bias (an fp32 addition) if given */
       for (int j = 0; j < k; ++j) {
         int best = -1;
+        float best_key = 0.0f;
         for (int e = 0; e < E; ++e) {
           int taken = 0;
           for (int q = 0; q < j; ++q)
             if (sel[q] == e) taken = 1;
           if (taken) continue;
-          if (best < 0 || l[e] > l[best]) best = e; /* strict: earlier index wins ties */
+          const float key = sel_bias ? l[e] + sel_bias[e] : l[e];
+          if (best < 0 || key > best_key) { /* strict: earlier index wins ties */
+            best = e;
+            best_key = key;
+          }
         }
         sel[j] = best;
       }
@@ -120,6 +139,45 @@ int orc_route(int T, int E, int k, int norm, const float* logits, const int32_t*
     }
   }
   return bad ? -1 : 0;
+}
+
+/* Noisy logits, [MOE-128x8] router pseudocode (noisy_logits = logits + noise *
+ * softplus(x @ W_noise)) and [LAB17] noisy top-k gating (standard normal noise
+ * times Softplus(W_noise x) added to the gate logits):
+ *   out[t,e] = fp32( l[t,e] + noise[t,e] * softplus(nl[t,e]) ),
+ *   softplus(z) = ln(1 + e^z)
+ * nl = x W_noise^T (orc_logits with the noise matrix); the noise values are an
+ * input (drawn by the caller). */
+int orc_noisy_logits(int T, int E, const float* logits, const float* nlogits, const float* noise,
+                     float* out) {
+  if (T < 0 || E < 1 || !logits || !nlogits || !noise || !out) return -1;
+  for (size_t i = 0; i < (size_t)T * E; ++i) {
+    const double z = (double)nlogits[i];
+    const double sp = z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+    out[i] = (float)((double)logits[i] + (double)noise[i] * sp);
+  }
+  return 0;
+}
+
+/* Router z-loss statistic. [MOE-128x8] names a router z-loss for training
+ * stability without a formula; the one taken here is the mean over tokens of
+ * the squared log-sum-exp of the router logits:
+ *   z = (1/T) sum_t ( ln sum_e exp(l[t,e]) )^2 */
+int orc_z_loss(int T, int E, const float* logits, double* z) {
+  if (T < 1 || E < 1 || !logits || !z) return -1;
+  double acc = 0.0;
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e)
+      if ((double)l[e] > m) m = (double)l[e];
+    double s = 0.0;
+    for (int e = 0; e < E; ++e) s += exp((double)l[e] - m);
+    const double lse = m + log(s);
+    acc += lse * lse;
+  }
+  *z = acc / (double)T;
+  return 0;
 }
 
 /* Dispatch as a counting sort of the pairs by expert ([QWEN3-READ] §三: put the

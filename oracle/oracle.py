@@ -44,6 +44,9 @@ def _load():
         i = ctypes.c_int
         lib.orc_logits.argtypes = [i, i, i, i, P, P, P, P]
         lib.orc_route.argtypes = [i, i, i, i, P, P, P, P, P]
+        lib.orc_route_sel.argtypes = [i, i, i, i, P, P, P, P, P, P]
+        lib.orc_noisy_logits.argtypes = [i, i, P, P, P, P]
+        lib.orc_z_loss.argtypes = [i, i, P, P]
         lib.orc_dispatch.argtypes = [i, i, i, P, P, P, P, P]
         lib.orc_expert_rows.argtypes = [i, i, i, P, P, P, P, i, P, P, i, P]
         lib.orc_combine.argtypes = [i, i, i, P, P, P]
@@ -55,7 +58,8 @@ def _load():
                                            P, P, P, P]
         for f in (lib.orc_logits, lib.orc_route, lib.orc_dispatch, lib.orc_expert_rows,
                   lib.orc_combine, lib.orc_combine_kept, lib.orc_capacity,
-                  lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens):
+                  lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens,
+                  lib.orc_route_sel, lib.orc_noisy_logits, lib.orc_z_loss):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -98,18 +102,39 @@ def logits(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None = None) 
     return out
 
 
-def route(lg: np.ndarray, k: int, norm: bool, forced_idx: np.ndarray | None = None):
-    """Softmax + top-k (+ renormalisation). Returns (idx int32 [T,k],
-    w float64 [T,k], probs float64 [T,E])."""
+def route(lg: np.ndarray, k: int, norm: bool, forced_idx: np.ndarray | None = None,
+          sel_bias: np.ndarray | None = None):
+    """Softmax + top-k (+ renormalisation); sel_bias [E] (optional) moves only
+    the selection. Returns (idx int32 [T,k], w float64 [T,k], probs float64 [T,E])."""
     lg = _c(lg, np.float32)
     T, E = lg.shape
     forced_idx = _c(forced_idx, np.int32)
+    sel_bias = _c(sel_bias, np.float32)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     probs = np.empty((T, E), np.float64)
-    _check(_load().orc_route(T, E, k, int(bool(norm)), _p(lg), _p(forced_idx), _p(idx), _p(w),
-                             _p(probs)), "route")
+    _check(_load().orc_route_sel(T, E, k, int(bool(norm)), _p(lg), _p(sel_bias), _p(forced_idx),
+                                 _p(idx), _p(w), _p(probs)), "route")
     return idx, w, probs
+
+
+def noisy_logits(lg: np.ndarray, nlg: np.ndarray, noise: np.ndarray) -> np.ndarray:
+    """fp32( l + noise * softplus(nl) ) [T,E]."""
+    lg, nlg, noise = _c(lg, np.float32), _c(nlg, np.float32), _c(noise, np.float32)
+    T, E = lg.shape
+    assert nlg.shape == (T, E) and noise.shape == (T, E)
+    out = np.empty((T, E), np.float32)
+    _check(_load().orc_noisy_logits(T, E, _p(lg), _p(nlg), _p(noise), _p(out)), "noisy_logits")
+    return out
+
+
+def z_loss(lg: np.ndarray) -> float:
+    """(1/T) sum_t logsumexp(l_t)^2."""
+    lg = _c(lg, np.float32)
+    T, E = lg.shape
+    z = np.empty(1, np.float64)
+    _check(_load().orc_z_loss(T, E, _p(lg), _p(z)), "z_loss")
+    return float(z[0])
 
 
 def dispatch(idx: np.ndarray, E: int):
@@ -221,4 +246,31 @@ def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool =
                                       _p(wd), n, _p(tokens), _p(forced_idx), _p(keep),
                                       int(round_h),
                                       _p(lg), _p(idx), _p(w), _p(out)), "forward_tokens")
+    return {"logits": lg, "idx": idx, "w": w, "out": out}
+
+
+def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_bias=None,
+                    keep=None, round_h: bool = False):
+    """Block forward of the listed tokens with the router variants, composed
+    from the steps above: logits (+ bias), noisy logits if `noise` [T,E] and
+    `w_noise` [E,H] are given (the noise rows of the listed tokens are used),
+    selection with the optional selection-only bias, experts, combine over
+    the kept slots. Returns dict(logits (the ones the softmax saw), idx, w,
+    out)."""
+    x = _c(inp["x"])
+    T = x.shape[0]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = _c(tokens, np.int32)
+    xs = np.ascontiguousarray(x[tokens])
+    lg = logits(xs, inp["w_router"], inp.get("logit_bias"))
+    if noise is not None:
+        nlg = logits(xs, w_noise)
+        lg = noisy_logits(lg, nlg, np.asarray(noise, np.float32)[tokens])
+    idx, w, _ = route(lg, cfg.k, cfg.norm, sel_bias=sel_bias)
+    n = tokens.shape[0]
+    tok = np.repeat(np.arange(n, dtype=np.int32), cfg.k)
+    y = expert_rows(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tok, idx.ravel(),
+                    round_h=round_h)
+    out = combine(w, y, keep)
     return {"logits": lg, "idx": idx, "w": w, "out": out}

@@ -138,6 +138,86 @@ def test_logits_match_numpy_matmul(orc, dtype):
     assert not np.allclose(lg, (ref - d["logit_bias"]).astype(np.float32), atol=1e-3)
 
 
+# ------------------------------------------------------------ router variants
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_selection_bias_moves_choice_not_weights(orc, seed):
+    rng = _rng(300 + seed)
+    T, E, k = 40, 16, 4
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.7).astype(np.float32)
+    for norm in (True, False):
+        idx, w, probs = orc.route(lg, k, norm, sel_bias=bias)
+        p = sp_softmax(lg.astype(np.float64), axis=1)
+        for t in range(T):
+            key = (lg[t] + bias).astype(np.float32)  # fp32 addition
+            ref = sorted(range(E), key=lambda e: (-float(key[e]), e))[:k]
+            assert idx[t].tolist() == ref
+            sel = p[t, ref]  # weights from the unbiased softmax
+            np.testing.assert_allclose(w[t], sel / sel.sum() if norm else sel, rtol=1e-12)
+        np.testing.assert_allclose(probs, p, rtol=1e-12)
+    # zero bias is the plain router; a large bias forces an expert in
+    i0, w0, _ = orc.route(lg, k, True)
+    i1, w1, _ = orc.route(lg, k, True, sel_bias=np.zeros(E, np.float32))
+    assert (i0 == i1).all() and (w0 == w1).all()
+    big = np.zeros(E, np.float32)
+    big[9] = 100.0
+    i2, w2, _ = orc.route(lg, k, False, sel_bias=big)
+    assert (i2[:, 0] == 9).all()
+    np.testing.assert_allclose(w2[:, 0], sp_softmax(lg.astype(np.float64), axis=1)[:, 9],
+                               rtol=1e-12)
+
+
+def test_noisy_logits_match_softplus_and_keep_topk_formula(orc):
+    rng = _rng(310)
+    T, E, k = 30, 12, 3
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    nlg = (rng.standard_normal((T, E)) * 4).astype(np.float32)
+    noise = rng.standard_normal((T, E)).astype(np.float32)
+    out = orc.noisy_logits(lg, nlg, noise)
+    ref = lg.astype(np.float64) + noise.astype(np.float64) * np.logaddexp(0.0, nlg.astype(np.float64))
+    np.testing.assert_allclose(out, ref.astype(np.float32), rtol=1.2e-7, atol=0)
+    assert (orc.noisy_logits(lg, nlg, np.zeros_like(noise)) == lg).all()
+    # softplus(0) = ln 2
+    np.testing.assert_allclose(orc.noisy_logits(lg, np.zeros_like(nlg), noise),
+                               (lg + noise * np.log(2.0)).astype(np.float32), rtol=1.2e-7)
+    # [LAB17] H(x) = Softmax(KeepTopK(noisy logits, K)) = the renormalised router
+    idx, w, _ = orc.route(out, k, True)
+    for t in range(T):
+        kept = np.full(E, -np.inf)
+        kept[idx[t]] = out[t][idx[t]]
+        np.testing.assert_allclose(w[t], sp_softmax(kept)[idx[t]], rtol=1e-12)
+
+
+def test_z_loss_closed_forms(orc):
+    from scipy.special import logsumexp
+    for E in (1, 8, 128):
+        assert orc.z_loss(np.zeros((5, E), np.float32)) == pytest.approx(math.log(E) ** 2,
+                                                                         rel=1e-15, abs=1e-15)
+    rng = _rng(320)
+    lg = (rng.standard_normal((50, 64)) * 3).astype(np.float32)
+    ref = float((logsumexp(lg.astype(np.float64), axis=1) ** 2).mean())
+    assert orc.z_loss(lg) == pytest.approx(ref, rel=1e-13)
+    # shift invariance of the softmax does not hold for z: l + c -> (lse + c)^2
+    c = 2.5
+    ref2 = float(((logsumexp(lg.astype(np.float64), axis=1) + c) ** 2).mean())
+    assert orc.z_loss(lg + np.float32(c)) == pytest.approx(ref2, rel=1e-6)
+
+
+def test_forward_variant_composes_the_plain_forward(orc):
+    cfg = MoEConfig("var", T=10, H=64, E=8, k=2, I=64, norm=True, dtype="bf16")
+    inp = make_inputs(cfg)
+    a = orc.forward_tokens(inp, cfg)
+    b = orc.forward_variant(inp, cfg)
+    assert (a["idx"] == b["idx"]).all() and (a["logits"] == b["logits"]).all()
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-12, atol=1e-14)
+    # zero noise leaves the router unchanged
+    z = orc.forward_variant(inp, cfg, noise=np.zeros((cfg.T, cfg.E), np.float32),
+                            w_noise=inp["w_router"])
+    assert (z["idx"] == a["idx"]).all()
+
+
 # ------------------------------------------------------------------- dispatch
 
 
