@@ -82,6 +82,7 @@ typedef struct {
 } moe_config;
 
 /* Load-balance outputs; every field may be NULL (then it is not written).
+ * z_loss is described at the field.
  *   counts[E] int32 : n_e = number of pairs routed to expert e
  *   f[E]      fp32  : f_e = n_e / (T*k), the fraction of routed pairs
  *   P[E]      fp32  : P_e = (1/T) * sum_t softmax(l_t)_e, the mean router
@@ -93,7 +94,34 @@ typedef struct {
   float* f;
   float* P;
   float* aux;
+  float* z_loss; /* [1] fp32: (1/T) sum_t (ln sum_e exp l[t,e])^2 over the logits the
+                    softmax used. [MOE-128x8] (challenge 3: a router z-loss for
+                    training stability) names the statistic without a formula;
+                    this is the form taken. */
 } moe_aux_out;
+
+/* Options of moe_layer_forward_ex / moe_router_topk_ex. Zero-initialised =
+ * the plain forward. */
+typedef struct {
+  int32_t capacity; /* 0: dropless. > 0: capacity-limited dispatch with this
+                       capacity (moe_dispatch_capacity; see moe_capacity) */
+  int32_t* dropped; /* [1] int32 out or NULL: pairs dropped by the capacity */
+  /* Noisy top-k, [MOE-128x8] router pseudocode (noisy_logits = logits + noise *
+   * softplus(x @ W_noise)) and [LAB17] noisy top-k gating: the logits become
+   *   l'[t,e] = l[t,e] + noise[t,e] * softplus((x W_noise^T)[t,e]),
+   * softplus(z) = ln(1 + e^z), and l' replaces l everywhere after (softmax,
+   * selection, weights, P_e, z_loss, the router_logits output). With
+   * norm_topk_prob the weights are [LAB17]'s Softmax(KeepTopK(l', k)).
+   * noise [T,E] fp32 (the caller's draws, e.g. standard normal), w_noise
+   * [E,H] dtype; both or neither. */
+  const float* noise;
+  const void* w_noise;
+  /* Selection-only bias, [LAB17] (DeepSeek-V3 load balancing without an
+   * auxiliary loss, by a per-expert bias on the routing): [E] fp32 added to the
+   * logits for the top-k choice only (fp32 keys l + b, ties to the lower
+   * index); the weights and statistics use the unbiased logits. NULL: none. */
+  const float* select_bias;
+} moe_options;
 
 /* Bytes of workspace every entry point below needs for `cfg` (the maximum
  * over all of them). Host-only and pure; returns 0 if `cfg` is invalid. */
@@ -123,6 +151,16 @@ const char* moe_status_string(moe_status s);
 moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_router,
                            const float* logit_bias, float* logits, int32_t* topk_idx,
                            float* topk_w, hipStream_t stream);
+
+/* moe_router_topk with the router options of moe_options (noise, w_noise,
+ * select_bias; the other fields are ignored). Noise needs x (the noise logits
+ * are computed from it) and a workspace of moe_workspace_size bytes; logits
+ * (if non-NULL) receives the noisy logits. Without noise no workspace is used
+ * (may be NULL). */
+moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, const void* x,
+                              const void* w_router, const float* logit_bias, float* logits,
+                              int32_t* topk_idx, float* topk_w, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch: group the T*k pairs by expert (a stable counting sort).
  * Replaces the one-hot mask + per-expert torch.where loop of [QWEN3-READ]
@@ -215,12 +253,6 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
                          moe_aux_out out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-/* Options of moe_layer_forward_ex. Zero-initialised = the plain forward. */
-typedef struct {
-  int32_t capacity; /* 0: dropless. > 0: capacity-limited dispatch with this
-                       capacity (moe_dispatch_capacity; see moe_capacity) */
-  int32_t* dropped; /* [1] int32 out or NULL: pairs dropped by the capacity */
-} moe_options;
 
 /* The whole block: router -> dispatch -> experts -> combine -> statistics,
  * all on `stream`, with no host synchronisation.

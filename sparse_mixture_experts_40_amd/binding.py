@@ -21,7 +21,8 @@ MOE_DTYPE = {"f32": 0, "bf16": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # public entry points of include/moe.h
-EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_dispatch",
+EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_router_topk_ex",
+           "moe_dispatch",
            "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_layer_forward",
            "moe_layer_forward_ex")
@@ -35,12 +36,14 @@ class moe_config(ctypes.Structure):
 
 
 class moe_options(ctypes.Structure):
-    _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p)]
+    _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p),
+                ("noise", ctypes.c_void_p), ("w_noise", ctypes.c_void_p),
+                ("select_bias", ctypes.c_void_p)]
 
 
 class moe_aux_out(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("f", ctypes.c_void_p), ("P", ctypes.c_void_p),
-                ("aux", ctypes.c_void_p)]
+                ("aux", ctypes.c_void_p), ("z_loss", ctypes.c_void_p)]
 
 
 _lib = None
@@ -62,6 +65,7 @@ def load(path: str = LIB_PATH):
     lib.moe_capacity.argtypes, lib.moe_capacity.restype = [C, ctypes.c_float], ctypes.c_int32
     sig = {
         "moe_router_topk": [C, V, V, V, V, V, V, V],
+        "moe_router_topk_ex": [C, ctypes.POINTER(moe_options), V, V, V, V, V, V, V, S, V],
         "moe_dispatch": [C, V, V, V, V, V, V, S, V],
         "moe_dispatch_capacity": [C, V, ctypes.c_int32, V, V, V, V, V, V, S, V],
         "moe_expert_gate_up": [C, V, V, V, V, V, V, V, S, V],
@@ -124,6 +128,22 @@ def router_topk(c: moe_config, x, w_router, logit_bias, logits, topk_idx, topk_w
            "moe_router_topk")
 
 
+def options(capacity: int = 0, dropped=None, noise=None, w_noise=None,
+            select_bias=None) -> moe_options:
+    """moe_options from tensors (the tensors must outlive the calls)."""
+    return moe_options(int(capacity), _ptr(dropped), _ptr(noise), _ptr(w_noise),
+                       _ptr(select_bias))
+
+
+def router_topk_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, logits,
+                   topk_idx, topk_w, ws=None):
+    _check(load().moe_router_topk_ex(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
+                                     _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(logits),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream()),
+           "moe_router_topk_ex")
+
+
 def dispatch(c: moe_config, topk_idx, counts, offsets, sorted_pair, pair_pos, ws):
     _check(load().moe_dispatch(ctypes.byref(c), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
                                _ptr(sorted_pair), _ptr(pair_pos), _ptr(ws), ws.numel(),
@@ -169,13 +189,15 @@ def combine(c: moe_config, y_sorted, pair_pos, topk_w, out):
                               _ptr(out), _stream()), "moe_combine")
 
 
-def _aux(counts=None, f=None, P=None, aux=None) -> moe_aux_out:
-    return moe_aux_out(_ptr(counts), _ptr(f), _ptr(P), _ptr(aux))
+def _aux(counts=None, f=None, P=None, aux=None, z_loss=None) -> moe_aux_out:
+    return moe_aux_out(_ptr(counts), _ptr(f), _ptr(P), _ptr(aux), _ptr(z_loss))
 
 
-def aux_stats(c: moe_config, logits, topk_idx, ws, counts=None, f=None, P=None, aux=None):
+def aux_stats(c: moe_config, logits, topk_idx, ws, counts=None, f=None, P=None, aux=None,
+              z_loss=None):
     _check(load().moe_aux_stats(ctypes.byref(c), _ptr(logits), _ptr(topk_idx),
-                                _aux(counts, f, P, aux), _ptr(ws), ws.numel(), _stream()),
+                                _aux(counts, f, P, aux, z_loss), _ptr(ws), ws.numel(),
+                                _stream()),
            "moe_aux_stats")
 
 
@@ -191,11 +213,12 @@ def layer_forward(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, 
 
 def layer_forward_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, w_gate,
                      w_up, w_down, out, ws, router_logits=None, topk_idx=None, topk_w=None,
-                     counts=None, f=None, P=None, aux=None):
+                     counts=None, f=None, P=None, aux=None, z_loss=None):
     _check(load().moe_layer_forward_ex(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
                                        _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate),
                                        _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(router_logits),
-                                       _ptr(topk_idx), _ptr(topk_w), _aux(counts, f, P, aux),
+                                       _ptr(topk_idx), _ptr(topk_w),
+                                       _aux(counts, f, P, aux, z_loss),
                                        _ptr(ws), ws.numel(), _stream()),
            "moe_layer_forward_ex")
 
@@ -211,16 +234,30 @@ def to_device(a, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+def _as_tensor(a, device):
+    if a is None or isinstance(a, torch.Tensor):
+        return a
+    return to_device(a, device)
+
+
 class MoEBlock:
     """Device-resident block: holds the weights and a workspace, runs the
     whole forward with one library call per step."""
 
-    def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0):
-        """capacity > 0: capacity-limited dispatch (see moe_capacity)."""
+    def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0,
+                 noise=None, w_noise=None, select_bias=None):
+        """capacity > 0: capacity-limited dispatch (see moe_capacity); noise
+        [T,E] fp32 + w_noise [E,H]: noisy top-k; select_bias [E] fp32:
+        selection-only bias (numpy arrays or tensors)."""
         self.cfg = cfg
         self.c = make_config(cfg)
         self.dropped = torch.zeros(1, dtype=torch.int32, device=device)
-        self.opts = moe_options(int(capacity), _ptr(self.dropped)) if capacity else None
+        self.noise = _as_tensor(noise, device)
+        self.w_noise = _as_tensor(w_noise, device)
+        self.select_bias = _as_tensor(select_bias, device)
+        variant = capacity or noise is not None or select_bias is not None
+        self.opts = options(capacity, self.dropped, self.noise, self.w_noise,
+                            self.select_bias) if variant else None
         self.w_router = to_device(inputs["w_router"], device)
         self.w_gate = to_device(inputs["w_gate"], device)
         self.w_up = to_device(inputs["w_up"], device)
@@ -236,6 +273,7 @@ class MoEBlock:
         self.f = torch.empty(E, dtype=torch.float32, device=device)
         self.P = torch.empty(E, dtype=torch.float32, device=device)
         self.aux = torch.empty(1, dtype=torch.float32, device=device)
+        self.z_loss = torch.empty(1, dtype=torch.float32, device=device)
 
     def forward(self, x: torch.Tensor, outputs: bool = True):
         """outputs=False: only `out` (logits, selection and statistics stay in
@@ -243,7 +281,8 @@ class MoEBlock:
         if outputs:
             layer_forward_ex(self.c, self.opts, x, self.w_router, self.logit_bias, self.w_gate,
                              self.w_up, self.w_down, self.out, self.ws, self.logits,
-                             self.topk_idx, self.topk_w, self.counts, self.f, self.P, self.aux)
+                             self.topk_idx, self.topk_w, self.counts, self.f, self.P, self.aux,
+                             self.z_loss)
         else:
             layer_forward_ex(self.c, self.opts, x, self.w_router, self.logit_bias, self.w_gate,
                              self.w_up, self.w_down, self.out, self.ws)

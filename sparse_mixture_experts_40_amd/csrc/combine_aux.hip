@@ -100,18 +100,37 @@ __global__ __launch_bounds__(kThreads) void aux_expert_kernel(
   }
 }
 
-// aux = E * sum_e f_e P_e (fixed-shape tree over the experts).
-__global__ __launch_bounds__(kThreads) void aux_final_kernel(int E, const double* __restrict__ fp,
-                                                             float* __restrict__ aux_out) {
+// aux = E * sum_e f_e P_e (fixed-shape tree over the experts) and, if zpart is
+// given, z = (1/T) sum of the router blocks' (ln sum_e exp l)^2 sums (thread i
+// takes blocks i, i+256, ... in order, then a fixed-shape tree).
+__global__ __launch_bounds__(kThreads) void aux_final_kernel(int T, int E,
+                                                             const double* __restrict__ fp,
+                                                             const float* __restrict__ zpart,
+                                                             int nz, float* __restrict__ aux_out,
+                                                             float* __restrict__ z_out) {
   __shared__ double s[kThreads];
   const int e = threadIdx.x;
-  s[e] = (e < E) ? fp[e] : 0.0;
-  __syncthreads();
-  for (int d = kThreads / 2; d > 0; d >>= 1) {
-    if (e < d) s[e] += s[e + d];
+  if (aux_out) {
+    s[e] = (e < E) ? fp[e] : 0.0;
+    __syncthreads();
+    for (int d = kThreads / 2; d > 0; d >>= 1) {
+      if (e < d) s[e] += s[e + d];
+      __syncthreads();
+    }
+    if (e == 0) aux_out[0] = (float)((double)E * s[0]);
     __syncthreads();
   }
-  if (e == 0) aux_out[0] = (float)((double)E * s[0]);
+  if (z_out) {
+    double acc = 0.0;
+    for (int b = e; b < nz; b += kThreads) acc += (double)zpart[b];
+    s[e] = acc;
+    __syncthreads();
+    for (int d = kThreads / 2; d > 0; d >>= 1) {
+      if (e < d) s[e] += s[e + d];
+      __syncthreads();
+    }
+    if (e == 0) z_out[0] = (float)(s[0] / (double)T);
+  }
 }
 
 }  // namespace
@@ -140,11 +159,16 @@ hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pai
 }
 
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s) {
-  aux_expert_kernel<<<c.num_experts, kThreads, 0, s>>>(c.num_tokens, c.num_experts, c.top_k,
-                                                       counts, prob_partials, n_partials,
-                                                       out.counts, out.f, out.P, fp_scratch);
-  if (out.aux) aux_final_kernel<<<1, kThreads, 0, s>>>(c.num_experts, fp_scratch, out.aux);
+                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s,
+                      const float* zpart, int n_zpart) {
+  if (out.counts || out.f || out.P || out.aux)
+    aux_expert_kernel<<<c.num_experts, kThreads, 0, s>>>(c.num_tokens, c.num_experts, c.top_k,
+                                                         counts, prob_partials, n_partials,
+                                                         out.counts, out.f, out.P, fp_scratch);
+  float* z_out = zpart ? out.z_loss : nullptr;
+  if (out.aux || z_out)
+    aux_final_kernel<<<1, kThreads, 0, s>>>(c.num_tokens, c.num_experts, fp_scratch, zpart,
+                                            n_zpart, out.aux, z_out);
   return hipGetLastError();
 }
 

@@ -317,8 +317,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
   constexpr int MB = BM / 64;                 // token blocks of 32 rows per wave
   constexpr int NB = BN / (WN * 32);          // weight blocks of 32 rows per wave
   constexpr int NCOL = GATEUP ? BN / 2 : BN;  // output columns per tile
-  constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
-  constexpr int RPI = 64 / CPR;               // tile rows per load instruction
   constexpr int LA = BM * BK / (512 * NW);    // A load instructions per wave per stage
   constexpr int LB = BN * BK / (512 * NW);    // B load instructions per wave per stage
   constexpr int STAGE = (BM + BN) * BK;       // elements per stage

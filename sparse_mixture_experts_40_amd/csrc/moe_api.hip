@@ -63,10 +63,12 @@ struct Layout {
   int32_t* idx;
   float* w;
   float* rpart;   // split-K router partials [splits, T, E]
-  float* rlogits; // split-K router logits [T, E]
+  float* rlogits; // router logits [T, E] (split-K or noisy routing)
+  float* nlogits; // noise logits x W_noise^T [T, E]
+  float* zpart;   // per router block z-loss sums
   void* h;
   void* y;
-  size_t dispatch_end, aux_end, layer_end;
+  size_t dispatch_end, aux_end, router_end, layer_end;
 };
 
 Layout carve(const moe_config& c, void* ws) {
@@ -82,10 +84,13 @@ Layout carve(const moe_config& c, void* ws) {
   L.offsets = cv.take<int32_t>(E + 1);
   L.idx = cv.take<int32_t>(P);
   L.w = cv.take<float>(P);
+  L.zpart = cv.take<float>((size_t)router_num_blocks(c, true));  // the larger count
   L.aux_end = cv.off;
   const int ks = router_k_splits(c);
   L.rpart = ks > 1 ? cv.take<float>((size_t)ks * c.num_tokens * E) : nullptr;
-  L.rlogits = ks > 1 ? cv.take<float>((size_t)c.num_tokens * E) : nullptr;
+  L.rlogits = cv.take<float>((size_t)c.num_tokens * E);
+  L.nlogits = cv.take<float>((size_t)c.num_tokens * E);
+  L.router_end = cv.off;
   L.sorted_pair = cv.take<int32_t>(P);
   L.pair_pos = cv.take<int32_t>(P);
   L.h = cv.take<char>(P * c.intermediate * elem_bytes(c));
@@ -130,6 +135,36 @@ moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_r
   if (x ? !w_router : !logits) return MOE_ERR_INVALID_ARGUMENT;
   return launched(launch_router(*cfg, x, w_router, x ? logit_bias : nullptr, logits,
                                 logits != nullptr, topk_idx, topk_w, nullptr, true, stream));
+}
+
+moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, const void* x,
+                              const void* w_router, const float* logit_bias, float* logits,
+                              int32_t* topk_idx, float* topk_w, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_options none{};
+  const moe_options& o = opt ? *opt : none;
+  if (!topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (x ? !w_router : !logits) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.noise && (!x || !o.w_noise)) return MOE_ERR_INVALID_ARGUMENT;
+  RouterExtras ex;
+  ex.sel_bias = o.select_bias;
+  if (!o.noise)
+    return launched(launch_router(*cfg, x, w_router, x ? logit_bias : nullptr, logits,
+                                  logits != nullptr, topk_idx, topk_w, nullptr, true, stream,
+                                  ex));
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.router_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  st = launched(launch_logits(*cfg, x, w_router, logit_bias, L.rlogits, stream));
+  if (st != MOE_OK) return st;
+  st = launched(launch_logits(*cfg, x, o.w_noise, nullptr, L.nlogits, stream));
+  if (st != MOE_OK) return st;
+  ex.noise = o.noise;
+  ex.nlogits = L.nlogits;
+  ex.logits_final = logits;
+  return launched(launch_router(*cfg, nullptr, nullptr, nullptr, L.rlogits, false, topk_idx,
+                                topk_w, nullptr, true, stream, ex));
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* expert_counts,
@@ -225,17 +260,19 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
   if (!logits || !topk_idx) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.aux_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!out.counts && !out.f && !out.P && !out.aux) return MOE_OK;
-  // per-block softmax sums from the logits (selection skipped)
+  if (!out.counts && !out.f && !out.P && !out.aux && !out.z_loss) return MOE_OK;
+  // per-block softmax (and z-loss) sums from the logits (selection skipped)
+  RouterExtras ex;
+  ex.zpart = out.z_loss ? L.zpart : nullptr;
   st = launched(launch_router(*cfg, nullptr, nullptr, nullptr, const_cast<float*>(logits), false,
-                              L.idx, L.w, L.partials, false, stream));
+                              L.idx, L.w, L.partials, false, stream, ex));
   if (st != MOE_OK) return st;
   // expert counts from the given selection (histogram + scan only)
   st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
                                 nullptr, false, 0, nullptr, stream));
   if (st != MOE_OK) return st;
-  return launched(launch_aux(*cfg, L.counts, L.partials, router_num_blocks(*cfg, true), L.fp, out,
-                             stream));
+  const int nb = router_num_blocks(*cfg, true);
+  return launched(launch_aux(*cfg, L.counts, L.partials, nb, L.fp, out, stream, ex.zpart, nb));
 }
 
 moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, const void* x,
@@ -249,21 +286,39 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
   const moe_options none{};
   const moe_options& o = opt ? *opt : none;
-  if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.capacity < 0 || (o.noise && !o.w_noise)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const moe_config& c = *cfg;
   int32_t* idx = topk_idx ? topk_idx : L.idx;
   float* w = topk_w ? topk_w : L.w;
   const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
+  float* partials = want_aux ? L.partials : nullptr;
+  RouterExtras ex;
+  ex.sel_bias = o.select_bias;
+  ex.zpart = aux.z_loss ? L.zpart : nullptr;
 
-  if (router_k_splits(c) > 1)
+  int router_blocks;
+  if (o.noise) {  // clean logits, noise logits, then the noisy top-k from them
+    st = launched(launch_logits(c, x, w_router, logit_bias, L.rlogits, stream));
+    if (st != MOE_OK) return st;
+    st = launched(launch_logits(c, x, o.w_noise, nullptr, L.nlogits, stream));
+    if (st != MOE_OK) return st;
+    ex.noise = o.noise;
+    ex.nlogits = L.nlogits;
+    ex.logits_final = router_logits;
+    st = launched(launch_router(c, nullptr, nullptr, nullptr, L.rlogits, false, idx, w, partials,
+                                true, stream, ex));
+    router_blocks = router_num_blocks(c, true);
+  } else if (router_k_splits(c) > 1) {
     st = launched(launch_router_split(c, x, w_router, logit_bias, L.rlogits, router_logits,
-                                      L.rpart, idx, w, want_aux ? L.partials : nullptr, stream));
-  else
+                                      L.rpart, idx, w, partials, stream, ex));
+    router_blocks = router_num_blocks(c, true);
+  } else {
     st = launched(launch_router(c, x, w_router, logit_bias, router_logits,
-                                router_logits != nullptr, idx, w,
-                                want_aux ? L.partials : nullptr, true, stream));
+                                router_logits != nullptr, idx, w, partials, true, stream, ex));
+    router_blocks = router_num_blocks(c, false);
+  }
   if (st != MOE_OK) return st;
   st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
                                 L.base, true, o.capacity, o.dropped, stream));
@@ -274,9 +329,9 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
   if (st != MOE_OK) return st;
   st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
   if (st != MOE_OK) return st;
-  if (want_aux)
-    st = launched(launch_aux(c, L.counts, L.partials,
-                             router_num_blocks(c, router_k_splits(c) > 1), L.fp, aux, stream));
+  if (want_aux || aux.z_loss)
+    st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, aux, stream, ex.zpart,
+                             router_blocks));
   return st;
 }
 

@@ -82,9 +82,21 @@ __device__ void row_tile_find(const int* s_scan, int E, int tile_id, int& expert
 // x == nullptr: logits are read from `logits`. prob_partials (nullable):
 // [router_num_blocks(c, x == nullptr), E] per-block sums of the full softmax.
 // do_select == 0 skips the top-k (only partials are produced).
+// Router variants and extra outputs (all nullable).
+struct RouterExtras {
+  const float* noise = nullptr;     // [T,E] logits-input mode: l + noise * softplus(nlogits)
+  const float* nlogits = nullptr;   // [T,E] x W_noise^T
+  const float* sel_bias = nullptr;  // [E] added to the top-k keys only
+  float* zpart = nullptr;           // [blocks] per-block sums of (ln sum_e exp l)^2
+  float* logits_final = nullptr;    // logits-input mode: the logits the softmax used
+};
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
-                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s);
+                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s,
+                         const RouterExtras& ex = {});
+// Logits only: out [T,E] = x w^T (+ bias).
+hipError_t launch_logits(const moe_config& c, const void* x, const void* w, const float* bias,
+                         float* out, hipStream_t s);
 int router_num_blocks(const moe_config& c, bool from_logits);
 // Split-K router for small token counts (bf16): K splits (1 = not worth it),
 // and the launch sequence partial logits -> fixed-order sum (+ bias) ->
@@ -93,7 +105,8 @@ int router_k_splits(const moe_config& c);
 hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
                                const float* bias, float* logits_ws, float* logits_out,
                                float* part, int32_t* topk_idx, float* topk_w,
-                               float* prob_partials, hipStream_t s);
+                               float* prob_partials, hipStream_t s,
+                               const RouterExtras& ex = {});
 
 // Dispatch: histogram per chunk, scan, stable scatter. capacity 0 keeps every
 // pair; > 0 keeps the first `capacity` pairs of each expert (pair_pos = -1 for
@@ -116,7 +129,10 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s);
 // fp_scratch: E doubles of workspace (per-expert f_e * P_e).
+// zpart [n_zpart] (nullable): per router block sums of (ln sum_e exp l)^2 for
+// out.z_loss.
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s);
+                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s,
+                      const float* zpart = nullptr, int n_zpart = 0);
 
 }  // namespace moe

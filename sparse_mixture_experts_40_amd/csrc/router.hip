@@ -14,7 +14,13 @@
 //     (order-preserving fp32 bits, then 0xFFFF - e), so equal logits go to
 //     the lower expert index; -0.0 is folded into +0.0 first.
 //  3. per-block sums of the full softmax over the block's tokens (fixed order)
-//     for the load-balance statistic P_e.
+//     for the load-balance statistic P_e, and of (ln sum_e exp l)^2 for the
+//     router z-loss.
+// Variants: noisy logits l + n * softplus(x W_noise) ([MOE-128x8] router
+// pseudocode, [LAB17] noisy top-k gating; the noise logits are a second
+// logits pass, the noise values an input) are formed when the logits are read;
+// a selection-only bias ([LAB17], DeepSeek-V3 balancing without an auxiliary
+// loss) is added to the top-k keys only, the weights use the unbiased logits.
 #include "moe_internal.h"
 
 namespace moe {
@@ -155,7 +161,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     int T, int H, int E, int k, int norm, const void* __restrict__ x, const void* __restrict__ wr,
     const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partials,
-    int do_select, int tpb) {
+    int do_select, int tpb, const float* __restrict__ noise, const float* __restrict__ nlogits,
+    const float* __restrict__ sel_bias, float* __restrict__ zpart) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * tpb;  // tpb = 64 when the logits are computed here
@@ -165,7 +172,17 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   if (logits_in) {
     for (int i = tid; i < tpb * E; i += kThreads) {
       const int t = i / E, e = i - t * E;
-      s_log[t * ls + e] = (t0 + t < T) ? logits_in[(size_t)(t0 + t) * E + e] : 0.0f;
+      float l = 0.0f;
+      if (t0 + t < T) {
+        const size_t g = (size_t)(t0 + t) * E + e;
+        l = logits_in[g];
+        if (noise) {  // l + n * softplus(nl), softplus(z) = ln(1 + e^z)
+          const float z = nlogits[g];
+          const float sp = z > 0.0f ? z + log1pf(expf(-z)) : log1pf(expf(z));
+          l = fmaf(noise[g], sp, l);
+        }
+      }
+      s_log[t * ls + e] = l;
     }
   } else if constexpr (BF16) {
     router_logits_mfma(T, H, E, t0, 0, H, static_cast<const uint16_t*>(x),
@@ -187,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
   const int EQ = (E + 63) >> 6;  // <= 4 experts per lane
   float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float zacc = 0.0f;  // this wave's sum of (ln sum_e exp l)^2 over its tokens
   // kNT tokens at a time per wave: their cross-lane reductions are independent
   // chains, so the shuffle latencies overlap.
   for (int tt = 0; tt < tpb / 4; tt += kNT) {
@@ -224,6 +242,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
       if (ok[u]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) pacc[q] += ex[u][q] * inv[u];
+        const float lse = m[u] + logf(ssum[u]);
+        zacc = fmaf(lse, lse, zacc);
       }
     }
 
@@ -239,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int e = lane + 64 * q;
-          key[u][q] = (q < EQ && e < E) ? order_key(v[u][q]) : 0u;
+          const bool live = q < EQ && e < E;
+          key[u][q] = live ? order_key(sel_bias ? v[u][q] + sel_bias[e] : v[u][q]) : 0u;
         }
       }
       for (int j = 0; j < k; ++j) {
@@ -263,7 +284,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
             for (int q = 0; q < 4; ++q)
               if (q == (ej >> 6)) key[u][q] = 0u;
           }
-          const float pj = expf(key_value(static_cast<uint32_t>(best[u] >> 32)) - m[u]) * inv[u];
+          // with a selection bias the key is not the logit: read the logit back
+          const float lj = sel_bias ? s_log[(tb0 + u) * ls + ej]
+                                    : key_value(static_cast<uint32_t>(best[u] >> 32));
+          const float pj = expf(lj - m[u]) * inv[u];
           psum[u] += pj;
           if (lane == j) {
             my_e[u] = ej;
@@ -282,6 +306,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     }
   }
 
+  if (zpart) {  // fixed order: waves 0..3, each in its token order
+    __shared__ float s_z[4];
+    __syncthreads();
+    if (lane == 0) s_z[wave] = zacc;
+    __syncthreads();
+    if (tid == 0) zpart[blockIdx.x] = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
+  }
   if (partials) {
     __syncthreads();  // every wave is done with s_log
     float* s_part = reinterpret_cast<float*>(smem);  // [4][256]
@@ -360,7 +391,7 @@ int router_k_splits(const moe_config& c) {
 hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
                                const float* bias, float* logits_ws, float* logits_out,
                                float* part, int32_t* topk_idx, float* topk_w,
-                               float* prob_partials, hipStream_t s) {
+                               float* prob_partials, hipStream_t s, const RouterExtras& ex) {
   const int ks = router_k_splits(c), E = c.num_experts;
   const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
@@ -372,13 +403,18 @@ hipError_t launch_router_split(const moe_config& c, const void* x, const void* w
   const int n = c.num_tokens * E;
   router_reduce_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(
       c.num_tokens, E, ks, part, bias, logits_ws, logits_out);
+  RouterExtras e2 = ex;
+  e2.noise = nullptr;  // the split path serves the plain logits
+  e2.nlogits = nullptr;
+  e2.logits_final = nullptr;
   return launch_router(c, nullptr, nullptr, nullptr, logits_ws, false, topk_idx, topk_w,
-                       prob_partials, true, s);
+                       prob_partials, true, s, e2);
 }
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
-                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s) {
+                         float* topk_w, float* prob_partials, bool do_select, hipStream_t s,
+                         const RouterExtras& ex) {
   const int E = c.num_experts;
   const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
@@ -391,16 +427,24 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   const int tpb = router_tpb(c, from_logits);
   const dim3 grid(router_num_blocks(c, from_logits)), block(kThreads);
   const float* lin = x ? nullptr : logits;
-  float* lout = (x && logits_out) ? logits : nullptr;
+  float* lout = x ? (logits_out ? logits : nullptr) : ex.logits_final;
+  const float* noise = x ? nullptr : ex.noise;
   if (c.dtype == MOE_DTYPE_BF16)
-    router_kernel<true><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
-                                                 c.norm_topk_prob, x, w_router, bias, lin, lout,
-                                                 topk_idx, topk_w, prob_partials, do_select, tpb);
+    router_kernel<true><<<grid, block, lds, s>>>(
+        c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
+        topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
+        ex.zpart);
   else
-    router_kernel<false><<<grid, block, lds, s>>>(c.num_tokens, c.hidden, E, c.top_k,
-                                                  c.norm_topk_prob, x, w_router, bias, lin, lout,
-                                                  topk_idx, topk_w, prob_partials, do_select, tpb);
+    router_kernel<false><<<grid, block, lds, s>>>(
+        c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
+        topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
+        ex.zpart);
   return hipGetLastError();
+}
+
+hipError_t launch_logits(const moe_config& c, const void* x, const void* w, const float* bias,
+                         float* out, hipStream_t s) {
+  return launch_router(c, x, w, bias, out, true, nullptr, nullptr, nullptr, false, s, {});
 }
 
 }  // namespace moe

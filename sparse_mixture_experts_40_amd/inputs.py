@@ -13,7 +13,10 @@ reproducible on any machine):
   * bf16 workloads round every value to bf16 (round to nearest even); arrays
     are then the uint16 bit patterns;
   * skewed workloads (zipf_s > 0) add the per-expert logit bias
-    log(Zipf_s(rank = e + 1)) = -s ln(e+1) - ln(sum_{r=1..E} r^-s).
+    log(Zipf_s(rank = e + 1)) = -s ln(e+1) - ln(sum_{r=1..E} r^-s);
+  * router variants (make_router_variant_inputs): w_noise [E,H] like the
+    router (scale 1/sqrt(H), bf16 for bf16 workloads), noise [T,E] float32
+    standard normals, select_bias [E] float32 normals times 0.5.
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ import numpy as np
 from .configs import MoEConfig
 
 CHUNK = 1 << 22
-TENSOR_IDS = {"x": 0, "w_router": 1, "w_gate": 2, "w_up": 3, "w_down": 4}
+TENSOR_IDS = {"x": 0, "w_router": 1, "w_gate": 2, "w_up": 3, "w_down": 4, "w_noise": 5,
+              "noise": 6, "select_bias": 7}
 
 
 def _workers() -> int:
@@ -106,3 +110,18 @@ def make_inputs(cfg: MoEConfig, seed: int | None = None, tokens: int | None = No
         d["w_up"] = normal_tensor((E, I, H), seed, TENSOR_IDS["w_up"], 1.0 / math.sqrt(H), bf)
         d["w_down"] = normal_tensor((E, H, I), seed, TENSOR_IDS["w_down"], 1.0 / math.sqrt(I), bf)
     return d
+
+
+def make_router_variant_inputs(cfg: MoEConfig, seed: int | None = None,
+                               tokens: int | None = None) -> dict:
+    """Inputs of the router variants: w_noise [E,H] (dtype of the workload),
+    noise [T,E] float32 draws, select_bias [E] float32."""
+    seed = cfg.seed if seed is None else seed
+    T = cfg.T if tokens is None else tokens
+    H, E = cfg.H, cfg.E
+    return {
+        "w_noise": normal_tensor((E, H), seed, TENSOR_IDS["w_noise"], 1.0 / math.sqrt(H),
+                                 cfg.dtype == "bf16"),
+        "noise": normal_tensor((T, E), seed, TENSOR_IDS["noise"], 1.0, False),
+        "select_bias": normal_tensor((E,), seed, TENSOR_IDS["select_bias"], 0.5, False),
+    }
