@@ -141,6 +141,51 @@ int orc_route_sel(int T, int E, int k, int norm, const float* logits, const floa
   return bad ? -1 : 0;
 }
 
+/* Entropy-driven number of experts per token, [QWEN3-ROUTE] §二 (dynamic
+ * TopK: the token's complexity is the entropy of its router probabilities):
+ *   H_t = -sum_e p[t,e] ln(max(p[t,e], 1e-10))
+ *   k_t = clamp( floor(k_min + (k_max - k_min) * H_t / ln E), k_min, k_max )
+ * then the k_t experts with the largest logits (ties to the lower index) take
+ * slots 0..k_t-1 and their weights are renormalised over those k_t (norm) or
+ * left as probabilities; slots k_t..k_max-1 are empty (idx -1, w 0).
+ * kt [T] receives k_t; xk [T] (nullable) the unfloored k_min + (k_max -
+ * k_min) H_t / ln E. */
+int orc_route_dynamic(int T, int E, int k_max, int k_min, int norm, const float* logits,
+                      int32_t* idx, double* w, int32_t* kt, double* xk) {
+  if (T < 0 || E < 2 || k_min < 1 || k_max < k_min || k_max > E || !logits || !idx || !w || !kt)
+    return -1;
+  double* probs = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * E);
+  if (!probs) return -1;
+  /* the full top-k_max selection and probabilities first */
+  if (orc_route(T, E, k_max, 0, logits, NULL, idx, w, probs)) {
+    free(probs);
+    return -1;
+  }
+  for (int t = 0; t < T; ++t) {
+    const double* p = probs + (size_t)t * E;
+    double H = 0.0;
+    for (int e = 0; e < E; ++e) H -= p[e] * log(p[e] > 1e-10 ? p[e] : 1e-10);
+    const double x = (double)k_min + (double)(k_max - k_min) * H / log((double)E);
+    int k = (int)floor(x);
+    if (k < k_min) k = k_min;
+    if (k > k_max) k = k_max;
+    kt[t] = k;
+    if (xk) xk[t] = x;
+    double psum = 0.0;
+    for (int j = 0; j < k; ++j) psum += w[(size_t)t * k_max + j]; /* unrenormalised p */
+    for (int j = 0; j < k_max; ++j) {
+      if (j < k) {
+        if (norm) w[(size_t)t * k_max + j] /= psum;
+      } else {
+        idx[(size_t)t * k_max + j] = -1;
+        w[(size_t)t * k_max + j] = 0.0;
+      }
+    }
+  }
+  free(probs);
+  return 0;
+}
+
 /* Noisy logits, [MOE-128x8] router pseudocode (noisy_logits = logits + noise *
  * softplus(x @ W_noise)) and [LAB17] noisy top-k gating (standard normal noise
  * times Softplus(W_noise x) added to the gate logits):
@@ -184,7 +229,8 @@ int orc_z_loss(int T, int E, const float* logits, double* z) {
  * tokens of one expert next to each other, and keep the inverse):
  *   counts[e] = #{p : idx[p] == e};  offsets = exclusive prefix sum;
  *   sorted_pair = pair ids grouped by expert, ascending inside a group;
- *   pair_pos[sorted_pair[i]] = i. */
+ *   pair_pos[sorted_pair[i]] = i. An idx of -1 is an empty slot: not a pair,
+ *   pair_pos = -1. */
 int orc_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
                  int32_t* sorted_pair, int32_t* pair_pos) {
   if (T < 0 || E < 1 || k < 1 || !idx || !counts || !offsets || !sorted_pair || !pair_pos)
@@ -192,6 +238,7 @@ int orc_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32
   const long P = (long)T * k;
   for (int e = 0; e < E; ++e) counts[e] = 0;
   for (long p = 0; p < P; ++p) {
+    if (idx[p] == -1) continue; /* empty slot (a token routed to fewer than k experts) */
     if (idx[p] < 0 || idx[p] >= E) return -1;
     counts[idx[p]] += 1;
   }
@@ -201,6 +248,10 @@ int orc_dispatch(int T, int E, int k, const int32_t* idx, int32_t* counts, int32
   if (!fill) return -1;
   for (int e = 0; e < E; ++e) fill[e] = offsets[e];
   for (long p = 0; p < P; ++p) {
+    if (idx[p] == -1) {
+      pair_pos[p] = -1;
+      continue;
+    }
     int32_t pos = fill[idx[p]]++;
     sorted_pair[pos] = (int32_t)p;
     pair_pos[p] = pos;
@@ -244,6 +295,10 @@ int orc_dispatch_capacity(int T, int E, int k, int capacity, const int32_t* idx,
   *dropped = 0;
   for (long p = 0; p < P; ++p) { /* the walk: keep or drop, in pair order */
     const int e = idx[p];
+    if (e == -1) { /* empty slot: not a pair */
+      pair_pos[p] = -2;
+      continue;
+    }
     if (e < 0 || e >= E) {
       free(accepted);
       return -1;
@@ -261,7 +316,10 @@ int orc_dispatch_capacity(int T, int E, int k, int capacity, const int32_t* idx,
   for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + accepted[e];
   for (int e = 0; e < E; ++e) accepted[e] = offsets[e]; /* next free slot */
   for (long p = 0; p < P; ++p) {
-    if (pair_pos[p] < 0) continue;
+    if (pair_pos[p] < 0) {
+      pair_pos[p] = -1; /* dropped or empty */
+      continue;
+    }
     const int32_t pos = accepted[idx[p]]++;
     sorted_pair[pos] = (int32_t)p;
     pair_pos[p] = pos;
@@ -343,17 +401,21 @@ int orc_combine(int T, int H, int k, const double* w, const double* y_pair, doub
 }
 
 /* Load-balance statistics, [MOE-128x8] load-balancing section, n = E:
- *   f_e = counts[e] / (T*k)       (fraction of routed pairs)
+ *   f_e = counts[e] / sum_e' counts[e']   (fraction of routed pairs; = T*k
+ *                                         when every token takes k experts)
  *   P_e = (1/T) sum_t probs[t,e]  (mean full-softmax probability)
  *   aux = E * sum_e f_e * P_e */
 int orc_aux(int T, int E, int k, const int32_t* counts, const double* probs, double* f,
             double* P, double* aux) {
   if (T < 1 || E < 1 || k < 1 || !counts || !probs || !f || !P || !aux) return -1;
   double acc = 0.0;
+  long routed = 0; /* T*k, or fewer when tokens take fewer than k experts */
+  for (int e = 0; e < E; ++e) routed += counts[e];
+  (void)k;
   for (int e = 0; e < E; ++e) {
     double s = 0.0;
     for (int t = 0; t < T; ++t) s += probs[(size_t)t * E + e];
-    f[e] = (double)counts[e] / ((double)T * (double)k);
+    f[e] = routed > 0 ? (double)counts[e] / (double)routed : 0.0;
     P[e] = s / (double)T;
     acc += f[e] * P[e];
   }

@@ -47,6 +47,7 @@ def _load():
         lib.orc_route_sel.argtypes = [i, i, i, i, P, P, P, P, P, P]
         lib.orc_noisy_logits.argtypes = [i, i, P, P, P, P]
         lib.orc_z_loss.argtypes = [i, i, P, P]
+        lib.orc_route_dynamic.argtypes = [i, i, i, i, i, P, P, P, P, P]
         lib.orc_dispatch.argtypes = [i, i, i, P, P, P, P, P]
         lib.orc_expert_rows.argtypes = [i, i, i, P, P, P, P, i, P, P, i, P]
         lib.orc_combine.argtypes = [i, i, i, P, P, P]
@@ -59,7 +60,8 @@ def _load():
         for f in (lib.orc_logits, lib.orc_route, lib.orc_dispatch, lib.orc_expert_rows,
                   lib.orc_combine, lib.orc_combine_kept, lib.orc_capacity,
                   lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens,
-                  lib.orc_route_sel, lib.orc_noisy_logits, lib.orc_z_loss):
+                  lib.orc_route_sel, lib.orc_noisy_logits, lib.orc_z_loss,
+                  lib.orc_route_dynamic):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -116,6 +118,20 @@ def route(lg: np.ndarray, k: int, norm: bool, forced_idx: np.ndarray | None = No
     _check(_load().orc_route_sel(T, E, k, int(bool(norm)), _p(lg), _p(sel_bias), _p(forced_idx),
                                  _p(idx), _p(w), _p(probs)), "route")
     return idx, w, probs
+
+
+def route_dynamic(lg: np.ndarray, k_max: int, k_min: int, norm: bool):
+    """Entropy-driven k per token. Returns (idx int32 [T,k_max] (-1 past k_t),
+    w float64 [T,k_max] (0 past k_t), kt int32 [T], x float64 [T] (unfloored))."""
+    lg = _c(lg, np.float32)
+    T, E = lg.shape
+    idx = np.empty((T, k_max), np.int32)
+    w = np.empty((T, k_max), np.float64)
+    kt = np.empty(T, np.int32)
+    x = np.empty(T, np.float64)
+    _check(_load().orc_route_dynamic(T, E, k_max, k_min, int(bool(norm)), _p(lg), _p(idx), _p(w),
+                                     _p(kt), _p(x)), "route_dynamic")
+    return idx, w, kt, x
 
 
 def noisy_logits(lg: np.ndarray, nlg: np.ndarray, noise: np.ndarray) -> np.ndarray:
@@ -250,7 +266,7 @@ def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool =
 
 
 def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_bias=None,
-                    keep=None, round_h: bool = False):
+                    keep=None, round_h: bool = False, k_min: int = 0):
     """Block forward of the listed tokens with the router variants, composed
     from the steps above: logits (+ bias), noisy logits if `noise` [T,E] and
     `w_noise` [E,H] are given (the noise rows of the listed tokens are used),
@@ -267,10 +283,17 @@ def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_b
     if noise is not None:
         nlg = logits(xs, w_noise)
         lg = noisy_logits(lg, nlg, np.asarray(noise, np.float32)[tokens])
-    idx, w, _ = route(lg, cfg.k, cfg.norm, sel_bias=sel_bias)
+    kt = None
+    if k_min:  # entropy-driven k (no selection bias with it)
+        assert sel_bias is None
+        idx, w, kt, _ = route_dynamic(lg, cfg.k, k_min, cfg.norm)
+        live = idx >= 0
+        keep = live if keep is None else (np.asarray(keep, bool) & live)
+    else:
+        idx, w, _ = route(lg, cfg.k, cfg.norm, sel_bias=sel_bias)
     n = tokens.shape[0]
     tok = np.repeat(np.arange(n, dtype=np.int32), cfg.k)
-    y = expert_rows(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tok, idx.ravel(),
-                    round_h=round_h)
+    ex = np.where(idx >= 0, idx, 0).ravel().astype(np.int32)  # empty slots: any row, not kept
+    y = expert_rows(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tok, ex, round_h=round_h)
     out = combine(w, y, keep)
-    return {"logits": lg, "idx": idx, "w": w, "out": out}
+    return {"logits": lg, "idx": idx, "w": w, "out": out, "kt": kt}

@@ -218,6 +218,60 @@ def test_forward_variant_composes_the_plain_forward(orc):
     assert (z["idx"] == a["idx"]).all()
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_dynamic_k_follows_entropy(orc, seed):
+    from scipy.stats import entropy
+    rng = _rng(330 + seed)
+    T, E, k_max, k_min = 60, 32, 8, 4
+    scale = rng.choice([0.3, 1.0, 3.0, 8.0], size=(T, 1))  # flat to peaked rows
+    lg = (rng.standard_normal((T, E)) * scale).astype(np.float32)
+    for norm in (True, False):
+        idx, w, kt, x = orc.route_dynamic(lg, k_max, k_min, norm)
+        p = sp_softmax(lg.astype(np.float64), axis=1)
+        x_ref = k_min + (k_max - k_min) * entropy(p, axis=1) / math.log(E)
+        np.testing.assert_allclose(x, x_ref, rtol=0, atol=1e-9)
+        for t in range(T):
+            if abs(x_ref[t] - round(x_ref[t])) > 1e-9:
+                assert kt[t] == min(k_max, max(k_min, math.floor(x_ref[t])))
+            k = kt[t]
+            order = _brute_topk(lg[t], E)
+            assert idx[t, :k].tolist() == order[:k]
+            assert (idx[t, k:] == -1).all() and (w[t, k:] == 0.0).all()
+            sel = p[t, order[:k]]
+            np.testing.assert_allclose(w[t, :k], sel / sel.sum() if norm else sel, rtol=1e-12)
+    # closed forms: a uniform row has H = ln E (k_max); a dominant logit H ~ 0 (k_min)
+    flat = np.zeros((1, E), np.float32)
+    _, _, kt0, x0 = orc.route_dynamic(flat, k_max, k_min, True)
+    assert x0[0] == pytest.approx(k_max, abs=1e-12)
+    peak = np.zeros((1, E), np.float32)
+    peak[0, 5] = 80.0
+    i1, w1, kt1, _ = orc.route_dynamic(peak, k_max, k_min, True)
+    assert kt1[0] == k_min and i1[0, 0] == 5 and (i1[0, k_min:] == -1).all()
+
+
+def test_dispatch_and_aux_with_empty_slots(orc):
+    rng = _rng(340)
+    T, E, k = 200, 16, 6
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    kt = rng.integers(2, k + 1, T)
+    for t in range(T):
+        idx[t, kt[t]:] = -1
+    counts, offsets, sp, pp = orc.dispatch(idx, E)
+    flat = idx.ravel()
+    live = np.flatnonzero(flat >= 0)
+    assert counts.sum() == kt.sum() == offsets[E]
+    assert (counts == np.bincount(flat[live], minlength=E)).all()
+    ref = live[np.argsort(flat[live], kind="stable")]
+    assert (sp[: offsets[E]] == ref).all()
+    assert (pp[flat < 0] == -1).all() and (sp[pp[live]] == live).all()
+    _, o2, sp2, pp2, d2 = orc.dispatch_capacity(idx, E, 10 ** 6)
+    assert d2 == 0 and (o2 == offsets).all() and (pp2 == pp).all()
+    probs = sp_softmax(rng.standard_normal((T, E)), axis=1)
+    f, P, aux = orc.aux(counts, probs, k)
+    assert f.sum() == pytest.approx(1.0, abs=1e-12)  # fraction of the routed pairs
+    np.testing.assert_allclose(f, counts / counts.sum(), rtol=1e-15)
+
+
 # ------------------------------------------------------------------- dispatch
 
 
