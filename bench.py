@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--capacity-factor CF]   # capacity-limited dispatch, C = ceil(T*k*CF/E)
                     [--router noise|bias|noise+bias]   # router variants (seeded inputs)
+                    [--dynamic-k-min KMIN]   # entropy-driven k in [KMIN, k]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
 
 A step is one moe_layer_forward (router, dispatch, gate/up GEMM, down GEMM,
@@ -139,6 +140,8 @@ def main():
                     help="> 0: capacity-limited dispatch with C = ceil(T*k*CF/E)")
     ap.add_argument("--router", default="plain", choices=["plain", "noise", "bias", "noise+bias"],
                     help="router variant: noisy top-k and/or selection-only bias")
+    ap.add_argument("--dynamic-k-min", type=int, default=0,
+                    help="> 0: entropy-driven number of experts per token in [KMIN, k]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times: the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -180,7 +183,8 @@ def main():
     blk = binding.MoEBlock(cfg, inp, capacity=cap,
                            noise=var.get("noise") if "noise" in args.router else None,
                            w_noise=var.get("w_noise") if "noise" in args.router else None,
-                           select_bias=var.get("select_bias") if "bias" in args.router else None)
+                           select_bias=var.get("select_bias") if "bias" in args.router else None,
+                           dynamic_k_min=args.dynamic_k_min)
     x = binding.to_device(inp["x"])
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
@@ -212,7 +216,8 @@ def main():
     sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     h = torch.empty(T * k, cfg.I, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
-    binding.router_topk(c, x, blk.w_router, blk.logit_bias, None, idx, wts)
+    # the same router (variants included) as the timed block
+    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, None, idx, wts, blk.ws)
     if cap:
         binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
     else:
@@ -273,6 +278,10 @@ def main():
         line["config"].update(line_cap)
     if args.router != "plain":
         line["config"]["router"] = args.router
+    if args.dynamic_k_min:
+        kt = blk.k_per_token.cpu().numpy()
+        line["config"].update({"dynamic_k_min": args.dynamic_k_min,
+                               "mean_k": float(kt.mean()), "routed_pairs": int(kt.sum())})
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

@@ -84,7 +84,8 @@ typedef struct {
 /* Load-balance outputs; every field may be NULL (then it is not written).
  * z_loss is described at the field.
  *   counts[E] int32 : n_e = number of pairs routed to expert e
- *   f[E]      fp32  : f_e = n_e / (T*k), the fraction of routed pairs
+ *   f[E]      fp32  : f_e = n_e / sum_e' n_e', the fraction of routed pairs
+ *                     (= n_e / (T*k) unless some slots are empty)
  *   P[E]      fp32  : P_e = (1/T) * sum_t softmax(l_t)_e, the mean router
  *                     probability (full softmax, before top-k)
  *   aux[1]    fp32  : E * sum_e f_e * P_e
@@ -121,6 +122,19 @@ typedef struct {
    * logits for the top-k choice only (fp32 keys l + b, ties to the lower
    * index); the weights and statistics use the unbiased logits. NULL: none. */
   const float* select_bias;
+  /* Entropy-driven number of experts per token, [QWEN3-ROUTE] §二 (dynamic
+   * TopK, with the entropy of the router probabilities as the token's
+   * complexity): 0 = every token takes top_k experts. k_min in [1, top_k]:
+   *   H_t = -sum_e p[t,e] ln(max(p[t,e], 1e-10)),
+   *   k_t = clamp(floor(k_min + (top_k - k_min) * H_t / ln E), k_min, top_k)
+   * (the page: k_min 4, top_k 8); token t keeps its k_t best experts in slots
+   * 0..k_t-1 (weights renormalised over those k_t iff norm_topk_prob) and
+   * slots k_t..top_k-1 are empty: topk_idx -1, topk_w 0. Every entry point
+   * that takes topk_idx treats a negative id as an empty slot (no pair);
+   * f_e is then n_e over the routed pairs. Needs E >= 2; not combined with
+   * select_bias (MOE_ERR_UNSUPPORTED). */
+  int32_t dynamic_k_min;
+  int32_t* k_per_token; /* [T] int32 out or NULL: k_t of every token */
 } moe_options;
 
 /* Bytes of workspace every entry point below needs for `cfg` (the maximum
@@ -165,7 +179,8 @@ moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, con
 /* Dispatch: group the T*k pairs by expert (a stable counting sort).
  * Replaces the one-hot mask + per-expert torch.where loop of [QWEN3-READ]
  * (forward code) by the token permutation described in its §三.
- *   topk_idx       [T,k] int32 in, every value in [0,E).
+ *   topk_idx       [T,k] int32 in, every value in [0,E), or negative for an
+ *                  empty slot (not a pair; pair_pos -1).
  *   expert_counts  [E]   int32 out: n_e.
  *   expert_offsets [E+1] int32 out: exclusive prefix sum of n_e; [E] = T*k.
  *   sorted_pair    [T*k] int32 out: pair ids grouped by expert, ascending

@@ -38,7 +38,8 @@ class moe_config(ctypes.Structure):
 class moe_options(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p),
                 ("noise", ctypes.c_void_p), ("w_noise", ctypes.c_void_p),
-                ("select_bias", ctypes.c_void_p)]
+                ("select_bias", ctypes.c_void_p), ("dynamic_k_min", ctypes.c_int32),
+                ("k_per_token", ctypes.c_void_p)]
 
 
 class moe_aux_out(ctypes.Structure):
@@ -128,11 +129,11 @@ def router_topk(c: moe_config, x, w_router, logit_bias, logits, topk_idx, topk_w
            "moe_router_topk")
 
 
-def options(capacity: int = 0, dropped=None, noise=None, w_noise=None,
-            select_bias=None) -> moe_options:
+def options(capacity: int = 0, dropped=None, noise=None, w_noise=None, select_bias=None,
+            dynamic_k_min: int = 0, k_per_token=None) -> moe_options:
     """moe_options from tensors (the tensors must outlive the calls)."""
     return moe_options(int(capacity), _ptr(dropped), _ptr(noise), _ptr(w_noise),
-                       _ptr(select_bias))
+                       _ptr(select_bias), int(dynamic_k_min), _ptr(k_per_token))
 
 
 def router_topk_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, logits,
@@ -245,19 +246,21 @@ class MoEBlock:
     whole forward with one library call per step."""
 
     def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0,
-                 noise=None, w_noise=None, select_bias=None):
+                 noise=None, w_noise=None, select_bias=None, dynamic_k_min: int = 0):
         """capacity > 0: capacity-limited dispatch (see moe_capacity); noise
         [T,E] fp32 + w_noise [E,H]: noisy top-k; select_bias [E] fp32:
-        selection-only bias (numpy arrays or tensors)."""
+        selection-only bias (numpy arrays or tensors); dynamic_k_min > 0:
+        entropy-driven k in [dynamic_k_min, k]."""
         self.cfg = cfg
         self.c = make_config(cfg)
         self.dropped = torch.zeros(1, dtype=torch.int32, device=device)
         self.noise = _as_tensor(noise, device)
         self.w_noise = _as_tensor(w_noise, device)
         self.select_bias = _as_tensor(select_bias, device)
-        variant = capacity or noise is not None or select_bias is not None
-        self.opts = options(capacity, self.dropped, self.noise, self.w_noise,
-                            self.select_bias) if variant else None
+        self.k_per_token = torch.empty(cfg.T, dtype=torch.int32, device=device)
+        variant = capacity or noise is not None or select_bias is not None or dynamic_k_min
+        self.opts = options(capacity, self.dropped, self.noise, self.w_noise, self.select_bias,
+                            dynamic_k_min, self.k_per_token) if variant else None
         self.w_router = to_device(inputs["w_router"], device)
         self.w_gate = to_device(inputs["w_gate"], device)
         self.w_up = to_device(inputs["w_up"], device)

@@ -74,13 +74,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int T, int H, int k_r
 }
 
 // One block per expert: P_e = (1/T) sum_b partials[b][e] (thread b takes the
-// fixed set b, b+256, ...; then a fixed-shape tree), f_e = n_e / (T k).
+// fixed set b, b+256, ...; then a fixed-shape tree), f_e = n_e / sum_e' n_e'
+// (= n_e / (T k) when every token takes k experts).
 __global__ __launch_bounds__(kThreads) void aux_expert_kernel(
     int T, int E, int k, const int32_t* __restrict__ counts, const float* __restrict__ partials,
     int np, int32_t* __restrict__ c_out, float* __restrict__ f_out, float* __restrict__ p_out,
     double* __restrict__ fp_out) {
   __shared__ double s[kThreads];
+  __shared__ int s_routed;  // sum of the counts: T*k, or fewer with empty slots
   const int e = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) s_routed = 0;
+  __syncthreads();
+  if (tid < E) atomicAdd(&s_routed, counts[tid]);  // integer: exact, order-free
   double acc = 0.0;
   for (int b = tid; b < np; b += kThreads) acc += (double)partials[(size_t)b * E + e];
   s[tid] = acc;
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void aux_expert_kernel(
   }
   if (tid == 0) {
     const int n = counts[e];
-    const double f = (double)n / ((double)T * (double)k);
+    const double f = s_routed > 0 ? (double)n / (double)s_routed : 0.0;
     const double P = s[0] / (double)T;
     if (c_out) c_out[e] = n;
     if (f_out) f_out[e] = (float)f;

@@ -18,7 +18,9 @@
 // an expert accepts while below its capacity): the pair of rank r inside its
 // expert is kept iff r < capacity, i.e. each expert keeps its first
 // `capacity` pairs in pair order; a dropped pair gets pair_pos = -1. A
-// capacity of 0 keeps every pair.
+// capacity of 0 keeps every pair. A negative expert id marks an empty slot (a
+// token routed to fewer than k experts): it is not a pair and gets
+// pair_pos = -1.
 // No device-to-host traffic; everything stays on the stream.
 #include "moe_internal.h"
 
@@ -41,7 +43,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(int P, int E,
   const int p0 = blockIdx.x * kChunk;
   for (int i = tid; i < kChunk; i += kThreads) {
     const int p = p0 + i;
-    if (p < P) atomicAdd(&s_h[clamp_expert(idx[p], E)], 1);
+    if (p < P) {
+      const int v = idx[p];
+      if (v >= 0) atomicAdd(&s_h[clamp_expert(v, E)], 1);  // v < 0: empty slot
+    }
   }
   __syncthreads();
   if (tid < E) hist[(size_t)blockIdx.x * E + tid] = s_h[tid];
@@ -104,8 +109,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
   for (int it = 0; it < kChunk / kThreads; ++it) {
     const int p = blockIdx.x * kChunk + it * kThreads + tid;
-    const bool valid = p < P;
-    const int v = valid ? clamp_expert(idx[p], E) : 0;
+    const int raw = p < P ? idx[p] : -1;
+    const bool valid = raw >= 0;  // a negative id is an empty slot: no pair
+    if (p < P && !valid) pair_pos[p] = -1;
+    const int v = valid ? clamp_expert(raw, E) : 0;
     unsigned long long same = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {

@@ -50,6 +50,15 @@ moe_status check_config(const moe_config* cfg) {
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Router fields of moe_options against the configuration.
+moe_status check_router_options(const moe_config& c, const moe_options& o) {
+  if ((o.noise != nullptr) != (o.w_noise != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.dynamic_k_min < 0 || o.dynamic_k_min > c.top_k) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.dynamic_k_min > 0 && c.num_experts < 2) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.dynamic_k_min > 0 && o.select_bias) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // Workspace regions. Each entry point carves the prefix it needs, in order.
 struct Layout {
   int32_t* hist;
@@ -147,9 +156,13 @@ moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, con
   const moe_options& o = opt ? *opt : none;
   if (!topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   if (x ? !w_router : !logits) return MOE_ERR_INVALID_ARGUMENT;
-  if (o.noise && (!x || !o.w_noise)) return MOE_ERR_INVALID_ARGUMENT;
+  st = check_router_options(*cfg, o);
+  if (st != MOE_OK) return st;
+  if (o.noise && !x) return MOE_ERR_INVALID_ARGUMENT;
   RouterExtras ex;
   ex.sel_bias = o.select_bias;
+  ex.k_min = o.dynamic_k_min;
+  ex.kt_out = o.k_per_token;
   if (!o.noise)
     return launched(launch_router(*cfg, x, w_router, x ? logit_bias : nullptr, logits,
                                   logits != nullptr, topk_idx, topk_w, nullptr, true, stream,
@@ -286,7 +299,9 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
   const moe_options none{};
   const moe_options& o = opt ? *opt : none;
-  if (o.capacity < 0 || (o.noise && !o.w_noise)) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  st = check_router_options(*cfg, o);
+  if (st != MOE_OK) return st;
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const moe_config& c = *cfg;
@@ -297,6 +312,8 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
   RouterExtras ex;
   ex.sel_bias = o.select_bias;
   ex.zpart = aux.z_loss ? L.zpart : nullptr;
+  ex.k_min = o.dynamic_k_min;
+  ex.kt_out = o.k_per_token;
 
   int router_blocks;
   if (o.noise) {  // clean logits, noise logits, then the noisy top-k from them

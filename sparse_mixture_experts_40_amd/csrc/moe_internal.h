@@ -89,6 +89,8 @@ struct RouterExtras {
   const float* sel_bias = nullptr;  // [E] added to the top-k keys only
   float* zpart = nullptr;           // [blocks] per-block sums of (ln sum_e exp l)^2
   float* logits_final = nullptr;    // logits-input mode: the logits the softmax used
+  int k_min = 0;                    // > 0: entropy-driven k in [k_min, top_k]
+  int32_t* kt_out = nullptr;        // [T] the k of every token (dynamic k)
 };
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,

@@ -20,7 +20,9 @@
 // pseudocode, [LAB17] noisy top-k gating; the noise logits are a second
 // logits pass, the noise values an input) are formed when the logits are read;
 // a selection-only bias ([LAB17], DeepSeek-V3 balancing without an auxiliary
-// loss) is added to the top-k keys only, the weights use the unbiased logits.
+// loss) is added to the top-k keys only, the weights use the unbiased logits;
+// entropy-driven k ([QWEN3-ROUTE] §二 dynamic TopK) keeps the first k_t slots
+// and marks the others empty (-1, weight 0).
 #include "moe_internal.h"
 
 namespace moe {
@@ -162,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partials,
     int do_select, int tpb, const float* __restrict__ noise, const float* __restrict__ nlogits,
-    const float* __restrict__ sel_bias, float* __restrict__ zpart) {
+    const float* __restrict__ sel_bias, float* __restrict__ zpart, int k_min,
+    int32_t* __restrict__ kt_out) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * tpb;  // tpb = 64 when the logits are computed here
@@ -247,6 +250,32 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
       }
     }
 
+    // entropy-driven number of experts ([QWEN3-ROUTE] §二 dynamic TopK):
+    // k_t = clamp(floor(k_min + (k - k_min) H_t / ln E)), H_t = -sum p ln max(p, 1e-10)
+    int kt[kNT];
+#pragma unroll
+    for (int u = 0; u < kNT; ++u) kt[u] = k;
+    if (k_min > 0) {
+      float hs[kNT];
+#pragma unroll
+      for (int u = 0; u < kNT; ++u) {
+        hs[u] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float pe = ex[u][q] * inv[u];
+          if (q < EQ && lane + 64 * q < E) hs[u] = fmaf(pe, logf(fmaxf(pe, 1e-10f)), hs[u]);
+        }
+      }
+      wave_sum_n(hs);
+      const float span = (float)(k - k_min) / logf((float)E);
+#pragma unroll
+      for (int u = 0; u < kNT; ++u) {
+        const int kk = (int)floorf(fmaf(-hs[u], span, (float)k_min));
+        kt[u] = kk < k_min ? k_min : (kk > k ? k : kk);
+        if (kt_out && ok[u] && lane == 0) kt_out[t0 + tb0 + u] = kt[u];
+      }
+    }
+
     if (do_select) {
       uint32_t key[kNT][4];
       int my_e[kNT];
@@ -288,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
           const float lj = sel_bias ? s_log[(tb0 + u) * ls + ej]
                                     : key_value(static_cast<uint32_t>(best[u] >> 32));
           const float pj = expf(lj - m[u]) * inv[u];
-          psum[u] += pj;
+          if (j < kt[u]) psum[u] += pj;
           if (lane == j) {
             my_e[u] = ej;
             my_p[u] = pj;
@@ -298,9 +327,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 #pragma unroll
       for (int u = 0; u < kNT; ++u) {
         const int gt = t0 + tb0 + u;
-        if (ok[u] && lane < k) {
-          topk_idx[(size_t)gt * k + lane] = my_e[u];
-          topk_w[(size_t)gt * k + lane] = norm ? my_p[u] / psum[u] : my_p[u];
+        if (ok[u] && lane < k) {  // slots past k_t are empty (dynamic k)
+          const bool live = lane < kt[u];
+          topk_idx[(size_t)gt * k + lane] = live ? my_e[u] : -1;
+          topk_w[(size_t)gt * k + lane] = live ? (norm ? my_p[u] / psum[u] : my_p[u]) : 0.0f;
         }
       }
     }
@@ -433,12 +463,12 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
     router_kernel<true><<<grid, block, lds, s>>>(
         c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
         topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
-        ex.zpart);
+        ex.zpart, ex.k_min, ex.kt_out);
   else
     router_kernel<false><<<grid, block, lds, s>>>(
         c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
         topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
-        ex.zpart);
+        ex.zpart, ex.k_min, ex.kt_out);
   return hipGetLastError();
 }
 
