@@ -372,6 +372,103 @@ int orc_expert_rows(int H, int I, int dtype, const void* x, const void* wg, cons
   return bad ? -1 : 0;
 }
 
+/* 4-bit group-quantised weights, [MOE-128x8] 参数量化与存储优化 (4-bit codes,
+ * group_size 128, an independent scale and bias per group):
+ *   w[e,n,k] = scale[e,n,g] * q[e,n,k] + bias[e,n,g],  g = k / 128,
+ *   q = the 4-bit code of element k: byte (e*N + n)*K/2 + k/2 holds element 2i
+ *   in its low nibble and 2i+1 in its high nibble;
+ *   sb[((e*N + n)*G + g)*2 + {0,1}] = (scale, bias) as bf16, G = K/128. */
+static double w4_elem(const uint8_t* codes, const uint16_t* sb, int N, int K, size_t e, size_t n,
+                      size_t k) {
+  const size_t row = e * (size_t)N + n;
+  const uint8_t byte = codes[(row * (size_t)K + k) / 2];
+  const int q = (k & 1) ? (byte >> 4) : (byte & 0xF);
+  const size_t g = row * (size_t)(K / 128) + k / 128;
+  const double scale = elem(sb, 1, 2 * g), bias = elem(sb, 1, 2 * g + 1);
+  return scale * (double)q + bias;
+}
+
+/* The dequantised matrices [E,N,K] as double. */
+int orc_dequant_w4(int E, int N, int K, const uint8_t* codes, const uint16_t* sb, double* w) {
+  if (E < 1 || N < 1 || K < 128 || K % 128 || !codes || !sb || !w) return -1;
+#pragma omp parallel for schedule(static)
+  for (int e = 0; e < E; ++e)
+    for (int n = 0; n < N; ++n)
+      for (int k = 0; k < K; ++k)
+        w[((size_t)e * N + n) * K + k] = w4_elem(codes, sb, N, K, e, n, k);
+  return 0;
+}
+
+/* orc_expert_rows with 4-bit weights, dequantised element by element (the
+ * same definition as orc_dequant_w4 followed by orc_expert_rows):
+ *   gate/up codes [E,I,H/2] with sb [E,I,H/128,2]; down codes [E,H,I/2] with
+ *   sb [E,H,I/128,2]; x [*,H] of dtype (0 fp32, 1 bf16). */
+int orc_expert_rows_w4(int H, int I, int dtype, const void* x, const uint8_t* cg,
+                       const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
+                       const uint8_t* cd, const uint16_t* sd, int n, const int32_t* tok,
+                       const int32_t* ex, int round_h, double* y) {
+  if (H < 128 || I < 128 || H % 128 || I % 128 || n < 0 || !x || !cg || !sg || !cu || !su ||
+      !cd || !sd || !tok || !ex || !y)
+    return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!a) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int r = 0; r < n; ++r) {
+      if (!a) continue;
+      const size_t t = (size_t)tok[r], e = (size_t)ex[r];
+      for (int i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int h = 0; h < H; ++h) {
+          const double xv = elem(x, dtype, t * (size_t)H + h);
+          g += w4_elem(cg, sg, I, H, e, i, h) * xv;
+          u += w4_elem(cu, su, I, H, e, i, h) * xv;
+        }
+        a[i] = g / (1.0 + exp(-g)) * u;
+        if (round_h) round_bf16_inplace(&a[i]);
+      }
+      for (int h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (int i = 0; i < I; ++i) s += w4_elem(cd, sd, H, I, e, h, i) * a[i];
+        y[(size_t)r * H + h] = s;
+      }
+    }
+    free(a);
+  }
+  return bad ? -1 : 0;
+}
+
+/* orc_expert_rows for double weight arrays (x of dtype 0 / 1): used to check
+ * the 4-bit path against dequantise-first. */
+int orc_expert_rows_f64w(int H, int I, int dtype, const void* x, const double* wg,
+                         const double* wu, const double* wd, int n, const int32_t* tok,
+                         const int32_t* ex, double* y) {
+  if (H < 1 || I < 1 || n < 0 || !x || !wg || !wu || !wd || !tok || !ex || !y) return -1;
+  for (int r = 0; r < n; ++r) {
+    const size_t t = (size_t)tok[r], e = (size_t)ex[r];
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!a) return -1;
+    for (int i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      for (int h = 0; h < H; ++h) {
+        const double xv = elem(x, dtype, t * (size_t)H + h);
+        g += wg[(e * I + i) * (size_t)H + h] * xv;
+        u += wu[(e * I + i) * (size_t)H + h] * xv;
+      }
+      a[i] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int h = 0; h < H; ++h) {
+      double s = 0.0;
+      for (int i = 0; i < I; ++i) s += wd[(e * H + h) * (size_t)I + i] * a[i];
+      y[(size_t)r * H + h] = s;
+    }
+    free(a);
+  }
+  return 0;
+}
+
 /* Routing-weighted combine, [QWEN3-READ] forward code (expert output times its
  * routing weight, accumulated into the token's row), over the kept slots:
  *   out[t,:] = sum_{j : keep[t,j]} w[t,j] * y_pair[t*k+j, :]  (slot order, double)

@@ -48,6 +48,9 @@ def _load():
         lib.orc_noisy_logits.argtypes = [i, i, P, P, P, P]
         lib.orc_z_loss.argtypes = [i, i, P, P]
         lib.orc_route_dynamic.argtypes = [i, i, i, i, i, P, P, P, P, P]
+        lib.orc_dequant_w4.argtypes = [i, i, i, P, P, P]
+        lib.orc_expert_rows_w4.argtypes = [i, i, i, P, P, P, P, P, P, P, i, P, P, i, P]
+        lib.orc_expert_rows_f64w.argtypes = [i, i, i, P, P, P, P, i, P, P, P]
         lib.orc_dispatch.argtypes = [i, i, i, P, P, P, P, P]
         lib.orc_expert_rows.argtypes = [i, i, i, P, P, P, P, i, P, P, i, P]
         lib.orc_combine.argtypes = [i, i, i, P, P, P]
@@ -61,7 +64,8 @@ def _load():
                   lib.orc_combine, lib.orc_combine_kept, lib.orc_capacity,
                   lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens,
                   lib.orc_route_sel, lib.orc_noisy_logits, lib.orc_z_loss,
-                  lib.orc_route_dynamic):
+                  lib.orc_route_dynamic, lib.orc_dequant_w4, lib.orc_expert_rows_w4,
+                  lib.orc_expert_rows_f64w):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -297,3 +301,63 @@ def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_b
     y = expert_rows(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tok, ex, round_h=round_h)
     out = combine(w, y, keep)
     return {"logits": lg, "idx": idx, "w": w, "out": out, "kt": kt}
+
+
+def dequant_w4(codes: np.ndarray, sb: np.ndarray) -> np.ndarray:
+    """codes uint8 [E,N,K/2], sb uint16 (bf16 bits) [E,N,K/128,2] -> float64 [E,N,K]."""
+    codes = _c(codes, np.uint8)
+    sb = _c(sb, np.uint16)
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    assert sb.shape == (E, N, K // 128, 2)
+    w = np.empty((E, N, K), np.float64)
+    _check(_load().orc_dequant_w4(E, N, K, _p(codes), _p(sb), _p(w)), "dequant_w4")
+    return w
+
+
+def expert_rows_w4(x, w4: dict, tok, ex, round_h: bool = False) -> np.ndarray:
+    """SwiGLU expert output (float64 [n,H]) with 4-bit weights w4 = dict of
+    gate/up/down codes and gate_sb/up_sb/down_sb."""
+    x = _c(x)
+    tok, ex = _c(tok, np.int32), _c(ex, np.int32)
+    H = x.shape[1]
+    E, I, _ = w4["gate"].shape
+    arrs = [_c(w4[n], np.uint8 if "sb" not in n else np.uint16)
+            for n in ("gate", "gate_sb", "up", "up_sb", "down", "down_sb")]
+    n = tok.shape[0]
+    y = np.empty((n, H), np.float64)
+    _check(_load().orc_expert_rows_w4(H, I, _dtype_code(x), _p(x), *(_p(a) for a in arrs), n,
+                                      _p(tok), _p(ex), int(round_h), _p(y)), "expert_rows_w4")
+    return y
+
+
+def expert_rows_f64w(x, wg, wu, wd, tok, ex) -> np.ndarray:
+    """SwiGLU expert output with float64 weight arrays (dequantised-first check)."""
+    x = _c(x)
+    wg, wu, wd = (_c(a, np.float64) for a in (wg, wu, wd))
+    tok, ex = _c(tok, np.int32), _c(ex, np.int32)
+    H = x.shape[1]
+    I = wg.shape[1]
+    n = tok.shape[0]
+    y = np.empty((n, H), np.float64)
+    _check(_load().orc_expert_rows_f64w(H, I, _dtype_code(x), _p(x), _p(wg), _p(wu), _p(wd), n,
+                                        _p(tok), _p(ex), _p(y)), "expert_rows_f64w")
+    return y
+
+
+def forward_w4(inp: dict, w4: dict, cfg, tokens=None, round_h: bool = False, keep=None):
+    """Block forward of the listed tokens with 4-bit expert weights (router as
+    forward_variant, experts dequantised element by element)."""
+    x = _c(inp["x"])
+    T = x.shape[0]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = _c(tokens, np.int32)
+    xs = np.ascontiguousarray(x[tokens])
+    lg = logits(xs, inp["w_router"], inp.get("logit_bias"))
+    idx, w, _ = route(lg, cfg.k, cfg.norm)
+    n = tokens.shape[0]
+    tok = np.repeat(np.arange(n, dtype=np.int32), cfg.k)
+    y = expert_rows_w4(xs, w4, tok, idx.ravel(), round_h=round_h)
+    out = combine(w, y, keep)
+    return {"logits": lg, "idx": idx, "w": w, "out": out}

@@ -16,7 +16,11 @@ reproducible on any machine):
     log(Zipf_s(rank = e + 1)) = -s ln(e+1) - ln(sum_{r=1..E} r^-s);
   * router variants (make_router_variant_inputs): w_noise [E,H] like the
     router (scale 1/sqrt(H), bf16 for bf16 workloads), noise [T,E] float32
-    standard normals, select_bias [E] float32 normals times 0.5.
+    standard normals, select_bias [E] float32 normals times 0.5;
+  * 4-bit expert weights (make_w4_inputs): uniform random code bytes, and per
+    group of 128 a bf16 scale s = |1 + 0.2 n1| / (4.6 sqrt(fan_in)) and bias
+    b = -s (7.5 + 0.5 n2) (n1, n2 standard normals), so that s q + b with q
+    uniform in 0..15 has mean ~0 and standard deviation ~1/sqrt(fan_in).
 """
 from __future__ import annotations
 
@@ -30,7 +34,8 @@ from .configs import MoEConfig
 
 CHUNK = 1 << 22
 TENSOR_IDS = {"x": 0, "w_router": 1, "w_gate": 2, "w_up": 3, "w_down": 4, "w_noise": 5,
-              "noise": 6, "select_bias": 7}
+              "noise": 6, "select_bias": 7, "gate_q": 8, "up_q": 9, "down_q": 10, "gate_s": 11,
+              "up_s": 12, "down_s": 13, "gate_b": 14, "up_b": 15, "down_b": 16}
 
 
 def _workers() -> int:
@@ -125,3 +130,43 @@ def make_router_variant_inputs(cfg: MoEConfig, seed: int | None = None,
         "noise": normal_tensor((T, E), seed, TENSOR_IDS["noise"], 1.0, False),
         "select_bias": normal_tensor((E,), seed, TENSOR_IDS["select_bias"], 0.5, False),
     }
+
+
+def uniform_bytes(shape, seed: int, tensor_id: int) -> np.ndarray:
+    """Chunked Philox uniform bytes (0..255), the same chunk seeding as
+    normal_tensor."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint8)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def fill(c: int):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        ss = np.random.SeedSequence(seed, spawn_key=(tensor_id, c))
+        out[lo:hi] = np.random.Generator(np.random.Philox(ss)).integers(0, 256, hi - lo,
+                                                                        dtype=np.uint8)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def make_w4_inputs(cfg: MoEConfig, seed: int | None = None) -> dict:
+    """4-bit expert weights: gate/up codes uint8 [E,I,H/2], down [E,H,I/2]
+    (element 2i in the low nibble of byte i), and *_sb uint16 bf16 bits
+    [E,N,K/128,2] = (scale, bias) per group of 128 consecutive K."""
+    seed = cfg.seed if seed is None else seed
+    H, E, I = cfg.H, cfg.E, cfg.I
+    d = {}
+    for name, N, K in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        d[name] = uniform_bytes((E, N, K // 2), seed, TENSOR_IDS[name + "_q"])
+        G = K // 128
+        n1 = normal_tensor((E, N, G), seed, TENSOR_IDS[name + "_s"], 1.0, False)
+        n2 = normal_tensor((E, N, G), seed, TENSOR_IDS[name + "_b"], 1.0, False)
+        scale = (np.abs(1.0 + 0.2 * n1) / (4.6 * math.sqrt(K))).astype(np.float32)
+        bias = (-scale * (7.5 + 0.5 * n2)).astype(np.float32)
+        d[name + "_sb"] = np.stack([bf16_bits(scale), bf16_bits(bias)], axis=-1)
+    return d

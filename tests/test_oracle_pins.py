@@ -386,6 +386,50 @@ def test_forward_keep_mask(orc):
                                    atol=1e-12)
 
 
+# ------------------------------------------------------------- 4-bit weights
+
+
+def test_w4_dequant_matches_numpy_unpacking(orc):
+    from sparse_mixture_experts_40_amd.inputs import make_w4_inputs
+    cfg = MoEConfig("w4", T=4, H=256, E=3, k=1, I=384, norm=True, dtype="bf16")
+    w4 = make_w4_inputs(cfg, seed=2)
+    for name, N, K in (("gate", cfg.I, cfg.H), ("down", cfg.H, cfg.I)):
+        codes, sb = w4[name], w4[name + "_sb"]
+        q = np.empty(codes.shape[:2] + (K,), np.float64)
+        q[..., 0::2] = codes & 0x0F  # element 2i: low nibble of byte i
+        q[..., 1::2] = codes >> 4
+        sbf = as_f32(sb).astype(np.float64)
+        scale = np.repeat(sbf[..., 0], 128, axis=-1)
+        bias = np.repeat(sbf[..., 1], 128, axis=-1)
+        np.testing.assert_allclose(orc.dequant_w4(codes, sb), scale * q + bias, rtol=1e-15,
+                                   atol=1e-18)
+    # hand-made group: byte 0x21 is (1, 2), 0xF0 is (0, 15); scale 1, bias -0.5
+    codes = np.zeros((1, 1, 64), np.uint8)
+    codes[0, 0, 0], codes[0, 0, 1] = 0x21, 0xF0
+    sb = np.zeros((1, 1, 1, 2), np.uint16)
+    sb[..., 0], sb[..., 1] = 0x3F80, 0xBF00  # bf16 1.0 and -0.5
+    w = orc.dequant_w4(codes, sb)
+    assert w[0, 0, :4].tolist() == [0.5, 1.5, -0.5, 14.5]
+    assert (w[0, 0, 4:] == -0.5).all()
+
+
+def test_w4_expert_rows_equal_dequantise_first(orc):
+    from sparse_mixture_experts_40_amd.inputs import make_w4_inputs
+    cfg = MoEConfig("w4", T=6, H=256, E=4, k=2, I=128, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=3, weights=False)
+    w4 = make_w4_inputs(cfg, seed=3)
+    tok = np.array([0, 1, 2, 3, 4, 5, 5, 0], np.int32)
+    ex = np.array([0, 1, 2, 3, 3, 2, 0, 1], np.int32)
+    y = orc.expert_rows_w4(inp["x"], w4, tok, ex)
+    wg, wu, wd = (orc.dequant_w4(w4[n], w4[n + "_sb"]) for n in ("gate", "up", "down"))
+    y2 = orc.expert_rows_f64w(inp["x"], wg, wu, wd, tok, ex)
+    np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-14)
+    x = as_f32(inp["x"]).astype(np.float64)
+    for r in range(len(tok)):
+        ref = _swiglu_np(x[tok[r]:tok[r] + 1], wg[ex[r]], wu[ex[r]], wd[ex[r]])[0]
+        np.testing.assert_allclose(y2[r], ref, rtol=1e-11, atol=1e-13)
+
+
 # --------------------------------------------------------------------- expert
 
 
