@@ -137,6 +137,26 @@ typedef struct {
   int32_t* k_per_token; /* [T] int32 out or NULL: k_t of every token */
 } moe_options;
 
+/* 4-bit group-quantised expert weights, [MOE-128x8] 参数量化与存储优化 (4-bit
+ * codes, group_size 128, an independent scale and bias per group; ~75% less
+ * memory than 16-bit weights). For a matrix [E, N, K] (gate/up: N = I, K = H;
+ * down: N = H, K = I):
+ *   codes [E, N, K/2] uint8: element k of row (e, n) is the low nibble of byte
+ *         (e*N + n)*K/2 + k/2 for even k and its high nibble for odd k;
+ *   sb    [E, N, K/128, 2] bf16: (scale, bias) of the group of 128 consecutive
+ *         k starting at 128 g;
+ *   w[e,n,k] = scale * q + bias.
+ * Device pointers, 16-byte aligned. Used by the *_w4 entry points, which need
+ * dtype bf16 and H, I multiples of 512 (MOE_ERR_UNSUPPORTED otherwise). */
+typedef struct {
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const void* gate_sb;
+  const void* up_sb;
+  const void* down_sb;
+} moe_w4_weights;
+
 /* Bytes of workspace every entry point below needs for `cfg` (the maximum
  * over all of them). Host-only and pure; returns 0 if `cfg` is invalid. */
 size_t moe_workspace_size(const moe_config* cfg);
@@ -244,6 +264,18 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* 
                            const void* w_down, void* y_sorted, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* moe_expert_gate_up / moe_expert_down with 4-bit weights (moe_w4_weights).
+ * The kernels stream the codes of the experts that have rows and dequantise
+ * them in registers (fp32 scale * q + bias, rounded once to bf16 as the MFMA
+ * operand); they are built for few rows per expert (decode batches) and are
+ * correct for any number of rows. */
+moe_status moe_expert_gate_up_w4(const moe_config* cfg, const void* x,
+                                 const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                 const moe_w4_weights* w, void* h, hipStream_t stream);
+moe_status moe_expert_down_w4(const moe_config* cfg, const void* h,
+                              const int32_t* expert_offsets, const moe_w4_weights* w,
+                              void* y_sorted, hipStream_t stream);
+
 /* Both halves: y_sorted[i] = W_down[e] (silu(W_gate[e] x_t) * W_up[e] x_t),
  * the unweighted output of expert e for the token of sorted row i. The
  * intermediate h lives in `workspace`. */
@@ -292,6 +324,14 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
                                 void* out, float* router_logits, int32_t* topk_idx,
                                 float* topk_w, moe_aux_out aux, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* moe_layer_forward_ex with 4-bit expert weights (moe_w4_weights); the
+ * router matrix stays in dtype. */
+moe_status moe_layer_forward_w4(const moe_config* cfg, const moe_options* opt, const void* x,
+                                const void* w_router, const float* logit_bias,
+                                const moe_w4_weights* w, void* out, float* router_logits,
+                                int32_t* topk_idx, float* topk_w, moe_aux_out aux,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

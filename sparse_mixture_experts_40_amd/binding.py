@@ -25,7 +25,8 @@ EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_ro
            "moe_dispatch",
            "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_layer_forward",
-           "moe_layer_forward_ex")
+           "moe_layer_forward_ex", "moe_expert_gate_up_w4", "moe_expert_down_w4",
+           "moe_layer_forward_w4")
 
 
 class moe_config(ctypes.Structure):
@@ -40,6 +41,12 @@ class moe_options(ctypes.Structure):
                 ("noise", ctypes.c_void_p), ("w_noise", ctypes.c_void_p),
                 ("select_bias", ctypes.c_void_p), ("dynamic_k_min", ctypes.c_int32),
                 ("k_per_token", ctypes.c_void_p)]
+
+
+class moe_w4_weights(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_sb", ctypes.c_void_p), ("up_sb", ctypes.c_void_p),
+                ("down_sb", ctypes.c_void_p)]
 
 
 class moe_aux_out(ctypes.Structure):
@@ -77,6 +84,11 @@ def load(path: str = LIB_PATH):
         "moe_layer_forward": [C, V, V, V, V, V, V, V, V, V, V, moe_aux_out, V, S, V],
         "moe_layer_forward_ex": [C, ctypes.POINTER(moe_options), V, V, V, V, V, V, V, V, V, V,
                                  moe_aux_out, V, S, V],
+        "moe_expert_gate_up_w4": [C, V, V, V, ctypes.POINTER(moe_w4_weights), V, V],
+        "moe_expert_down_w4": [C, V, V, ctypes.POINTER(moe_w4_weights), V, V],
+        "moe_layer_forward_w4": [C, ctypes.POINTER(moe_options), V, V, V,
+                                 ctypes.POINTER(moe_w4_weights), V, V, V, V, moe_aux_out, V, S,
+                                 V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -224,6 +236,48 @@ def layer_forward_ex(c: moe_config, opts: moe_options | None, x, w_router, logit
            "moe_layer_forward_ex")
 
 
+def w4_weights(t: dict) -> moe_w4_weights:
+    """moe_w4_weights from a dict of device tensors gate/up/down (uint8 codes)
+    and gate_sb/up_sb/down_sb (bf16 (scale, bias) pairs)."""
+    return moe_w4_weights(*(_ptr(t[n]) for n in ("gate", "up", "down", "gate_sb", "up_sb",
+                                                  "down_sb")))
+
+
+def w4_to_device(w4: dict, device="cuda") -> dict:
+    """numpy 4-bit weights (make_w4_inputs layout) -> device tensors."""
+    import numpy as np
+    out = {}
+    for n, a in w4.items():
+        if a.dtype == np.uint16:
+            out[n] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(device)
+        else:
+            out[n] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return out
+
+
+def expert_gate_up_w4(c: moe_config, x, sorted_pair, offsets, w4: moe_w4_weights, h):
+    _check(load().moe_expert_gate_up_w4(ctypes.byref(c), _ptr(x), _ptr(sorted_pair),
+                                        _ptr(offsets), ctypes.byref(w4), _ptr(h), _stream()),
+           "moe_expert_gate_up_w4")
+
+
+def expert_down_w4(c: moe_config, h, offsets, w4: moe_w4_weights, y_sorted):
+    _check(load().moe_expert_down_w4(ctypes.byref(c), _ptr(h), _ptr(offsets), ctypes.byref(w4),
+                                     _ptr(y_sorted), _stream()), "moe_expert_down_w4")
+
+
+def layer_forward_w4(c: moe_config, opts: moe_options | None, x, w_router, logit_bias,
+                     w4: moe_w4_weights, out, ws, router_logits=None, topk_idx=None, topk_w=None,
+                     counts=None, f=None, P=None, aux=None, z_loss=None):
+    _check(load().moe_layer_forward_w4(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
+                                       _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(w4),
+                                       _ptr(out), _ptr(router_logits), _ptr(topk_idx),
+                                       _ptr(topk_w), _aux(counts, f, P, aux, z_loss), _ptr(ws),
+                                       ws.numel(), _stream()),
+           "moe_layer_forward_w4")
+
+
 def to_device(a, device="cuda") -> torch.Tensor:
     """numpy input array (float32, or uint16 bf16 bits) -> GPU tensor of the
     matching torch dtype (bf16 bits are reinterpreted, not converted)."""
@@ -246,11 +300,12 @@ class MoEBlock:
     whole forward with one library call per step."""
 
     def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0,
-                 noise=None, w_noise=None, select_bias=None, dynamic_k_min: int = 0):
+                 noise=None, w_noise=None, select_bias=None, dynamic_k_min: int = 0, w4=None):
         """capacity > 0: capacity-limited dispatch (see moe_capacity); noise
         [T,E] fp32 + w_noise [E,H]: noisy top-k; select_bias [E] fp32:
         selection-only bias (numpy arrays or tensors); dynamic_k_min > 0:
-        entropy-driven k in [dynamic_k_min, k]."""
+        entropy-driven k in [dynamic_k_min, k]; w4: 4-bit expert weights
+        (make_w4_inputs layout) used instead of inputs' w_gate/w_up/w_down."""
         self.cfg = cfg
         self.c = make_config(cfg)
         self.dropped = torch.zeros(1, dtype=torch.int32, device=device)
@@ -262,9 +317,12 @@ class MoEBlock:
         self.opts = options(capacity, self.dropped, self.noise, self.w_noise, self.select_bias,
                             dynamic_k_min, self.k_per_token) if variant else None
         self.w_router = to_device(inputs["w_router"], device)
-        self.w_gate = to_device(inputs["w_gate"], device)
-        self.w_up = to_device(inputs["w_up"], device)
-        self.w_down = to_device(inputs["w_down"], device)
+        self.w4 = w4_to_device(w4, device) if w4 is not None else None
+        self.w4_struct = w4_weights(self.w4) if w4 is not None else None
+        if w4 is None:
+            self.w_gate = to_device(inputs["w_gate"], device)
+            self.w_up = to_device(inputs["w_up"], device)
+            self.w_down = to_device(inputs["w_down"], device)
         self.logit_bias = to_device(inputs.get("logit_bias"), device)
         self.ws = alloc_workspace(self.c, device)
         T, E, k = cfg.T, cfg.E, cfg.k
@@ -281,7 +339,12 @@ class MoEBlock:
     def forward(self, x: torch.Tensor, outputs: bool = True):
         """outputs=False: only `out` (logits, selection and statistics stay in
         the workspace / are not computed)."""
-        if outputs:
+        if self.w4 is not None:
+            extra = (self.logits, self.topk_idx, self.topk_w, self.counts, self.f, self.P,
+                     self.aux, self.z_loss) if outputs else ()
+            layer_forward_w4(self.c, self.opts, x, self.w_router, self.logit_bias,
+                             self.w4_struct, self.out, self.ws, *extra)
+        elif outputs:
             layer_forward_ex(self.c, self.opts, x, self.w_router, self.logit_bias, self.w_gate,
                              self.w_up, self.w_down, self.out, self.ws, self.logits,
                              self.topk_idx, self.topk_w, self.counts, self.f, self.P, self.aux,

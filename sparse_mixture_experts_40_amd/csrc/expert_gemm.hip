@@ -581,6 +581,62 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* const (&wrow)[
   }
 }
 
+// Split-K reduction over the 4 waves in fixed order (waves 0..3), then the
+// epilogue of one pass: gate/up blocks (nb 0 = gate, 1 = up) -> h = silu(g) u
+// in bf16; down blocks -> y_sorted in fp32. Rows p0.. of the pass, r1 = end
+// of the expert's rows; the accumulators hold D[n][m] (n weight row, m token).
+template <bool GATEUP, int NB>
+__device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2],
+                                             float (*s_part)[NB][2][16][64], int p0, int r1,
+                                             int ntb, int c, int N_out, void* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
+  __syncthreads();
+  {
+    const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, lane, half of r)
+    const int row = p0 + tb * 32 + (lane & 31);
+    if (tb < ntb && row < r1) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = half * 2 + qq;  // group of 4 consecutive columns
+        float v[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = q * 4 + j;
+            v[nb][j] = ((s_part[0][nb][tb][r][lane] + s_part[1][nb][tb][r][lane]) +
+                        s_part[2][nb][tb][r][lane]) + s_part[3][nb][tb][r][lane];
+          }
+        const int n_in = q * 8 + (lane >> 5) * 4;  // column inside a 32-wide block
+        if (GATEUP) {
+          const int col = c * 32 + n_in;
+          if (col < N_out) {
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hv[j] = silu(v[0][j]) * v[1][j];
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)row * N_out + col) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int col = c * 64 + nb * 32 + n_in;
+            if (col < N_out)
+              *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)row * N_out + col) =
+                  make_float4(v[nb][0], v[nb][1], v[nb][2], v[nb][3]);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
@@ -646,52 +702,239 @@ __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
         dec_kloop<NB, 2>(ng, wrow, trow, acc);
       else
         dec_kloop<NB, 1>(ng, wrow, trow, acc);
-      // split-K reduction over the 4 waves in fixed order, then the epilogue
+      dec_epilogue<GATEUP, NB>(acc, s_part, p0, r1, ntb, c, N_out, out);
+      __syncthreads();  // s_part is reused by the next pass / item
+    }
+  }
+}
+
+// ---- 4-bit weights, weight-streaming path --------------------------------
+//
+// [MOE-128x8] 参数量化与存储优化: 4-bit codes in groups of 128 along K with an
+// independent scale and bias per group, w = scale * q + bias. Work items,
+// token passes and the 4-way split-K are those of decode_gemm_bf16_kernel.
+// No weight is rounded: the MFMA multiplies the exact bf16 values 128 + q
+// (built from the codes with one byte permute and one OR per pair) with the
+// tokens, a second MFMA against ones gives the group's token sums, and each
+// group of 128 is folded into the fp32 accumulators as
+//   sum_k w x = scale * sum_k (128 + q) x + (bias - 128 scale) * sum_k x.
+// The tokens are the A operand and the weights the B operand, so a lane's
+// accumulators belong to one weight row (lane & 31) and one (scale, bias)
+// per group. K is taken in chunks of 64: lane half h covers elements
+// [32h, 32h + 32) of a chunk, i.e. 16 bytes of codes (one load), in 4 MFMA k
+// steps of 8; the token fragments are read in the same order.
+
+// 8 codes (element 2i in the low nibble of byte i) -> the bf16 values 128 + q.
+__device__ __forceinline__ bf16x8_t w4_unpack8(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  // dword j = elements (2j, 2j+1): bytes (lo.j, 0, hi.j, 0) | 0x43004300
+  const uint4 r = make_uint4(__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
+                             __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
+                             __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
+                             __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Loads of chunk ch: the codes of NB weight rows and the token fragments of
+// its 4 k steps.
+template <int NB, int NTB>
+__device__ __forceinline__ void w4_load(int ch, const uint8_t* const (&qrow)[NB],
+                                        const uint16_t* const (&trow)[2], uint4 (&cw)[NB],
+                                        bf16x8_t (&tf)[4][2]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) cw[nb] = *reinterpret_cast<const uint4*>(qrow[nb] + ch * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+      tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(trow[tb] + ch * 64 + j * 8);
+}
+
+// The 4 k steps of one chunk into the group accumulators: aq += tokens x
+// (128 + q), ax += tokens x 1.
+template <int NB, int NTB>
+__device__ __forceinline__ void w4_chunk(const uint4 (&cw)[NB], const bf16x8_t (&tf)[4][2],
+                                         f32x16_t (&aq)[NB][2], f32x16_t (&ax)[2]) {
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                0x3F803F80u, 0x3F803F80u));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t w = j == 0 ? cw[nb].x : j == 1 ? cw[nb].y : j == 2 ? cw[nb].z : cw[nb].w;
+      const bf16x8_t wq = w4_unpack8(w);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        aq[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], wq, aq[nb][tb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+      ax[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], ones, ax[tb], 0, 0, 0);
+  }
+}
+
+// This wave's groups of 128 (two chunks each), loads one chunk ahead.
+template <int NB, int NTB>
+__device__ __forceinline__ void w4_kloop(int ngroups, const uint8_t* const (&qrow)[NB],
+                                         const uint32_t* const (&sbrow)[NB],
+                                         const uint16_t* const (&trow)[2],
+                                         f32x16_t (&acc)[NB][2]) {
+  uint4 ca[NB], cb[NB];
+  bf16x8_t ta[4][2], tb_[4][2];
+  w4_load<NB, NTB>(0, qrow, trow, ca, ta);
+  for (int g = 0; g < ngroups; ++g) {
+    uint32_t sbw[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sbw[nb] = sbrow[nb][g];  // (scale, bias) bf16 pair
+    f32x16_t aq[NB][2], ax[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ax[tb][r] = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) aq[nb][tb][r] = 0.0f;
+    }
+    w4_load<NB, NTB>(2 * g + 1, qrow, trow, cb, tb_);
+    w4_chunk<NB, NTB>(ca, ta, aq, ax);
+    if (g + 1 < ngroups) w4_load<NB, NTB>(2 * g + 2, qrow, trow, ca, ta);
+    w4_chunk<NB, NTB>(cb, tb_, aq, ax);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float scale = __uint_as_float(sbw[nb] << 16);
+      const float bias2 = fmaf(-128.0f, scale, __uint_as_float(sbw[nb] & 0xFFFF0000u));
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[nb][tb][r] = fmaf(scale, aq[nb][tb][r], fmaf(bias2, ax[tb][r], acc[nb][tb][r]));
+    }
+  }
+}
+
+// Split-K reduction and epilogue for accumulators in the tokens-x-weights
+// orientation: (r, lane) of block (nb, tb) holds token row
+// (r / 4) * 8 + (lane / 32) * 4 + r % 4 and weight row lane & 31.
+template <bool GATEUP, int NB>
+__device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][2],
+                                            float (*s_part)[NB][2][16][64], int p0, int r1,
+                                            int ntb, int c, int N_out, void* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
+  __syncthreads();
+  {
+    const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, token m, half of columns)
+    const int m = lane & 31, row = p0 + tb * 32 + m;
+    const int r_m = (m >> 3) * 4 + (m & 3), l_m = ((m >> 2) & 1) * 32;  // where token m sits
+    if (tb < ntb && row < r1) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int n_in = (lane >> 5) * 16 + half * 8 + qq * 2;  // 2 columns of a 32-block
+        float v[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int ln = l_m + n_in + j;
+            v[nb][j] = ((s_part[0][nb][tb][r_m][ln] + s_part[1][nb][tb][r_m][ln]) +
+                        s_part[2][nb][tb][r_m][ln]) + s_part[3][nb][tb][r_m][ln];
+          }
+        if (GATEUP) {
+          const int col = c * 32 + n_in;
+          if (col < N_out)
+            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (size_t)row * N_out + col) =
+                pack_bf16x2(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1]);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int col = c * 64 + nb * 32 + n_in;
+            if (col < N_out)
+              *reinterpret_cast<float2*>(static_cast<float*>(out) + (size_t)row * N_out + col) =
+                  make_float2(v[nb][0], v[nb][1]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// K (= H for gate/up, I for down) is a multiple of 512, so each wave's quarter
+// is a whole number of 128-groups.
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 1) void decode_w4_kernel(
+    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ q0, const uint16_t* __restrict__ sb0,
+    const uint8_t* __restrict__ q1, const uint16_t* __restrict__ sb1, void* __restrict__ out,
+    int n_chunks) {
+  constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
+  __shared__ int s_scan[2 * 256 + 2];
+  __shared__ __align__(16) float s_part[4][NB][2][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  __syncthreads();
+  if (tid < E) s_scan[tid] = (s_scan[E + 2 + tid] > s_scan[E + 1 + tid]) ? 1 : 0;
+  __syncthreads();
+  for (int d = 1; d < E; d <<= 1) {
+    const int add = (tid < E && tid >= d) ? s_scan[tid - d] : 0;
+    __syncthreads();
+    if (tid < E) s_scan[tid] += add;
+    __syncthreads();
+  }
+  const int items = s_scan[E - 1] * n_chunks;
+  const int kw = K / 4;  // this wave's K range [wave*kw, wave*kw + kw)
+  const int ngroups = kw / 128;
+  const int G = K / 128;
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int rank = it / n_chunks, c = it - rank * n_chunks;
+    int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
+    }
+    const int e = lo;
+    const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
+    const uint8_t* qrow[NB];
+    const uint32_t* sbrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int n = GATEUP ? c * 32 + (lane & 31) : c * 64 + nb * 32 + (lane & 31);
+      n = n < N_out ? n : N_out - 1;
+      const uint8_t* qm = (GATEUP && nb == 1) ? q1 : q0;
+      const uint16_t* sm = (GATEUP && nb == 1) ? sb1 : sb0;
+      const size_t row = (size_t)e * N_out + n;
+      qrow[nb] = qm + row * (K / 2) + (wave * kw) / 2 + (lane >> 5) * 16;
+      sbrow[nb] = reinterpret_cast<const uint32_t*>(sm + (row * G + (wave * kw) / 128) * 2);
+    }
+    for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
+      const uint16_t* trow[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        int gi = p0 + tb * 32 + (lane & 31);
+        gi = gi < r1 ? gi : r1 - 1;
+        const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
+        trow[tb] = act + (size_t)arow * K + wave * kw + (lane >> 5) * 32;
+      }
+      const int ntb = (r1 - p0) > 32 ? 2 : 1;
+      f32x16_t acc[NB][2];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
-      __syncthreads();
-      {
-        const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, lane, half of r)
-        const int row = p0 + tb * 32 + (lane & 31);
-        if (tb < ntb && row < r1) {
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            const int q = half * 2 + qq;  // group of 4 consecutive columns
-            float v[NB][4];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int r = q * 4 + j;
-                v[nb][j] = ((s_part[0][nb][tb][r][lane] + s_part[1][nb][tb][r][lane]) +
-                            s_part[2][nb][tb][r][lane]) + s_part[3][nb][tb][r][lane];
-              }
-            const int n_in = q * 8 + (lane >> 5) * 4;  // column inside a 32-wide block
-            if (GATEUP) {
-              const int col = c * 32 + n_in;
-              if (col < N_out) {
-                float hv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) hv[j] = silu(v[0][j]) * v[1][j];
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)row * N_out + col) =
-                    make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-              }
-            } else {
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb) {
-                const int col = c * 64 + nb * 32 + n_in;
-                if (col < N_out)
-                  *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)row * N_out + col) =
-                      make_float4(v[nb][0], v[nb][1], v[nb][2], v[nb][3]);
-              }
-            }
-          }
-        }
-      }
+          for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
+      if (ntb > 1)
+        w4_kloop<NB, 2>(ngroups, qrow, sbrow, trow, acc);
+      else
+        w4_kloop<NB, 1>(ngroups, qrow, sbrow, trow, acc);
+      w4_epilogue<GATEUP, NB>(acc, s_part, p0, r1, ntb, c, N_out, out);
       __syncthreads();  // s_part is reused by the next pass / item
     }
   }
@@ -823,6 +1066,31 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
       <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
       c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h), nullptr,
       offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn);
+  return hipGetLastError();
+}
+
+bool w4_supported(const moe_config& c) {
+  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0 && c.intermediate % 512 == 0;
+}
+
+hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* sorted_pair,
+                             const int32_t* offsets, const moe_w4_weights& w, void* h,
+                             hipStream_t s) {
+  const int nch = (c.intermediate + 31) / 32;
+  decode_w4_kernel<true><<<persistent_grid(), 256, 0, s>>>(
+      c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
+      sorted_pair, offsets, w.gate, static_cast<const uint16_t*>(w.gate_sb), w.up,
+      static_cast<const uint16_t*>(w.up_sb), h, nch);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_w4(const moe_config& c, const void* h, const int32_t* offsets,
+                          const moe_w4_weights& w, void* y, hipStream_t s) {
+  const int nch = (c.hidden + 63) / 64;
+  decode_w4_kernel<false><<<persistent_grid(), 256, 0, s>>>(
+      c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
+      nullptr, offsets, w.down, static_cast<const uint16_t*>(w.down_sb), nullptr, nullptr, y,
+      nch);
   return hipGetLastError();
 }
 

@@ -115,6 +115,84 @@ size_t swiglu_bytes(const moe_config& c) {
   return cv.off;
 }
 
+// 4-bit weight arguments: all six arrays, bf16 activations, H and I
+// multiples of 512.
+moe_status check_w4(const moe_config& c, const moe_w4_weights* w) {
+  if (!w || !w->gate || !w->up || !w->down || !w->gate_sb || !w->up_sb || !w->down_sb)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return w4_supported(c) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+// The block forward with either dtype expert weights (w_gate/w_up/w_down) or
+// 4-bit ones (w4 != nullptr). Arguments are checked by the callers.
+moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, const void* x,
+                              const void* w_router, const float* logit_bias, const void* w_gate,
+                              const void* w_up, const void* w_down, const moe_w4_weights* w4,
+                              void* out, float* router_logits, int32_t* topk_idx, float* topk_w,
+                              moe_aux_out aux, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  moe_status st = MOE_OK;
+  const moe_options none{};
+  const moe_options& o = opt ? *opt : none;
+  if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  st = check_router_options(*cfg, o);
+  if (st != MOE_OK) return st;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_config& c = *cfg;
+  int32_t* idx = topk_idx ? topk_idx : L.idx;
+  float* w = topk_w ? topk_w : L.w;
+  const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
+  float* partials = want_aux ? L.partials : nullptr;
+  RouterExtras ex;
+  ex.sel_bias = o.select_bias;
+  ex.zpart = aux.z_loss ? L.zpart : nullptr;
+  ex.k_min = o.dynamic_k_min;
+  ex.kt_out = o.k_per_token;
+
+  int router_blocks;
+  if (o.noise) {  // clean logits, noise logits, then the noisy top-k from them
+    st = launched(launch_logits(c, x, w_router, logit_bias, L.rlogits, stream));
+    if (st != MOE_OK) return st;
+    st = launched(launch_logits(c, x, o.w_noise, nullptr, L.nlogits, stream));
+    if (st != MOE_OK) return st;
+    ex.noise = o.noise;
+    ex.nlogits = L.nlogits;
+    ex.logits_final = router_logits;
+    st = launched(launch_router(c, nullptr, nullptr, nullptr, L.rlogits, false, idx, w, partials,
+                                true, stream, ex));
+    router_blocks = router_num_blocks(c, true);
+  } else if (router_k_splits(c) > 1) {
+    st = launched(launch_router_split(c, x, w_router, logit_bias, L.rlogits, router_logits,
+                                      L.rpart, idx, w, partials, stream, ex));
+    router_blocks = router_num_blocks(c, true);
+  } else {
+    st = launched(launch_router(c, x, w_router, logit_bias, router_logits,
+                                router_logits != nullptr, idx, w, partials, true, stream, ex));
+    router_blocks = router_num_blocks(c, false);
+  }
+  if (st != MOE_OK) return st;
+  st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
+                                L.base, true, o.capacity, o.dropped, stream));
+  if (st != MOE_OK) return st;
+  if (w4) {
+    st = launched(launch_gate_up_w4(c, x, L.sorted_pair, L.offsets, *w4, L.h, stream));
+    if (st != MOE_OK) return st;
+    st = launched(launch_down_w4(c, L.h, L.offsets, *w4, L.y, stream));
+  } else {
+    st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
+    if (st != MOE_OK) return st;
+    st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream));
+  }
+  if (st != MOE_OK) return st;
+  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
+  if (st != MOE_OK) return st;
+  if (want_aux || aux.z_loss)
+    st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, aux, stream, ex.zpart,
+                             router_blocks));
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,59 +375,46 @@ moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, c
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
-  const moe_options none{};
-  const moe_options& o = opt ? *opt : none;
-  if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
-  st = check_router_options(*cfg, o);
-  if (st != MOE_OK) return st;
-  const Layout L = carve(*cfg, workspace);
-  if (!workspace || workspace_bytes < L.layer_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const moe_config& c = *cfg;
-  int32_t* idx = topk_idx ? topk_idx : L.idx;
-  float* w = topk_w ? topk_w : L.w;
-  const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
-  float* partials = want_aux ? L.partials : nullptr;
-  RouterExtras ex;
-  ex.sel_bias = o.select_bias;
-  ex.zpart = aux.z_loss ? L.zpart : nullptr;
-  ex.k_min = o.dynamic_k_min;
-  ex.kt_out = o.k_per_token;
+  return layer_forward_impl(cfg, opt, x, w_router, logit_bias, w_gate, w_up, w_down, nullptr,
+                            out, router_logits, topk_idx, topk_w, aux, workspace,
+                            workspace_bytes, stream);
+}
 
-  int router_blocks;
-  if (o.noise) {  // clean logits, noise logits, then the noisy top-k from them
-    st = launched(launch_logits(c, x, w_router, logit_bias, L.rlogits, stream));
-    if (st != MOE_OK) return st;
-    st = launched(launch_logits(c, x, o.w_noise, nullptr, L.nlogits, stream));
-    if (st != MOE_OK) return st;
-    ex.noise = o.noise;
-    ex.nlogits = L.nlogits;
-    ex.logits_final = router_logits;
-    st = launched(launch_router(c, nullptr, nullptr, nullptr, L.rlogits, false, idx, w, partials,
-                                true, stream, ex));
-    router_blocks = router_num_blocks(c, true);
-  } else if (router_k_splits(c) > 1) {
-    st = launched(launch_router_split(c, x, w_router, logit_bias, L.rlogits, router_logits,
-                                      L.rpart, idx, w, partials, stream, ex));
-    router_blocks = router_num_blocks(c, true);
-  } else {
-    st = launched(launch_router(c, x, w_router, logit_bias, router_logits,
-                                router_logits != nullptr, idx, w, partials, true, stream, ex));
-    router_blocks = router_num_blocks(c, false);
-  }
+moe_status moe_layer_forward_w4(const moe_config* cfg, const moe_options* opt, const void* x,
+                                const void* w_router, const float* logit_bias,
+                                const moe_w4_weights* w, void* out, float* router_logits,
+                                int32_t* topk_idx, float* topk_w, moe_aux_out aux,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
-                                L.base, true, o.capacity, o.dropped, stream));
+  st = check_w4(*cfg, w);
   if (st != MOE_OK) return st;
-  st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
+  if (!x || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
+  return layer_forward_impl(cfg, opt, x, w_router, logit_bias, nullptr, nullptr, nullptr, w, out,
+                            router_logits, topk_idx, topk_w, aux, workspace, workspace_bytes,
+                            stream);
+}
+
+moe_status moe_expert_gate_up_w4(const moe_config* cfg, const void* x,
+                                 const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                 const moe_w4_weights* w, void* h, hipStream_t stream) {
+  moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream));
+  st = check_w4(*cfg, w);
   if (st != MOE_OK) return st;
-  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
+  if (!x || !sorted_pair || !expert_offsets || !h) return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_gate_up_w4(*cfg, x, sorted_pair, expert_offsets, *w, h, stream));
+}
+
+moe_status moe_expert_down_w4(const moe_config* cfg, const void* h,
+                              const int32_t* expert_offsets, const moe_w4_weights* w,
+                              void* y_sorted, hipStream_t stream) {
+  moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (want_aux || aux.z_loss)
-    st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, aux, stream, ex.zpart,
-                             router_blocks));
-  return st;
+  st = check_w4(*cfg, w);
+  if (st != MOE_OK) return st;
+  if (!h || !expert_offsets || !y_sorted) return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_down_w4(*cfg, h, expert_offsets, *w, y_sorted, stream));
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,

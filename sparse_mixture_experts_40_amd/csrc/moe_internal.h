@@ -126,6 +126,14 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
                           hipStream_t s);
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offsets,
                        const void* w_down, void* y, hipStream_t s);
+// 4-bit weights (weight-streaming kernels): bf16 activations, H and I
+// multiples of 512.
+bool w4_supported(const moe_config& c);
+hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* sorted_pair,
+                             const int32_t* offsets, const moe_w4_weights& w, void* h,
+                             hipStream_t s);
+hipError_t launch_down_w4(const moe_config& c, const void* h, const int32_t* offsets,
+                          const moe_w4_weights& w, void* y, hipStream_t s);
 
 // Combine and statistics.
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,

@@ -108,3 +108,22 @@ def test_capacity_helper_and_validation(lib, orc):
     r = lib.moe_layer_forward_ex(ctypes.byref(c), ctypes.byref(opt), d, d, None, d, d, d, d,
                                  None, None, None, binding.moe_aux_out(), ws, big, None)
     assert r == 1
+
+
+def test_w4_validation(lib):
+    d = ctypes.c_void_p(16)
+    w4 = binding.moe_w4_weights(16, 16, 16, 16, 16, 16)
+    ok = binding.make_config(WORKLOADS["decode128_bf16"])
+    # not a multiple of 512 / not bf16: unsupported before any launch
+    bad_h = binding.moe_config(64, 768, 128, 8, 1536, 1, 1)
+    f32 = binding.make_config(WORKLOADS["tiny_f32"])
+    for c, want in ((bad_h, 2), (f32, 2)):
+        assert lib.moe_expert_gate_up_w4(ctypes.byref(c), d, d, d, ctypes.byref(w4), d, None) == want
+        assert lib.moe_expert_down_w4(ctypes.byref(c), d, d, ctypes.byref(w4), d, None) == want
+    missing = binding.moe_w4_weights(16, 16, None, 16, 16, 16)
+    assert lib.moe_expert_gate_up_w4(ctypes.byref(ok), d, d, d, ctypes.byref(missing), d,
+                                     None) == 1
+    assert lib.moe_expert_gate_up_w4(ctypes.byref(ok), d, d, d, None, d, None) == 1
+    ws = ctypes.c_void_p(256)
+    assert lib.moe_layer_forward_w4(ctypes.byref(ok), None, d, d, None, ctypes.byref(w4), d, None,
+                                    None, None, binding.moe_aux_out(), ws, 16, None) == 3
