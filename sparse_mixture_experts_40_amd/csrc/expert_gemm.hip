@@ -517,67 +517,142 @@ constexpr int kGemmBM = 256, kGemmBK = MOE_GEMM_BK, kGemmStages = MOE_GEMM_BK ==
 // 32 W_gate + 32 W_up rows, down reads 64 W_down rows, each exactly once; the
 // expert's token rows (n_e <= 64 per pass, padded to 32-row MFMA blocks) are
 // read from L2. K is split over the 4 waves (fixed reduction order through
-// LDS, so the result is deterministic). Weights go straight from HBM into
-// MFMA operand registers, two groups of 4 k steps in flight per wave.
+// LDS, so the result is deterministic). Each wave streams its K quarter in
+// groups of 64 elements (128 bytes of every weight and token row) through a
+// ring of LDS buffers of its own: LDS-DMA loads (buffer_load_dwordx4 ... lds)
+// in which 8 consecutive lanes cover one 128-byte line, so one instruction
+// moves 8 whole lines, and the MFMA fragments are then read from LDS. Loading
+// the fragments straight from global memory would give each lane of an
+// instruction its own cache line (32 weight rows per instruction), and the
+// vector L1 serves such an instruction one lane at a time.
 // Experts with no rows own no work items and read no weight bytes.
-constexpr int kDecG = 4;  // k steps (16 wide) per load group
+constexpr int kDecWRows = 64;      // weight rows per work item
+constexpr int kDecRegion = 18432;  // LDS ring of one wave, in bf16 elements (36 KB)
 
-// Loads of one group of kDecG k steps: NB weight fragments and NTB token
-// fragments per step, 16 bytes per lane each.
-template <int NB, int NTB>
-__device__ __forceinline__ void dec_load(int g, const uint16_t* const (&wrow)[NB],
-                                         const uint16_t* const (&trow)[2],
-                                         bf16x8_t (&wf)[kDecG][NB], bf16x8_t (&tf)[kDecG][2]) {
-#pragma unroll
-  for (int s = 0; s < kDecG; ++s) {
-    const int k = (g * kDecG + s) * 16;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wf[s][nb] = *reinterpret_cast<const bf16x8_t*>(wrow[nb] + k);
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) tf[s][tb] = *reinterpret_cast<const bf16x8_t*>(trow[tb] + k);
-  }
+// Ring geometry for NTB token blocks of 32 rows: a group buffer holds the 64
+// weight rows and 32 NTB token rows, 64 elements each (row r, 16-byte chunk
+// c stored at chunk c ^ swz_f<64>(r)); 3 buffers fit for one token block, 2
+// for two.
+template <int NTB>
+struct DecRing {
+  static constexpr int BUF = (kDecWRows + 32 * NTB) * 64;
+  static constexpr int NBUF = kDecRegion / BUF;
+  static constexpr int NL = kDecWRows / 8 + 4 * NTB;  // DMA instructions per group
+  static_assert(NBUF >= 2 && NBUF <= 3 && NL * (NBUF - 1) <= 32, "ring depth");
+};
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (raw addressing) whose fields are wave-uniform SGPRs.
+__device__ __forceinline__ i32x4_t dec_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
 }
 
-template <int NB, int NTB>
-__device__ __forceinline__ void dec_mfma(const bf16x8_t (&wf)[kDecG][NB],
-                                         const bf16x8_t (&tf)[kDecG][2], f32x16_t (&acc)[NB][2]) {
+// One LDS-DMA instruction: lane l's 16 bytes at rsrc + voff + soff land at LDS
+// byte address m0 + 16 l. Written as asm so that the compiler does not tie the
+// LDS reads that follow to these writes (it cannot tell the ring buffers
+// apart and would drain every load in flight); the ring orders them with
+// explicit vmcnt / lgkmcnt waits. The instruction has no register result.
+// M0 is named as clobbered; no compiler-generated code in these kernels keeps
+// a value in it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS-DMA of one group (byte offset kb along this wave's K range) into the
+// buffer at LDS byte address dst: 8 weight instructions (rows 8i .. 8i+7;
+// the first 4 from rw0, the last 4 from rw1) and 4 NTB token instructions.
+template <int NTB>
+__device__ __forceinline__ void dec_dma(uint32_t dst, i32x4_t rw0, i32x4_t rw1, i32x4_t ract,
+                                        const uint32_t (&w_off)[8], const uint32_t (&t_off)[8],
+                                        uint32_t kb) {
 #pragma unroll
-  for (int s = 0; s < kDecG; ++s)
+  for (int i = 0; i < 8; ++i) dma16(i < 4 ? rw0 : rw1, dst + i * 1024, w_off[i], kb);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+  for (int j = 0; j < 4 * NTB; ++j) dma16(ract, dst + 8192 + j * 1024, t_off[j], kb);
+}
+
+// The 4 k steps of one group from LDS: weight blocks (A operand, rows
+// 32 nb + lane & 31) against token blocks (B operand).
+template <int NTB>
+__device__ __forceinline__ void dec_compute(const uint16_t* src, int rd, int sw, int h,
+                                            f32x16_t (&acc)[2][2]) {
+  bf16x8_t wf[4][2], tf[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int pos = ((2 * s + h) ^ sw) * 8;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      wf[s][nb] = *reinterpret_cast<const bf16x8_t*>(src + nb * 2048 + rd + pos);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+      tf[s][tb] = *reinterpret_cast<const bf16x8_t*>(src + 4096 + tb * 2048 + rd + pos);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb)
         acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s][nb], tf[s][tb], acc[nb][tb],
                                                               0, 0, 0);
+  // every fragment read first, so that the reads of later steps land while
+  // the MFMAs of the first steps run
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * (2 + NTB), 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4 * 2 * NTB, 0);
 }
 
-// This wave's K range: groups of kDecG k steps, two groups of loads in flight
-// (static buffers A / B, so no register copies between groups).
-template <int NB, int NTB>
-__device__ __forceinline__ void dec_kloop(int ng, const uint16_t* const (&wrow)[NB],
-                                          const uint16_t* const (&trow)[2],
-                                          f32x16_t (&acc)[NB][2]) {
-  bf16x8_t wa[kDecG][NB], ta[kDecG][2], wb[kDecG][NB], tb_[kDecG][2];
-  dec_load<NB, NTB>(0, wrow, trow, wa, ta);
-  int g = 0;
-  constexpr int NL = kDecG * (NB + NTB), NM = kDecG * NB * NTB;
-  for (; g + 2 < ng; g += 2) {  // no conditional loads inside: exact vmcnt waits
-    dec_load<NB, NTB>(g + 1, wrow, trow, wb, tb_);
-    dec_mfma<NB, NTB>(wa, ta, acc);
-    dec_load<NB, NTB>(g + 2, wrow, trow, wa, ta);
-    dec_mfma<NB, NTB>(wb, tb_, acc);
-    // keep each group's loads ahead of the previous group's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-  }
-  if (g + 1 < ng) {
-    dec_load<NB, NTB>(g + 1, wrow, trow, wb, tb_);
-    dec_mfma<NB, NTB>(wa, ta, acc);
-    dec_mfma<NB, NTB>(wb, tb_, acc);
+// s_waitcnt vmcnt(NL * r) for r in [0, NBUF - 1), r wave-uniform.
+template <int NL, int NBUF>
+__device__ __forceinline__ void wait_groups(int r) {
+  if constexpr (NBUF <= 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-    dec_mfma<NB, NTB>(wa, ta, acc);
+    if (r >= 1) wait_vmcnt(NL); else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// This wave's ng groups through its ring of NBUF buffers (ring = element
+// pointer, ring_lds = its LDS byte address): NBUF - 1 groups in flight while
+// one is multiplied. Before a buffer is loaded again, the fragment reads of
+// the group it held are complete (lgkmcnt(0); the MFMAs of that group have
+// consumed them anyway).
+template <int NTB>
+__device__ __forceinline__ void dec_kloop(int ng, const uint16_t* ring, uint32_t ring_lds,
+                                          i32x4_t rw0, i32x4_t rw1, i32x4_t ract,
+                                          const uint32_t (&w_off)[8], const uint32_t (&t_off)[8],
+                                          int rd, int sw, int h, f32x16_t (&acc)[2][2]) {
+  using R = DecRing<NTB>;
+  constexpr int NBUF = R::NBUF, BUF = R::BUF, NL = R::NL;
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ng) dec_dma<NTB>(ring_lds + j * BUF * 2, rw0, rw1, ract, w_off, t_off, j * 128u);
+  for (int g0 = 0; g0 < ng; g0 += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      const int g = g0 + j, gl = g + NBUF - 1;
+      if (g < ng) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (gl < ng) {
+          dec_dma<NTB>(ring_lds + ((j + NBUF - 1) % NBUF) * BUF * 2, rw0, rw1, ract, w_off, t_off,
+                       (uint32_t)gl * 128u);
+          wait_vmcnt(NL * (NBUF - 1));
+        } else {
+          wait_groups<NL, NBUF>(ng - 1 - g);
+        }
+        dec_compute<NTB>(ring + j * BUF, rd, sw, h, acc);
+      }
+    }
   }
 }
 
@@ -585,17 +660,21 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* const (&wrow)[
 // epilogue of one pass: gate/up blocks (nb 0 = gate, 1 = up) -> h = silu(g) u
 // in bf16; down blocks -> y_sorted in fp32. Rows p0.. of the pass, r1 = end
 // of the expert's rows; the accumulators hold D[n][m] (n weight row, m token).
-template <bool GATEUP, int NB>
-__device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2],
-                                             float (*s_part)[NB][2][16][64], int p0, int r1,
-                                             int ntb, int c, int N_out, void* __restrict__ out) {
+// Wave w's partial sums sit at s_part + w * WST, [nb][tb][r][lane].
+template <bool GATEUP, int NB, int WST>
+__device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2], float* s_part, int p0,
+                                             int r1, int ntb, int c, int N_out,
+                                             void* __restrict__ out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto part = [&](int w, int nb, int tb, int r) -> float& {
+    return s_part[w * WST + ((nb * 2 + tb) * 16 + r) * 64 + lane];
+  };
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
+      for (int r = 0; r < 16; ++r) part(wave, nb, tb, r) = acc[nb][tb][r];
   __syncthreads();
   {
     const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, lane, half of r)
@@ -610,8 +689,8 @@ __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2],
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = q * 4 + j;
-            v[nb][j] = ((s_part[0][nb][tb][r][lane] + s_part[1][nb][tb][r][lane]) +
-                        s_part[2][nb][tb][r][lane]) + s_part[3][nb][tb][r][lane];
+            v[nb][j] = ((part(0, nb, tb, r) + part(1, nb, tb, r)) + part(2, nb, tb, r)) +
+                       part(3, nb, tb, r);
           }
         const int n_in = q * 8 + (lane >> 5) * 4;  // column inside a 32-wide block
         if (GATEUP) {
@@ -637,16 +716,20 @@ __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2],
   }
 }
 
+// act holds act_bytes bytes (token rows x K); every byte offset formed below
+// is smaller than that (the launcher checks it fits 32 bits).
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
-    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
+    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
     int n_chunks) {
   constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
+  static_assert(NB * 2 * 16 * 64 <= kDecRegion / 2, "partial sums fit the wave's ring");
+  __shared__ __align__(1024) uint16_t s_ring[4 * kDecRegion];
   __shared__ int s_scan[2 * 256 + 2];
-  __shared__ __align__(16) float s_part[4][NB][2][16][64];  // [wave][nb][tb][r][lane]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // s_scan[e]: inclusive count of experts with rows; offsets in s_scan[E+1..]
   for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
   __syncthreads();
@@ -659,35 +742,50 @@ __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
     __syncthreads();
   }
   const int items = s_scan[E - 1] * n_chunks;
-  const int kw = K / 4;  // this wave's K range [wave*kw, wave*kw + kw)
-  const int nsteps = kw / 16;
+  const int kw = K / 4;     // this wave's K range [wave*kw, wave*kw + kw)
+  const int ng = kw / 64;   // groups of 64 elements
+  uint16_t* ring = s_ring + wave * kDecRegion;
+  float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kDecRegion / 2
+  const int rd = (lane & 31) * 64, sw = swz_f<64>(lane & 31), h = lane >> 5;
+  const int lrow = lane >> 3, lch = lane & 7;  // lane's row / chunk inside a DMA instruction
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
+  const i32x4_t ract = dec_rsrc(act, act_bytes);
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int rank = it / n_chunks, c = it - rank * n_chunks;
+    const int rank = it / n_chunks, c = __builtin_amdgcn_readfirstlane(it - rank * n_chunks);
     int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
     }
-    const int e = lo;
+    const int e = __builtin_amdgcn_readfirstlane(lo);
     const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
-    // weight rows of this lane (A operand): block nb, row lane & 31
-    const uint16_t* wrow[NB];
+    // weight rows of the item: gate/up rows [32c, 32c + 32) of both matrices,
+    // down rows [64c, 64c + 64); rows past N_out are clamped to the last one
+    const int nrow0 = GATEUP ? c * 32 : c * 64;
+    const int nrows = min(GATEUP ? 32 : 64, N_out - nrow0);
+    const uint32_t wbytes = (uint32_t)nrows * (uint32_t)K * 2u;
+    const i32x4_t rw0 = dec_rsrc(w0 + ((size_t)e * N_out + nrow0) * K, wbytes);
+    const i32x4_t rw1 = GATEUP ? dec_rsrc(w1 + ((size_t)e * N_out + nrow0) * K, wbytes) : rw0;
+    uint32_t w_off[8];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int n = GATEUP ? c * 32 + (lane & 31) : c * 64 + nb * 32 + (lane & 31);
-      n = n < N_out ? n : N_out - 1;
-      const uint16_t* wm = (GATEUP && nb == 1) ? w1 : w0;
-      wrow[nb] = wm + ((size_t)e * N_out + n) * K + wave * kw + (lane >> 5) * 8;
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + lrow;  // LDS weight row (32 nb + row inside the block)
+      int nl = GATEUP ? (r & 31) : r;
+      nl = nl < nrows ? nl : nrows - 1;
+      w_off[i] = ((uint32_t)nl * (uint32_t)K + (uint32_t)(wave * kw) +
+                  (uint32_t)((lch ^ swz_f<64>(r)) * 8)) * 2u;
     }
     for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
-      const uint16_t* trow[2];
+      uint32_t t_off[8];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        int gi = p0 + tb * 32 + (lane & 31);
+      for (int j = 0; j < 8; ++j) {
+        const int t = 8 * j + lrow;  // token row of the pass (LDS row 64 + t)
+        int gi = p0 + t;
         gi = gi < r1 ? gi : r1 - 1;
         const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
-        trow[tb] = act + (size_t)arow * K + wave * kw + (lane >> 5) * 8;
+        t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
+                    (uint32_t)((lch ^ swz_f<64>(t)) * 8)) * 2u;
       }
       const int ntb = (r1 - p0) > 32 ? 2 : 1;
       f32x16_t acc[NB][2];
@@ -697,13 +795,15 @@ __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
-      const int ng = nsteps / kDecG;
       if (ntb > 1)
-        dec_kloop<NB, 2>(ng, wrow, trow, acc);
+        dec_kloop<2>(ng, ring, ring_lds, rw0, rw1, ract, w_off, t_off, rd, sw, h, acc);
       else
-        dec_kloop<NB, 1>(ng, wrow, trow, acc);
-      dec_epilogue<GATEUP, NB>(acc, s_part, p0, r1, ntb, c, N_out, out);
-      __syncthreads();  // s_part is reused by the next pass / item
+        dec_kloop<1>(ng, ring, ring_lds, rw0, rw1, ract, w_off, t_off, rd, sw, h, acc);
+      // every ring buffer of this wave has landed and been read: the wave's
+      // partial sums may overwrite its ring
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      dec_epilogue<GATEUP, NB, kDecRegion / 2>(acc, s_part, p0, r1, ntb, c, N_out, out);
+      __syncthreads();  // the partial sums are read before the next pass loads
     }
   }
 }
@@ -941,9 +1041,11 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
 }
 
 // The decode kernels take the block when the average expert has few rows.
+// Their token operand is addressed with 32-bit byte offsets.
 bool use_decode_path(const moe_config& c) {
-  return (long)c.num_tokens * c.top_k <= 16L * c.num_experts && c.hidden % 256 == 0 &&
-         c.intermediate % 256 == 0;
+  const long P = (long)c.num_tokens * c.top_k;
+  return P <= 16L * c.num_experts && c.hidden % 256 == 0 && c.intermediate % 256 == 0 &&
+         (long)c.num_tokens * c.hidden * 2 < (1L << 32) && P * c.intermediate * 2 < (1L << 32);
 }
 
 // ---- fp32 path ------------------------------------------------------------
@@ -1032,7 +1134,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
     const int nch = (c.intermediate + 31) / 32;
     decode_gemm_bf16_kernel<true><<<persistent_grid(), 256, 0, s>>>(
         c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
-        sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
+        (uint32_t)((size_t)c.num_tokens * c.hidden * 2), sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
         static_cast<const uint16_t*>(w_up), h, nch);
     return hipGetLastError();
   }
@@ -1058,7 +1160,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
     const int nch = (c.hidden + 63) / 64;
     decode_gemm_bf16_kernel<false><<<persistent_grid(), 256, 0, s>>>(
         c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
-        nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch);
+        (uint32_t)((size_t)P * c.intermediate * 2), nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch);
     return hipGetLastError();
   }
   const int ntn = (c.hidden + 255) / 256;
