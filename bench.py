@@ -46,10 +46,10 @@ FETCH_SCALE = 1048576.0 / 524303.1
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("dd3a62c798a465433a0d5d1ea815fb43c920d491c61e58a4da2b28de9b523ad9",
-                        2988434.1, 393413.4),
-    "decode128_bf16": ("dd3a62c798a465433a0d5d1ea815fb43c920d491c61e58a4da2b28de9b523ad9",
-                       548985.1, 1536.5),
+    "prefill128_bf16": ("f1639145d1ac81c4428616f37148ed2994fb2e5d0465e4a26518f6523decfe44",
+                        5457803.7, 394373.8),
+    "decode128_bf16": ("f1639145d1ac81c4428616f37148ed2994fb2e5d0465e4a26518f6523decfe44",
+                       548879.0, 1552.7),
 }
 
 

@@ -526,18 +526,28 @@ constexpr int kGemmBM = 256, kGemmBK = MOE_GEMM_BK, kGemmStages = MOE_GEMM_BK ==
 // instruction its own cache line (32 weight rows per instruction), and the
 // vector L1 serves such an instruction one lane at a time.
 // Experts with no rows own no work items and read no weight bytes.
-constexpr int kDecWRows = 64;      // weight rows per work item
-constexpr int kDecRegion = 18432;  // LDS ring of one wave, in bf16 elements (36 KB)
+#ifndef MOE_DEC_K
+#define MOE_DEC_K 64
+#endif
+constexpr int kDecWRows = 64;                      // weight rows per work item
+constexpr int kDecK = MOE_DEC_K;                   // K elements per group (row bytes / 2)
+constexpr int kDecOcc = kDecK == 32 ? 2 : 1;       // blocks per CU
+constexpr int kDecRegion = 18432 / kDecOcc;        // LDS ring of one wave, bf16 elements
+constexpr int kDecCPR = kDecK / 8;                 // 16-byte chunks per row
+constexpr int kDecRPI = 64 / kDecCPR;              // rows per DMA instruction (1 KB)
+static_assert(kDecK == 32 || kDecK == 64, "group width");
 
 // Ring geometry for NTB token blocks of 32 rows: a group buffer holds the 64
-// weight rows and 32 NTB token rows, 64 elements each (row r, 16-byte chunk
-// c stored at chunk c ^ swz_f<64>(r)); 3 buffers fit for one token block, 2
-// for two.
+// weight rows and 32 NTB token rows, kDecK elements each (row r, 16-byte
+// chunk c stored at chunk c ^ swz_f<kDecK>(r)); 3 buffers fit for one token
+// block, 2 for two.
 template <int NTB>
 struct DecRing {
-  static constexpr int BUF = (kDecWRows + 32 * NTB) * 64;
+  static constexpr int BUF = (kDecWRows + 32 * NTB) * kDecK;
   static constexpr int NBUF = kDecRegion / BUF;
-  static constexpr int NL = kDecWRows / 8 + 4 * NTB;  // DMA instructions per group
+  static constexpr int WI = kDecWRows / kDecRPI;  // weight DMA instructions per group
+  static constexpr int TI = 32 / kDecRPI;         // token DMA instructions per token block
+  static constexpr int NL = WI + TI * NTB;        // DMA instructions per group
   static_assert(NBUF >= 2 && NBUF <= 3 && NL * (NBUF - 1) <= 32, "ring depth");
 };
 
@@ -570,36 +580,40 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, 
 #pragma clang diagnostic pop
 
 // LDS-DMA of one group (byte offset kb along this wave's K range) into the
-// buffer at LDS byte address dst: 8 weight instructions (rows 8i .. 8i+7;
-// the first 4 from rw0, the last 4 from rw1) and 4 NTB token instructions.
+// buffer at LDS byte address dst: WI weight instructions (kDecRPI rows each;
+// the first half from rw0, the second from rw1) and TI NTB token instructions.
 template <int NTB>
 __device__ __forceinline__ void dec_dma(uint32_t dst, i32x4_t rw0, i32x4_t rw1, i32x4_t ract,
                                         const uint32_t (&w_off)[8], const uint32_t (&t_off)[8],
                                         uint32_t kb) {
+  constexpr int WI = DecRing<NTB>::WI, TI = DecRing<NTB>::TI;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma16(i < 4 ? rw0 : rw1, dst + i * 1024, w_off[i], kb);
+  for (int i = 0; i < WI; ++i) dma16(i < WI / 2 ? rw0 : rw1, dst + i * 1024, w_off[i], kb);
 #pragma unroll
-  for (int j = 0; j < 4 * NTB; ++j) dma16(ract, dst + 8192 + j * 1024, t_off[j], kb);
+  for (int j = 0; j < TI * NTB; ++j)
+    dma16(ract, dst + kDecWRows * kDecK * 2 + j * 1024, t_off[j], kb);
 }
 
-// The 4 k steps of one group from LDS: weight blocks (A operand, rows
+// The kDecK / 16 k steps of one group from LDS: weight blocks (A operand, rows
 // 32 nb + lane & 31) against token blocks (B operand).
 template <int NTB>
 __device__ __forceinline__ void dec_compute(const uint16_t* src, int rd, int sw, int h,
                                             f32x16_t (&acc)[2][2]) {
-  bf16x8_t wf[4][2], tf[4][2];
+  constexpr int KS = kDecK / 16;
+  bf16x8_t wf[KS][2], tf[KS][2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < KS; ++s) {
     const int pos = ((2 * s + h) ^ sw) * 8;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      wf[s][nb] = *reinterpret_cast<const bf16x8_t*>(src + nb * 2048 + rd + pos);
+      wf[s][nb] = *reinterpret_cast<const bf16x8_t*>(src + nb * 32 * kDecK + rd + pos);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
-      tf[s][tb] = *reinterpret_cast<const bf16x8_t*>(src + 4096 + tb * 2048 + rd + pos);
+      tf[s][tb] = *reinterpret_cast<const bf16x8_t*>(src + (kDecWRows + tb * 32) * kDecK + rd +
+                                                     pos);
   }
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -608,8 +622,8 @@ __device__ __forceinline__ void dec_compute(const uint16_t* src, int rd, int sw,
                                                               0, 0, 0);
   // every fragment read first, so that the reads of later steps land while
   // the MFMAs of the first steps run
-  __builtin_amdgcn_sched_group_barrier(0x100, 4 * (2 + NTB), 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 4 * 2 * NTB, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, KS * (2 + NTB), 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, KS * 2 * NTB, 0);
 }
 
 // s_waitcnt vmcnt(NL * r) for r in [0, NBUF - 1), r wave-uniform.
@@ -636,7 +650,8 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* ring, uint32_t
   constexpr int NBUF = R::NBUF, BUF = R::BUF, NL = R::NL;
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j)
-    if (j < ng) dec_dma<NTB>(ring_lds + j * BUF * 2, rw0, rw1, ract, w_off, t_off, j * 128u);
+    if (j < ng)
+      dec_dma<NTB>(ring_lds + j * BUF * 2, rw0, rw1, ract, w_off, t_off, j * (kDecK * 2u));
   for (int g0 = 0; g0 < ng; g0 += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
@@ -645,7 +660,7 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* ring, uint32_t
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (gl < ng) {
           dec_dma<NTB>(ring_lds + ((j + NBUF - 1) % NBUF) * BUF * 2, rw0, rw1, ract, w_off, t_off,
-                       (uint32_t)gl * 128u);
+                       (uint32_t)gl * (kDecK * 2u));
           wait_vmcnt(NL * (NBUF - 1));
         } else {
           wait_groups<NL, NBUF>(ng - 1 - g);
@@ -719,7 +734,7 @@ __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2], float
 // act holds act_bytes bytes (token rows x K); every byte offset formed below
 // is smaller than that (the launcher checks it fits 32 bits).
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
+__global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
@@ -743,11 +758,11 @@ __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
   }
   const int items = s_scan[E - 1] * n_chunks;
   const int kw = K / 4;     // this wave's K range [wave*kw, wave*kw + kw)
-  const int ng = kw / 64;   // groups of 64 elements
+  const int ng = kw / kDecK;  // groups of kDecK elements
   uint16_t* ring = s_ring + wave * kDecRegion;
   float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kDecRegion / 2
-  const int rd = (lane & 31) * 64, sw = swz_f<64>(lane & 31), h = lane >> 5;
-  const int lrow = lane >> 3, lch = lane & 7;  // lane's row / chunk inside a DMA instruction
+  const int rd = (lane & 31) * kDecK, sw = swz_f<kDecK>(lane & 31), h = lane >> 5;
+  const int lrow = lane / kDecCPR, lch = lane % kDecCPR;  // row / chunk inside a DMA instruction
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
   const i32x4_t ract = dec_rsrc(act, act_bytes);
 
@@ -769,23 +784,23 @@ __global__ __launch_bounds__(256, 1) void decode_gemm_bf16_kernel(
     const i32x4_t rw1 = GATEUP ? dec_rsrc(w1 + ((size_t)e * N_out + nrow0) * K, wbytes) : rw0;
     uint32_t w_off[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * i + lrow;  // LDS weight row (32 nb + row inside the block)
+    for (int i = 0; i < kDecWRows / kDecRPI; ++i) {
+      const int r = kDecRPI * i + lrow;  // LDS weight row (32 nb + row inside the block)
       int nl = GATEUP ? (r & 31) : r;
       nl = nl < nrows ? nl : nrows - 1;
       w_off[i] = ((uint32_t)nl * (uint32_t)K + (uint32_t)(wave * kw) +
-                  (uint32_t)((lch ^ swz_f<64>(r)) * 8)) * 2u;
+                  (uint32_t)((lch ^ swz_f<kDecK>(r)) * 8)) * 2u;
     }
     for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
       uint32_t t_off[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 8 * j + lrow;  // token row of the pass (LDS row 64 + t)
+      for (int j = 0; j < 64 / kDecRPI; ++j) {
+        const int t = kDecRPI * j + lrow;  // token row of the pass (LDS row 64 + t)
         int gi = p0 + t;
         gi = gi < r1 ? gi : r1 - 1;
         const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
         t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
-                    (uint32_t)((lch ^ swz_f<64>(t)) * 8)) * 2u;
+                    (uint32_t)((lch ^ swz_f<kDecK>(t)) * 8)) * 2u;
       }
       const int ntb = (r1 - p0) > 32 ? 2 : 1;
       f32x16_t acc[NB][2];
@@ -1132,7 +1147,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
   }
   if (use_decode_path(c)) {
     const int nch = (c.intermediate + 31) / 32;
-    decode_gemm_bf16_kernel<true><<<persistent_grid(), 256, 0, s>>>(
+    decode_gemm_bf16_kernel<true><<<persistent_grid() * kDecOcc, 256, 0, s>>>(
         c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
         (uint32_t)((size_t)c.num_tokens * c.hidden * 2), sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
         static_cast<const uint16_t*>(w_up), h, nch);
@@ -1158,7 +1173,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
   }
   if (use_decode_path(c)) {
     const int nch = (c.hidden + 63) / 64;
-    decode_gemm_bf16_kernel<false><<<persistent_grid(), 256, 0, s>>>(
+    decode_gemm_bf16_kernel<false><<<persistent_grid() * kDecOcc, 256, 0, s>>>(
         c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
         (uint32_t)((size_t)P * c.intermediate * 2), nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch);
     return hipGetLastError();
