@@ -108,6 +108,14 @@ Layout carve(const moe_config& c, void* ws) {
   return L;
 }
 
+// Logits x w^T (+ bias) into out: split-K for small token counts (part is
+// the split-K scratch of the workspace), one pass otherwise.
+hipError_t logits_any(const moe_config& c, const void* x, const void* w, const float* bias,
+                      float* out, float* part, hipStream_t s) {
+  if (router_k_splits(c) > 1) return launch_logits_split(c, x, w, bias, out, part, s);
+  return launch_logits(c, x, w, bias, out, s);
+}
+
 // gate/up + down alone need only h
 size_t swiglu_bytes(const moe_config& c) {
   Carver cv(nullptr);
@@ -152,9 +160,9 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
 
   int router_blocks;
   if (o.noise) {  // clean logits, noise logits, then the noisy top-k from them
-    st = launched(launch_logits(c, x, w_router, logit_bias, L.rlogits, stream));
+    st = launched(logits_any(c, x, w_router, logit_bias, L.rlogits, L.rpart, stream));
     if (st != MOE_OK) return st;
-    st = launched(launch_logits(c, x, o.w_noise, nullptr, L.nlogits, stream));
+    st = launched(logits_any(c, x, o.w_noise, nullptr, L.nlogits, L.rpart, stream));
     if (st != MOE_OK) return st;
     ex.noise = o.noise;
     ex.nlogits = L.nlogits;
@@ -163,8 +171,8 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
                                 true, stream, ex));
     router_blocks = router_num_blocks(c, true);
   } else if (router_k_splits(c) > 1) {
-    st = launched(launch_router_split(c, x, w_router, logit_bias, L.rlogits, router_logits,
-                                      L.rpart, idx, w, partials, stream, ex));
+    st = launched(launch_router_split(c, x, w_router, logit_bias, router_logits, L.rpart, idx, w,
+                                      partials, stream, ex));
     router_blocks = router_num_blocks(c, true);
   } else {
     st = launched(launch_router(c, x, w_router, logit_bias, router_logits,
@@ -241,15 +249,20 @@ moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, con
   ex.sel_bias = o.select_bias;
   ex.k_min = o.dynamic_k_min;
   ex.kt_out = o.k_per_token;
-  if (!o.noise)
+  const Layout L = carve(*cfg, workspace);
+  const bool have_ws = workspace && workspace_bytes >= L.router_end;
+  if (!o.noise) {
+    if (x && have_ws && router_k_splits(*cfg) > 1)  // small T: split-K logits
+      return launched(launch_router_split(*cfg, x, w_router, logit_bias, logits, L.rpart,
+                                          topk_idx, topk_w, nullptr, stream, ex));
     return launched(launch_router(*cfg, x, w_router, x ? logit_bias : nullptr, logits,
                                   logits != nullptr, topk_idx, topk_w, nullptr, true, stream,
                                   ex));
-  const Layout L = carve(*cfg, workspace);
-  if (!workspace || workspace_bytes < L.router_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  st = launched(launch_logits(*cfg, x, w_router, logit_bias, L.rlogits, stream));
+  }
+  if (!have_ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  st = launched(logits_any(*cfg, x, w_router, logit_bias, L.rlogits, L.rpart, stream));
   if (st != MOE_OK) return st;
-  st = launched(launch_logits(*cfg, x, o.w_noise, nullptr, L.nlogits, stream));
+  st = launched(logits_any(*cfg, x, o.w_noise, nullptr, L.nlogits, L.rpart, stream));
   if (st != MOE_OK) return st;
   ex.noise = o.noise;
   ex.nlogits = L.nlogits;

@@ -91,6 +91,8 @@ struct RouterExtras {
   float* logits_final = nullptr;    // logits-input mode: the logits the softmax used
   int k_min = 0;                    // > 0: entropy-driven k in [k_min, top_k]
   int32_t* kt_out = nullptr;        // [T] the k of every token (dynamic k)
+  const float* part = nullptr;      // logits-input mode: split-K partials [nsplit, T, E],
+  int nsplit = 0;                   //   summed in split order (+ bias) as they are read
 };
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
                          const float* bias, float* logits, bool logits_out, int32_t* topk_idx,
@@ -101,14 +103,17 @@ hipError_t launch_logits(const moe_config& c, const void* x, const void* w, cons
                          float* out, hipStream_t s);
 int router_num_blocks(const moe_config& c, bool from_logits);
 // Split-K router for small token counts (bf16): K splits (1 = not worth it),
-// and the launch sequence partial logits -> fixed-order sum (+ bias) ->
-// softmax / top-k. part: [splits, T, E] fp32, logits_ws: [T, E] fp32 scratch.
+// and the launch sequence partial logits -> softmax / top-k, which sums the
+// partials in split order (+ bias) as it reads them. part: [splits, T, E]
+// fp32; logits_out (optional) receives the summed logits.
 int router_k_splits(const moe_config& c);
 hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
-                               const float* bias, float* logits_ws, float* logits_out,
-                               float* part, int32_t* topk_idx, float* topk_w,
-                               float* prob_partials, hipStream_t s,
-                               const RouterExtras& ex = {});
+                               const float* bias, float* logits_out, float* part,
+                               int32_t* topk_idx, float* topk_w, float* prob_partials,
+                               hipStream_t s, const RouterExtras& ex = {});
+// Split-K logits only: out [T,E] = x w^T (+ bias), same summation order.
+hipError_t launch_logits_split(const moe_config& c, const void* x, const void* w,
+                               const float* bias, float* out, float* part, hipStream_t s);
 
 // Dispatch: histogram per chunk, scan, stable scatter. capacity 0 keeps every
 // pair; > 0 keeps the first `capacity` pairs of each expert (pair_pos = -1 for

@@ -4,15 +4,18 @@
 // without bias, softmax over the experts in fp32, top-k, and (Qwen3 only)
 // division of the k weights by their sum. [LAB17] 第二阶段 实现流程 steps 1-3.
 //
-// One block of 256 threads (4 wave64) owns 64 tokens:
+// One block of 256 threads (4 wave64) owns 64 tokens (fewer when it starts
+// from given or split-K partial logits and T is small):
 //  1. logits tile [64 tokens x E] — bf16: MFMA 32x32x16 with the router rows
 //     as the A operand and the tokens as B, K staged through swizzled LDS;
-//     fp32: plain FMA dot products. (x == nullptr: the tile is read.)
-//  2. each wave takes 16 tokens, 4 at a time (their reductions interleave);
-//     lanes hold experts e = lane + 64q. Softmax max/sum are xor-butterfly
-//     reductions (every lane ends with the same bits). Top-k is k rounds of a wave max over 64-bit keys
-//     (order-preserving fp32 bits, then 0xFFFF - e), so equal logits go to
-//     the lower expert index; -0.0 is folded into +0.0 first.
+//     fp32: plain FMA dot products. (x == nullptr: the tile is read, or
+//     summed from split-K partials.)
+//  2. each wave takes a quarter of the tokens, up to 4 at a time (their
+//     reductions interleave); lanes hold experts e = lane + 64q. Softmax
+//     max/sum are xor-butterfly reductions (every lane ends with the same
+//     bits). Top-k is k rounds of a wave max over 64-bit keys (order-preserving
+//     fp32 bits, then 0xFFFF - e), so equal logits go to the lower expert
+//     index; -0.0 is folded into +0.0 first.
 //  3. per-block sums of the full softmax over the block's tokens (fixed order)
 //     for the load-balance statistic P_e, and of (ln sum_e exp l)^2 for the
 //     router z-loss.
@@ -44,27 +47,29 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-constexpr int kNT = 4;  // tokens reduced together per wave
-
-__device__ __forceinline__ void wave_max_n(float (&v)[kNT]) {
+// Reductions over the 64 lanes of N tokens at once (independent chains).
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
   for (int msk = 32; msk >= 1; msk >>= 1)
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) v[u] = fmaxf(v[u], __shfl_xor(v[u], msk, 64));
+    for (int u = 0; u < N; ++u) v[u] = fmaxf(v[u], __shfl_xor(v[u], msk, 64));
 }
 
-__device__ __forceinline__ void wave_sum_n(float (&v)[kNT]) {
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
 #pragma unroll
   for (int msk = 32; msk >= 1; msk >>= 1)
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) v[u] += __shfl_xor(v[u], msk, 64);
+    for (int u = 0; u < N; ++u) v[u] += __shfl_xor(v[u], msk, 64);
 }
 
-__device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[kNT]) {
+template <int N>
+__device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[N]) {
 #pragma unroll
   for (int msk = 32; msk >= 1; msk >>= 1)
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) {
+    for (int u = 0; u < N; ++u) {
       const unsigned long long o = __shfl_xor(v[u], msk, 64);
       v[u] = (o > v[u]) ? o : v[u];
     }
@@ -74,7 +79,7 @@ __device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[kNT]) {
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
 
 // Logits tile by bf16 MFMA into s_log[t * ls + e] (+ bias).
-__device__ void router_logits_mfma(int T, int H, int E, int t0, int kbeg, int kend,
+__device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, int kbeg, int kend,
                                    const uint16_t* __restrict__ x,
                                    const uint16_t* __restrict__ wr, const float* __restrict__ bias,
                                    char* smem, float* s_log, int ls) {
@@ -158,21 +163,45 @@ __device__ void router_logits_mfma(int T, int H, int E, int t0, int kbeg, int ke
   }
 }
 
-template <bool BF16>
+// NT: tokens a wave reduces together (1 when a wave owns a single token).
+template <bool BF16, int NT>
 __global__ __launch_bounds__(kThreads) void router_kernel(
     int T, int H, int E, int k, int norm, const void* __restrict__ x, const void* __restrict__ wr,
     const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, float* __restrict__ partials,
     int do_select, int tpb, const float* __restrict__ noise, const float* __restrict__ nlogits,
     const float* __restrict__ sel_bias, float* __restrict__ zpart, int k_min,
-    int32_t* __restrict__ kt_out) {
+    int32_t* __restrict__ kt_out, const float* __restrict__ part, int nsplit) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * tpb;  // tpb = 64 when the logits are computed here
   const int ls = ((E + 31) & ~31) + 1;
   float* s_log = reinterpret_cast<float*>(smem);  // [64][ls]
 
-  if (logits_in) {
+  if (part) {  // split-K partial logits: sum in split order, then the bias
+    // The loads of 16 splits are issued before the first add (one memory
+    // round trip per 16 splits instead of one per split); the adds keep the
+    // split order.
+    const size_t stride = (size_t)T * E;
+    for (int i = tid; i < tpb * E; i += kThreads) {
+      const int t = i / E, e = i - t * E;
+      float l = 0.0f;
+      if (t0 + t < T) {
+        const float* p = part + (size_t)(t0 + t) * E + e;
+        int ks = 0;
+        for (; ks + 16 <= nsplit; ks += 16) {
+          float r[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) r[j] = p[(size_t)(ks + j) * stride];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) l += r[j];
+        }
+        for (; ks < nsplit; ++ks) l += p[(size_t)ks * stride];
+        if (bias) l += bias[e];
+      }
+      s_log[t * ls + e] = l;
+    }
+  } else if (logits_in) {
     for (int i = tid; i < tpb * E; i += kThreads) {
       const int t = i / E, e = i - t * E;
       float l = 0.0f;
@@ -208,28 +237,30 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   const int EQ = (E + 63) >> 6;  // <= 4 experts per lane
   float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float zacc = 0.0f;  // this wave's sum of (ln sum_e exp l)^2 over its tokens
-  // kNT tokens at a time per wave: their cross-lane reductions are independent
-  // chains, so the shuffle latencies overlap.
-  for (int tt = 0; tt < tpb / 4; tt += kNT) {
-    const int tb0 = wave * (tpb / 4) + tt;
+  // Each wave owns tpb / 4 tokens, taken NT at a time: their cross-lane
+  // reductions are independent chains, so the shuffle latencies overlap.
+  const int tpw = tpb / 4;
+  for (int tt = 0; tt < tpw; tt += NT) {
+    const int tb0 = wave * tpw + tt;
     if (t0 + tb0 >= T) break;  // wave-uniform
-    bool ok[kNT];
-    float v[kNT][4], m[kNT], ex[kNT][4], ssum[kNT], inv[kNT];
+    bool ok[NT];
+    float v[NT][4], m[NT], ex[NT][4], ssum[NT], inv[NT];
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) {
+    for (int u = 0; u < NT; ++u) {
       const int t = tb0 + u, gt = t0 + t;
-      ok[u] = gt < T;
+      const bool mine = tt + u < tpw;  // a row of this wave (and of this block)
+      ok[u] = mine && gt < T;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        v[u][q] = (q < EQ && e < E) ? s_log[t * ls + e] : -INFINITY;
+        v[u][q] = (q < EQ && e < E) ? (mine ? s_log[t * ls + e] : 0.0f) : -INFINITY;
         if (logits_out && ok[u] && q < EQ && e < E) logits_out[(size_t)gt * E + e] = v[u][q];
       }
       m[u] = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
     }
     wave_max_n(m);
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) {
+    for (int u = 0; u < NT; ++u) {
       ssum[u] = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -240,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     }
     wave_sum_n(ssum);
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) {
+    for (int u = 0; u < NT; ++u) {
       inv[u] = 1.0f / ssum[u];
       if (ok[u]) {
 #pragma unroll
@@ -252,13 +283,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
     // entropy-driven number of experts ([QWEN3-ROUTE] §二 dynamic TopK):
     // k_t = clamp(floor(k_min + (k - k_min) H_t / ln E)), H_t = -sum p ln max(p, 1e-10)
-    int kt[kNT];
+    int kt[NT];
 #pragma unroll
-    for (int u = 0; u < kNT; ++u) kt[u] = k;
+    for (int u = 0; u < NT; ++u) kt[u] = k;
     if (k_min > 0) {
-      float hs[kNT];
+      float hs[NT];
 #pragma unroll
-      for (int u = 0; u < kNT; ++u) {
+      for (int u = 0; u < NT; ++u) {
         hs[u] = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
       wave_sum_n(hs);
       const float span = (float)(k - k_min) / logf((float)E);
 #pragma unroll
-      for (int u = 0; u < kNT; ++u) {
+      for (int u = 0; u < NT; ++u) {
         const int kk = (int)floorf(fmaf(-hs[u], span, (float)k_min));
         kt[u] = kk < k_min ? k_min : (kk > k ? k : kk);
         if (kt_out && ok[u] && lane == 0) kt_out[t0 + tb0 + u] = kt[u];
@@ -277,11 +308,11 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     }
 
     if (do_select) {
-      uint32_t key[kNT][4];
-      int my_e[kNT];
-      float my_p[kNT], psum[kNT];
+      uint32_t key[NT][4];
+      int my_e[NT];
+      float my_p[NT], psum[NT];
 #pragma unroll
-      for (int u = 0; u < kNT; ++u) {
+      for (int u = 0; u < NT; ++u) {
         my_e[u] = 0;
         my_p[u] = 0.0f;
         psum[u] = 0.0f;
@@ -293,9 +324,9 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
         }
       }
       for (int j = 0; j < k; ++j) {
-        unsigned long long best[kNT];
+        unsigned long long best[NT];
 #pragma unroll
-        for (int u = 0; u < kNT; ++u) {
+        for (int u = 0; u < NT; ++u) {
           best[u] = 0ull;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -306,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
         }
         wave_max_u64_n(best);
 #pragma unroll
-        for (int u = 0; u < kNT; ++u) {
+        for (int u = 0; u < NT; ++u) {
           const int ej = 0xFFFF - static_cast<int>(best[u] & 0xFFFFull);
           if ((ej & 63) == lane) {
 #pragma unroll
@@ -325,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
         }
       }
 #pragma unroll
-      for (int u = 0; u < kNT; ++u) {
+      for (int u = 0; u < NT; ++u) {
         const int gt = t0 + tb0 + u;
         if (ok[u] && lane < k) {  // slots past k_t are empty (dynamic k)
           const bool live = lane < kt[u];
@@ -361,8 +392,9 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 // Split-K router logits for small token counts (a single 64-token block
 // would stream the whole router matrix through one CU): block (tile, ks)
 // computes the partial logits of its 64 tokens over K range ks, written to
-// part[ks][t][e]; router_reduce_kernel sums the partials in ks order and adds
-// the bias, then the usual router_kernel runs on the summed logits.
+// part[ks][t][e]. The top-k pass (router_kernel) sums the partials in ks order
+// and adds the bias as it reads them; router_reduce_kernel does the same sum
+// where only the logits are wanted.
 __global__ __launch_bounds__(kThreads) void router_partial_kernel(
     int T, int H, int E, int kchunk, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wr, float* __restrict__ part) {
@@ -387,7 +419,16 @@ __global__ __launch_bounds__(kThreads) void router_reduce_kernel(int T, int E, i
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= T * E) return;
   float s = 0.0f;
-  for (int ks = 0; ks < nsplit; ++ks) s += part[(size_t)ks * T * E + i];
+  const size_t stride = (size_t)T * E;
+  int ks = 0;
+  for (; ks + 16 <= nsplit; ks += 16) {  // 16 loads in flight, adds in split order
+    float r[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = part[(size_t)(ks + j) * stride + i];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += r[j];
+  }
+  for (; ks < nsplit; ++ks) s += part[(size_t)ks * stride + i];
   if (bias) s += bias[i % E];
   logits[i] = s;
   if (logits_out) logits_out[i] = s;
@@ -396,10 +437,11 @@ __global__ __launch_bounds__(kThreads) void router_reduce_kernel(int T, int E, i
 }  // namespace
 
 // Tokens per router block: 64 when the block computes its logits (one MFMA
-// tile); 16 when it starts from logits and T is small (more waves share the
-// top-k work).
+// tile); fewer when it starts from logits and T is small, so that more waves
+// share the top-k work (its cost is the serial reduction chain of each wave).
 int router_tpb(const moe_config& c, bool from_logits) {
-  return (from_logits && c.num_tokens <= 4096) ? 16 : kTok;
+  if (!from_logits) return kTok;
+  return c.num_tokens <= 256 ? 4 : c.num_tokens <= 4096 ? 16 : kTok;
 }
 
 int router_num_blocks(const moe_config& c, bool from_logits) {
@@ -413,15 +455,15 @@ int router_k_splits(const moe_config& c) {
   // and top-k in one pass) is faster than split + reduce + a top-k pass.
   int ks = 1;
   while (router_num_blocks(c, false) * ks * 2 <= 256 && c.hidden % (ks * 2 * kBK) == 0 &&
-         c.hidden / (ks * 2) >= 256)
+         c.hidden / (ks * 2) >= 2 * kBK)
     ks *= 2;
   return ks;
 }
 
-hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
-                               const float* bias, float* logits_ws, float* logits_out,
-                               float* part, int32_t* topk_idx, float* topk_w,
-                               float* prob_partials, hipStream_t s, const RouterExtras& ex) {
+namespace {
+
+void launch_partial(const moe_config& c, const void* x, const void* w, float* part,
+                    hipStream_t s) {
   const int ks = router_k_splits(c), E = c.num_experts;
   const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
@@ -429,16 +471,33 @@ hipError_t launch_router_split(const moe_config& c, const void* x, const void* w
   if (tiles > lds) lds = tiles;
   router_partial_kernel<<<dim3(router_num_blocks(c, false), ks), kThreads, lds, s>>>(
       c.num_tokens, c.hidden, E, c.hidden / ks, static_cast<const uint16_t*>(x),
-      static_cast<const uint16_t*>(w_router), part);
-  const int n = c.num_tokens * E;
-  router_reduce_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(
-      c.num_tokens, E, ks, part, bias, logits_ws, logits_out);
+      static_cast<const uint16_t*>(w), part);
+}
+
+}  // namespace
+
+hipError_t launch_router_split(const moe_config& c, const void* x, const void* w_router,
+                               const float* bias, float* logits_out, float* part,
+                               int32_t* topk_idx, float* topk_w, float* prob_partials,
+                               hipStream_t s, const RouterExtras& ex) {
+  launch_partial(c, x, w_router, part, s);
   RouterExtras e2 = ex;
   e2.noise = nullptr;  // the split path serves the plain logits
   e2.nlogits = nullptr;
-  e2.logits_final = nullptr;
-  return launch_router(c, nullptr, nullptr, nullptr, logits_ws, false, topk_idx, topk_w,
+  e2.logits_final = logits_out;
+  e2.part = part;
+  e2.nsplit = router_k_splits(c);
+  return launch_router(c, nullptr, nullptr, bias, nullptr, false, topk_idx, topk_w,
                        prob_partials, true, s, e2);
+}
+
+hipError_t launch_logits_split(const moe_config& c, const void* x, const void* w,
+                               const float* bias, float* out, float* part, hipStream_t s) {
+  launch_partial(c, x, w, part, s);
+  const int n = c.num_tokens * c.num_experts;
+  router_reduce_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(
+      c.num_tokens, c.num_experts, router_k_splits(c), part, bias, out, nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const moe_config& c, const void* x, const void* w_router,
@@ -459,16 +518,18 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   const float* lin = x ? nullptr : logits;
   float* lout = x ? (logits_out ? logits : nullptr) : ex.logits_final;
   const float* noise = x ? nullptr : ex.noise;
-  if (c.dtype == MOE_DTYPE_BF16)
-    router_kernel<true><<<grid, block, lds, s>>>(
-        c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
-        topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
-        ex.zpart, ex.k_min, ex.kt_out);
-  else
-    router_kernel<false><<<grid, block, lds, s>>>(
-        c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,
-        topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias,
-        ex.zpart, ex.k_min, ex.kt_out);
+#define MOE_ROUTER_LAUNCH(BF, NT_)                                                            \
+  router_kernel<BF, NT_><<<grid, block, lds, s>>>(                                              \
+      c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,       \
+      topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias, ex.zpart, \
+      ex.k_min, ex.kt_out, ex.part, ex.nsplit)
+  const bool one = tpb / 4 == 1;  // one token per wave
+  if (c.dtype == MOE_DTYPE_BF16) {
+    if (one) MOE_ROUTER_LAUNCH(true, 1); else MOE_ROUTER_LAUNCH(true, 4);
+  } else {
+    if (one) MOE_ROUTER_LAUNCH(false, 1); else MOE_ROUTER_LAUNCH(false, 4);
+  }
+#undef MOE_ROUTER_LAUNCH
   return hipGetLastError();
 }
 

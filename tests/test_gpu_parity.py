@@ -82,6 +82,36 @@ def test_router_from_x_matches_oracle(orc, dtype, T, H, E, k, zipf):
     np.testing.assert_allclose(host(g_w)[same], w_ref[same], rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("T,H,E,k,zipf", [(64, 4096, 128, 8, 1.2), (5, 512, 40, 3, 0.0),
+                                          (70, 1024, 256, 4, 0.0), (129, 2048, 64, 8, 1.2),
+                                          (300, 512, 64, 8, 0.0), (1, 256, 8, 2, 0.0)])
+def test_router_ex_split_k_matches_oracle(orc, T, H, E, k, zipf):
+    """router_topk_ex with a workspace takes the split-K logits for small T
+    (partials summed in split order by the top-k pass)."""
+    cfg = MoEConfig("t", T=T, H=H, E=E, k=k, I=64, norm=True, dtype="bf16", zipf_s=zipf)
+    inp = make_inputs(cfg, seed=8, weights=False)
+    lg_ref = orc.logits(inp["x"], inp["w_router"], inp["logit_bias"])
+    idx_ref, w_ref, _ = orc.route(lg_ref, k, True)
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    g_lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    g_idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    g_w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    binding.router_topk_ex(c, None, dev(inp["x"]), dev(inp["w_router"]), dev(inp["logit_bias"]),
+                           g_lg, g_idx, g_w, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(g_lg), lg_ref, rtol=0, atol=2e-5 * max(1.0, H / 1024))
+    gi = host(g_idx)
+    for t in np.where((gi != idx_ref).any(1))[0]:
+        check_selection_row(lg_ref[t], gi[t], idx_ref[t], k, t)
+    same = (gi == idx_ref).all(1)
+    np.testing.assert_allclose(host(g_w)[same], w_ref[same], rtol=0, atol=1e-5)
+    # the selection of the returned logits is exact
+    idx2, w2, _ = orc.route(host(g_lg), k, True)
+    assert (gi == idx2).all()
+    np.testing.assert_allclose(host(g_w), w2, rtol=1e-6, atol=1e-7)
+
+
 # ---------------------------------------------------------------- dispatch
 
 
