@@ -12,15 +12,23 @@ combine, load-balance statistics) over one batch of seeded synthetic input that
 is already resident in HBM. Prints ONE JSON line with throughput (tokens/s), the
 roofline of the dominant kernel (the gate/up grouped GEMM, timed on its own with
 HIP events on the stream it runs on) and the CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload. Also in the line: the per-step distribution
+(median, p10, p90 from one event per step), each stage timed on its own, the
+shader clock sampled from sysfs during the timed steps, and for weight-streaming
+workloads the same steps (and the gate/up launch) with 512 MB of other data
+touched between them, outside the timed events: read (no weight byte can then
+come from the 256 MB MALL) and, separately, written (the MALL is then full of
+dirty lines that the next kernel's reads evict with write-backs).
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -146,11 +154,89 @@ def cpu_baseline(cfg, inp, budget_s: float, w4=None):
                       f"fp64 scalar loops), {dt:.1f} s"}
 
 
+def pct(v, q):
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q))
+
+
+def dist(v):
+    return {"median_ms": pct(v, 50), "p10_ms": pct(v, 10), "p90_ms": pct(v, 90)}
+
+
+def clock_files(torch):
+    """sysfs file with the shader clock levels of device 0 (amdgpu pp_dpm_sclk,
+    the current level marked with '*'), found through its PCI address."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        bdf = "%04x:%02x:%02x.0" % (getattr(pr, "pci_domain_id", 0), pr.pci_bus_id,
+                                    pr.pci_device_id)
+    except Exception:
+        return []
+    return glob.glob(f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk")
+
+
+def read_sclk_mhz(fn):
+    with open(fn) as f:
+        for ln in f:
+            if ln.rstrip().endswith("*"):
+                return float(ln.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+    return None
+
+
+class ClockSampler:
+    """Reads the current shader clock from sysfs every 20 ms on a host thread."""
+
+    def __init__(self, files):
+        self.files, self.samples, self._stop = files, [], threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            for fn in self.files:
+                try:
+                    v = read_sclk_mhz(fn)
+                    if v is not None:
+                        self.samples.append(v)
+                except (OSError, ValueError, IndexError):
+                    pass
+            self._stop.wait(0.02)
+
+    def __enter__(self):
+        if self.files:
+            self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        if self.files:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"source": "sysfs pp_dpm_sclk (current level)", "samples": len(self.samples),
+                "median_mhz": pct(self.samples, 50), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples)}
+
+
+def time_per_call(torch, stream, fn, reps):
+    """Per-call times (ms) of fn from one HIP event before each call."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(stream)
+        fn()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill128_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -217,17 +303,46 @@ def main():
         blk.forward(x)
     torch.cuda.synchronize()
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the K timed steps, one event before each (and one after the last)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        blk.forward(x)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    with ClockSampler(clock_files(torch)) as clk:
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            evs[i].record(stream)
+            blk.forward(x)
+        evs[args.steps].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    ms_step = evs[0].elapsed_time(evs[args.steps]) / args.steps
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     log(f"layer: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    streaming = uses_decode_kernel(cfg) or args.w4
+    scrub = torch.ones(1 << 27, dtype=torch.float32, device="cuda") if streaming else None
+    scrubs = {"read": lambda i: scrub.sum(), "write": lambda i: scrub.fill_(float(i))}
+
+    def scrubbed_times(fn, how):
+        """Per-call times of fn with 512 MB of other data read or written before
+        each call (outside the events)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scrubs[how](i)
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    scrubbed = None
+    if streaming:
+        scrubbed = {"scrub_bytes": 4 << 27}
+        for how in ("read", "write"):
+            sm = scrubbed_times(lambda: blk.forward(x), how)
+            scrubbed[f"after_{how}"] = {**dist(sm), "tokens_per_s": cfg.T / (pct(sm, 50) * 1e-3)}
 
     # dominant kernel: gate/up grouped GEMM on its own, same inputs, same stream
     c = blk.c
@@ -260,6 +375,39 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     gu_ms = ev0.elapsed_time(ev1) / args.steps
+    gu_scrubbed = {}
+    if streaming:
+        for how in ("read", "write"):
+            gu_scrubbed[how] = pct(scrubbed_times(gate_up, how), 50)
+    # every stage on its own, same inputs and stream (median of per-call times)
+    y = torch.empty(T * k, cfg.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, cfg.H, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
+    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, lg, idx, wts, blk.ws)
+    def down():
+        if args.w4:
+            binding.expert_down_w4(c, h, offsets, blk.w4_struct, y)
+        else:
+            binding.expert_down(c, h, offsets, blk.w_down, y)
+    def disp():
+        if cap:
+            binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
+        else:
+            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+    stage_fns = [
+        ("router", lambda: binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias,
+                                                  None, idx, wts, blk.ws)),
+        ("dispatch", disp),
+        ("gate_up", gate_up),
+        ("down", down),
+        ("combine", lambda: binding.combine(c, y, pp, wts, out)),
+        ("aux_stats_from_logits", lambda: binding.aux_stats(c, lg, idx, blk.ws, counts=counts,
+                                                            f=blk.f, P=blk.P, aux=blk.aux)),
+    ]
+    stages = {n: pct(time_per_call(torch, stream, fn, max(10, args.steps)), 50)
+              for n, fn in stage_fns}
+    disp()  # counts / offsets of the router's selection again
+    torch.cuda.synchronize()
     cnt = counts.cpu().numpy()
     rows = int(offsets[E].item())  # kept pairs (all of them without a capacity)
     gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt, rows, args.w4)
@@ -286,6 +434,10 @@ def main():
     else:
         roof["kernel"] = "grouped_gemm_bf16_kernel<true,...> (gate/up, SiLU*mul epilogue)"
     roof["kernel_ms"] = gu_ms
+    for how, ms in gu_scrubbed.items():  # same algorithmic bytes, 512 MB touched before
+        ach = gbytes / (ms * 1e-3) / 1e9
+        roof[f"after_{how}_512mb"] = {"kernel_ms": ms, "achieved": ach,
+                                      "frac": ach / PEAK_HBM_GBS}
     roof["algorithmic"] = {"flops": gflops, "bytes": gbytes}
     roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
 
@@ -300,11 +452,16 @@ def main():
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "E": E, "k": k, "I": cfg.I,
                    "norm_topk_prob": cfg.norm, "zipf_s": cfg.zipf_s, "seed": cfg.seed},
         "roofline": roof,
+        "step_ms": dist(step_ms),
+        "stages_ms": stages,
+        "gpu_clock": clk.summary(),
         "layer": {"tflops": lflops / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "hbm_gbs_min_bytes": lbytes / (ms_step * 1e-3) / 1e9,
                   "touched_experts": touched, "wall_ms_per_step": wall * 1e3 / args.steps},
     }
+    if scrubbed:
+        line["mall_scrubbed"] = scrubbed
     if cap:
         line["config"].update(line_cap)
     if args.router != "plain":
