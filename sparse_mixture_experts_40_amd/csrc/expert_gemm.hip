@@ -836,8 +836,12 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
 // The tokens are the A operand and the weights the B operand, so a lane's
 // accumulators belong to one weight row (lane & 31) and one (scale, bias)
 // per group. K is taken in chunks of 64: lane half h covers elements
-// [32h, 32h + 32) of a chunk, i.e. 16 bytes of codes (one load), in 4 MFMA k
-// steps of 8; the token fragments are read in the same order.
+// [32h, 32h + 32) of a chunk, i.e. 16 bytes of codes, in 4 MFMA k steps of 8;
+// the token fragments are read in the same order. As in the bf16 kernel, each
+// wave streams its chunks through a ring of LDS buffers filled by LDS-DMA
+// (codes: 2 lanes per 32-byte row piece; tokens: 8 lanes per 128-byte line;
+// the (scale, bias) dword of every row), so loads coalesce and all waits are
+// explicit counts.
 
 // 8 codes (element 2i in the low nibble of byte i) -> the bf16 values 128 + q.
 __device__ __forceinline__ bf16x8_t w4_unpack8(uint32_t w) {
@@ -850,98 +854,205 @@ __device__ __forceinline__ bf16x8_t w4_unpack8(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-// Loads of chunk ch: the codes of NB weight rows and the token fragments of
-// its 4 k steps.
-template <int NB, int NTB>
-__device__ __forceinline__ void w4_load(int ch, const uint8_t* const (&qrow)[NB],
-                                        const uint16_t* const (&trow)[2], uint4 (&cw)[NB],
-                                        bf16x8_t (&tf)[4][2]) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) cw[nb] = *reinterpret_cast<const uint4*>(qrow[nb] + ch * 32);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-      tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(trow[tb] + ch * 64 + j * 8);
-}
-
 // The 4 k steps of one chunk into the group accumulators: aq += tokens x
-// (128 + q), ax += tokens x 1.
-template <int NB, int NTB>
-__device__ __forceinline__ void w4_chunk(const uint4 (&cw)[NB], const bf16x8_t (&tf)[4][2],
-                                         f32x16_t (&aq)[NB][2], f32x16_t (&ax)[2]) {
+// (128 + q), ax += tokens x 1. FIRST: the chunk opens a group (the first k
+// step starts from zero accumulators).
+template <int NTB, bool FIRST>
+__device__ __forceinline__ void w4_chunk(const uint4 (&cw)[2], const bf16x8_t (&tf)[4][2],
+                                         f32x16_t (&aq)[2][NTB], f32x16_t (&ax)[NTB]) {
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
+  const f32x16_t zero = {};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < 2; ++nb) {
       const uint32_t w = j == 0 ? cw[nb].x : j == 1 ? cw[nb].y : j == 2 ? cw[nb].z : cw[nb].w;
       const bf16x8_t wq = w4_unpack8(w);
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb)
-        aq[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], wq, aq[nb][tb], 0, 0, 0);
+        aq[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tf[j][tb], wq, (FIRST && j == 0) ? zero : aq[nb][tb], 0, 0, 0);
     }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
-      ax[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], ones, ax[tb], 0, 0, 0);
+      ax[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], ones,
+                                                       (FIRST && j == 0) ? zero : ax[tb], 0, 0, 0);
   }
 }
 
-// This wave's groups of 128 (two chunks each), loads one chunk ahead.
-template <int NB, int NTB>
-__device__ __forceinline__ void w4_kloop(int ngroups, const uint8_t* const (&qrow)[NB],
-                                         const uint32_t* const (&sbrow)[NB],
-                                         const uint16_t* const (&trow)[2],
-                                         f32x16_t (&acc)[NB][2]) {
-  uint4 ca[NB], cb[NB];
-  bf16x8_t ta[4][2], tb_[4][2];
-  w4_load<NB, NTB>(0, qrow, trow, ca, ta);
-  for (int g = 0; g < ngroups; ++g) {
-    uint32_t sbw[NB];
+// One LDS-DMA instruction of 4 bytes per lane: lane l's dword at
+// rsrc + voff + soff lands at LDS byte address m0 + 4 l (no register result).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Ring geometry of the 4-bit kernel, per chunk of 64 K elements (bytes): the
+// codes of the 64 weight rows (32 bytes each, 16-byte piece p of row r at
+// p ^ ((r >> 3) & 1)), the (scale, bias) dwords of rows 0..31 and 32..63
+// (256 bytes each, lane l's slot holding row l & 31 of its half), and 32 NTB
+// token rows of 128 bytes (chunk c of row t at c ^ swz_f<64>(t)).
+template <int NTB>
+struct W4Ring {
+  static constexpr int CODE = 0, SB = 2048, TOK = 2560;
+  static constexpr int BUF = TOK + 32 * NTB * 128;
+  static constexpr int NBUF = (2 * kDecRegion) / BUF < 4 ? (2 * kDecRegion) / BUF : 4;
+  static constexpr int NL = 2 + 2 + 4 * NTB;  // DMA instructions per chunk
+  static_assert(NBUF >= 3 && NL * (NBUF - 1) <= 32, "ring depth (reads one chunk ahead)");
+};
+
+// s_waitcnt vmcnt(NL * r), r in [0, NBUF - 1) wave-uniform.
+template <int NL, int NBUF>
+__device__ __forceinline__ void wait_chunks(int r) {
+  if (NBUF > 3 && r >= 2) wait_vmcnt(2 * NL);
+  else if (NBUF > 2 && r >= 1) wait_vmcnt(NL);
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// LDS-DMA of chunk ch of this wave's K range into the buffer at LDS byte
+// address dst (codes from rq0 / rq1, scale-bias dwords from rs0 / rs1).
+template <int NTB>
+__device__ __forceinline__ void w4_dma(uint32_t dst, i32x4_t rq0, i32x4_t rq1, i32x4_t rs0,
+                                       i32x4_t rs1, i32x4_t ract, const uint32_t (&q_off)[2],
+                                       const uint32_t (&s_off)[2], const uint32_t (&t_off)[8],
+                                       int ch) {
+  using R = W4Ring<NTB>;
+  dma16(rq0, dst + R::CODE, q_off[0], ch * 32u);
+  dma16(rq1, dst + R::CODE + 1024, q_off[1], ch * 32u);
+  dma4(rs0, dst + R::SB, s_off[0], (ch >> 1) * 4u);
+  dma4(rs1, dst + R::SB + 256, s_off[1], (ch >> 1) * 4u);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sbw[nb] = sbrow[nb][g];  // (scale, bias) bf16 pair
-    f32x16_t aq[NB][2], ax[2];
+  for (int j = 0; j < 4 * NTB; ++j) dma16(ract, dst + R::TOK + j * 1024, t_off[j], ch * 128u);
+}
+
+// Fragments of the chunk in buffer src (LDS bytes): this lane's codes of its
+// two weight rows and the token fragments of the 4 k steps.
+template <int NTB>
+__device__ __forceinline__ void w4_frag(const uint8_t* src, int lane, uint4 (&cw)[2],
+                                        bf16x8_t (&tf)[4][2]) {
+  using R = W4Ring<NTB>;
+  const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+  for (int nb = 0; nb < 2; ++nb)
+    cw[nb] = *reinterpret_cast<const uint4*>(src + R::CODE + (nb * 32 + n) * 32 +
+                                             ((h ^ ((n >> 3) & 1)) * 16));
+  const int sw = swz_f<64>(n);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ax[tb][r] = 0.0f;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int tb = 0; tb < NTB; ++tb)
+      tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(src + R::TOK + (tb * 32 + n) * 128 +
+                                                     (((4 * h + j) ^ sw) * 16));
+}
+
+// Fold of one group of 128 (two chunks) into acc with the (scale, bias) of
+// this lane's weight rows, read from buffer src.
+template <int NTB>
+__device__ __forceinline__ void w4_fold(const uint8_t* src, int lane, const f32x16_t (&aq)[2][NTB],
+                                        const f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) {
+  using R = W4Ring<NTB>;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) aq[nb][tb][r] = 0.0f;
+  for (int nb = 0; nb < 2; ++nb) {
+    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(src + R::SB + nb * 256 + (lane & 31) * 4);
+    const float scale = __uint_as_float(sbw << 16);
+    const float bias2 = fmaf(-128.0f, scale, __uint_as_float(sbw & 0xFFFF0000u));
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[nb][tb][r] = fmaf(scale, aq[nb][tb][r], fmaf(bias2, ax[tb][r], acc[nb][tb][r]));
+  }
+}
+
+// The ring state of one wave's K loop.
+template <int NTB>
+struct W4Stream {
+  const uint8_t* ring;
+  uint32_t ring_lds;
+  i32x4_t rq0, rq1, rs0, rs1, ract;
+  const uint32_t (&q_off)[2];
+  const uint32_t (&s_off)[2];
+  const uint32_t (&t_off)[8];
+  int nch, lane;
+
+  __device__ __forceinline__ void dma(int ch, int buf) const {
+    w4_dma<NTB>(ring_lds + buf * W4Ring<NTB>::BUF, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off,
+                ch);
+  }
+  // Chunk ch (in buffer bi): start the loads of chunk ch + NBUF - 1, wait for
+  // chunk ch + 1 and read its fragments into the other set (nc, nt) while
+  // chunk ch is multiplied from (cc, ct); FIRST opens a group, otherwise the
+  // group is folded into acc.
+  template <bool FIRST>
+  __device__ __forceinline__ void step(int ch, int bi, const uint4 (&cc)[2],
+                                       const bf16x8_t (&ct)[4][2], uint4 (&nc)[2],
+                                       bf16x8_t (&nt)[4][2], f32x16_t (&aq)[2][NTB],
+                                       f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) const {
+    constexpr int NBUF = W4Ring<NTB>::NBUF, NL = W4Ring<NTB>::NL;
+    // the buffer loaded next held chunk ch - 1, whose reads are complete
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int gl = ch + NBUF - 1;
+    if (gl < nch) dma(gl, (bi + NBUF - 1) % NBUF);
+    if (ch + 1 < nch) {
+      wait_chunks<NL, NBUF>((gl < nch ? gl : nch - 1) - (ch + 1));
+      w4_frag<NTB>(ring + ((bi + 1) % NBUF) * W4Ring<NTB>::BUF, lane, nc, nt);
     }
-    w4_load<NB, NTB>(2 * g + 1, qrow, trow, cb, tb_);
-    w4_chunk<NB, NTB>(ca, ta, aq, ax);
-    if (g + 1 < ngroups) w4_load<NB, NTB>(2 * g + 2, qrow, trow, ca, ta);
-    w4_chunk<NB, NTB>(cb, tb_, aq, ax);
+    w4_chunk<NTB, FIRST>(cc, ct, aq, ax);
+    if (!FIRST) w4_fold<NTB>(ring + bi * W4Ring<NTB>::BUF, lane, aq, ax, acc);
+  }
+};
+
+// This wave's nch chunks (an even number: two per group of 128) through its
+// ring; ring is the byte pointer of the wave's LDS region, ring_lds its LDS
+// address.
+template <int NTB>
+__device__ __forceinline__ void w4_kloop(int nch, const uint8_t* ring, uint32_t ring_lds,
+                                         i32x4_t rq0, i32x4_t rq1, i32x4_t rs0, i32x4_t rs1,
+                                         i32x4_t ract, const uint32_t (&q_off)[2],
+                                         const uint32_t (&s_off)[2], const uint32_t (&t_off)[8],
+                                         int lane, f32x16_t (&acc)[2][NTB]) {
+  constexpr int NBUF = W4Ring<NTB>::NBUF, NL = W4Ring<NTB>::NL;
+  const W4Stream<NTB> st{ring, ring_lds, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off, nch,
+                         lane};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float scale = __uint_as_float(sbw[nb] << 16);
-      const float bias2 = fmaf(-128.0f, scale, __uint_as_float(sbw[nb] & 0xFFFF0000u));
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[nb][tb][r] = fmaf(scale, aq[nb][tb][r], fmaf(bias2, ax[tb][r], acc[nb][tb][r]));
-    }
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < nch) st.dma(j, j);
+  wait_chunks<NL, NBUF>((NBUF - 2 < nch - 1 ? NBUF - 2 : nch - 1));  // chunk 0 has landed
+  uint4 c0[2], c1[2];
+  bf16x8_t t0[4][2], t1[4][2];
+  w4_frag<NTB>(ring, lane, c0, t0);
+  f32x16_t aq[2][NTB], ax[NTB];
+  int bi = 0;  // buffer of the even chunk
+  for (int ch = 0; ch < nch; ch += 2) {
+    st.template step<true>(ch, bi, c0, t0, c1, t1, aq, ax, acc);
+    const int bo = bi + 1 == NBUF ? 0 : bi + 1;
+    st.template step<false>(ch + 1, bo, c1, t1, c0, t0, aq, ax, acc);
+    bi = bo + 1 == NBUF ? 0 : bo + 1;
   }
 }
 
 // Split-K reduction and epilogue for accumulators in the tokens-x-weights
 // orientation: (r, lane) of block (nb, tb) holds token row
-// (r / 4) * 8 + (lane / 32) * 4 + r % 4 and weight row lane & 31.
-template <bool GATEUP, int NB>
-__device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][2],
-                                            float (*s_part)[NB][2][16][64], int p0, int r1,
-                                            int ntb, int c, int N_out, void* __restrict__ out) {
+// (r / 4) * 8 + (lane / 32) * 4 + r % 4 and weight row lane & 31. Wave w's
+// partial sums sit at s_part + w * WST, [nb][tb][r][lane].
+template <bool GATEUP, int NB, int NTB, int WST>
+__device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][NTB], float* s_part, int p0,
+                                            int r1, int ntb, int c, int N_out,
+                                            void* __restrict__ out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto part = [&](int w, int nb, int tb, int r, int ln) -> float& {
+    return s_part[w * WST + ((nb * 2 + tb) * 16 + r) * 64 + ln];
+  };
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_part[wave][nb][tb][r][lane] = acc[nb][tb][r];
+      for (int r = 0; r < 16; ++r) part(wave, nb, tb, r, lane) = acc[nb][tb][r];
   __syncthreads();
   {
     const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, token m, half of columns)
@@ -957,8 +1068,8 @@ __device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][2],
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int ln = l_m + n_in + j;
-            v[nb][j] = ((s_part[0][nb][tb][r_m][ln] + s_part[1][nb][tb][r_m][ln]) +
-                        s_part[2][nb][tb][r_m][ln]) + s_part[3][nb][tb][r_m][ln];
+            v[nb][j] = ((part(0, nb, tb, r_m, ln) + part(1, nb, tb, r_m, ln)) +
+                        part(2, nb, tb, r_m, ln)) + part(3, nb, tb, r_m, ln);
           }
         if (GATEUP) {
           const int col = c * 32 + n_in;
@@ -980,18 +1091,21 @@ __device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][2],
 }
 
 // K (= H for gate/up, I for down) is a multiple of 512, so each wave's quarter
-// is a whole number of 128-groups.
+// is a whole number of 128-groups. act holds act_bytes bytes; every byte
+// offset formed below is smaller (the launcher checks it fits 32 bits).
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
-    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
+    int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ q0, const uint16_t* __restrict__ sb0,
     const uint8_t* __restrict__ q1, const uint16_t* __restrict__ sb1, void* __restrict__ out,
     int n_chunks) {
   constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
+  static_assert(NB * 2 * 16 * 64 <= kDecRegion / 2, "partial sums fit the wave's ring");
+  __shared__ __align__(1024) uint8_t s_ring[4 * 2 * kDecRegion];
   __shared__ int s_scan[2 * 256 + 2];
-  __shared__ __align__(16) float s_part[4][NB][2][16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
   __syncthreads();
   if (tid < E) s_scan[tid] = (s_scan[E + 2 + tid] > s_scan[E + 1 + tid]) ? 1 : 0;
@@ -1003,54 +1117,80 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
     __syncthreads();
   }
   const int items = s_scan[E - 1] * n_chunks;
-  const int kw = K / 4;  // this wave's K range [wave*kw, wave*kw + kw)
-  const int ngroups = kw / 128;
-  const int G = K / 128;
+  const int kw = K / 4;      // this wave's K range [wave*kw, wave*kw + kw)
+  const int nch = kw / 64;   // chunks of 64 (an even number)
+  const int G = K / 128;     // (scale, bias) groups per row
+  uint8_t* ring = s_ring + wave * 2 * kDecRegion;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
+  float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kDecRegion / 2
+  const i32x4_t ract = dec_rsrc(act, act_bytes);
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int rank = it / n_chunks, c = it - rank * n_chunks;
+    const int rank = it / n_chunks, c = __builtin_amdgcn_readfirstlane(it - rank * n_chunks);
     int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
     }
-    const int e = lo;
+    const int e = __builtin_amdgcn_readfirstlane(lo);
     const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
-    const uint8_t* qrow[NB];
-    const uint32_t* sbrow[NB];
+    // weight rows of the item (gate/up: rows [32c, 32c + 32) of both matrices;
+    // down: rows [64c, 64c + 64)); rows past N_out are clamped to the last one
+    const int nrow0 = GATEUP ? c * 32 : c * 64;
+    const int nrows = min(GATEUP ? 32 : 64, N_out - nrow0);
+    const size_t row0 = (size_t)e * N_out + nrow0;
+    const i32x4_t rq0 = dec_rsrc(q0 + row0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
+    const i32x4_t rq1 =
+        GATEUP ? dec_rsrc(q1 + row0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2)) : rq0;
+    const i32x4_t rs0 = dec_rsrc(sb0 + row0 * G * 2, (uint32_t)nrows * (uint32_t)G * 4u);
+    const i32x4_t rs1 =
+        GATEUP ? dec_rsrc(sb1 + row0 * G * 2, (uint32_t)nrows * (uint32_t)G * 4u) : rs0;
+    uint32_t q_off[2], s_off[2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int n = GATEUP ? c * 32 + (lane & 31) : c * 64 + nb * 32 + (lane & 31);
-      n = n < N_out ? n : N_out - 1;
-      const uint8_t* qm = (GATEUP && nb == 1) ? q1 : q0;
-      const uint16_t* sm = (GATEUP && nb == 1) ? sb1 : sb0;
-      const size_t row = (size_t)e * N_out + n;
-      qrow[nb] = qm + row * (K / 2) + (wave * kw) / 2 + (lane >> 5) * 16;
-      sbrow[nb] = reinterpret_cast<const uint32_t*>(sm + (row * G + (wave * kw) / 128) * 2);
+    for (int i = 0; i < 2; ++i) {
+      const int r = 32 * i + (lane >> 1);  // LDS code row: 32 nb + row inside the block
+      int nl = GATEUP ? (r & 31) : r;
+      nl = nl < nrows ? nl : nrows - 1;
+      q_off[i] = (uint32_t)nl * (uint32_t)(K / 2) + (uint32_t)(wave * kw / 2) +
+                 (uint32_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
+      int ns = (GATEUP || i == 0) ? (lane & 31) : 32 + (lane & 31);
+      ns = ns < nrows ? ns : nrows - 1;
+      s_off[i] = ((uint32_t)ns * (uint32_t)G + (uint32_t)(wave * kw / 128)) * 4u;
     }
     for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
-      const uint16_t* trow[2];
+      uint32_t t_off[8];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        int gi = p0 + tb * 32 + (lane & 31);
+      for (int j = 0; j < 8; ++j) {
+        const int t = 8 * j + (lane >> 3);  // token row of the pass
+        int gi = p0 + t;
         gi = gi < r1 ? gi : r1 - 1;
         const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
-        trow[tb] = act + (size_t)arow * K + wave * kw + (lane >> 5) * 32;
+        t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
+                    (uint32_t)(((lane & 7) ^ swz_f<64>(t)) * 8)) * 2u;
       }
       const int ntb = (r1 - p0) > 32 ? 2 : 1;
-      f32x16_t acc[NB][2];
+      // one pass with NT token blocks (accumulators sized for them)
+      auto pass = [&](auto ntb_c) {
+        constexpr int NT = decltype(ntb_c)::value;
+        f32x16_t acc[NB][NT];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+          for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
+        w4_kloop<NT>(nch, ring, ring_lds, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off, lane,
+                     acc);
+        // every ring buffer of this wave has landed and been read: its
+        // partial sums may overwrite its ring
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        w4_epilogue<GATEUP, NB, NT, kDecRegion / 2>(acc, s_part, p0, r1, ntb, c, N_out, out);
+      };
       if (ntb > 1)
-        w4_kloop<NB, 2>(ngroups, qrow, sbrow, trow, acc);
+        pass(std::integral_constant<int, 2>{});
       else
-        w4_kloop<NB, 1>(ngroups, qrow, sbrow, trow, acc);
-      w4_epilogue<GATEUP, NB>(acc, s_part, p0, r1, ntb, c, N_out, out);
-      __syncthreads();  // s_part is reused by the next pass / item
+        pass(std::integral_constant<int, 1>{});
+      __syncthreads();  // the partial sums are read before the next pass loads
     }
   }
 }
@@ -1186,8 +1326,11 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
   return hipGetLastError();
 }
 
+// The 4-bit kernels address their token operand with 32-bit byte offsets.
 bool w4_supported(const moe_config& c) {
-  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0 && c.intermediate % 512 == 0;
+  const long P = (long)c.num_tokens * c.top_k;
+  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0 && c.intermediate % 512 == 0 &&
+         (long)c.num_tokens * c.hidden * 2 < (1L << 32) && P * c.intermediate * 2 < (1L << 32);
 }
 
 hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* sorted_pair,
@@ -1196,7 +1339,7 @@ hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* 
   const int nch = (c.intermediate + 31) / 32;
   decode_w4_kernel<true><<<persistent_grid(), 256, 0, s>>>(
       c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
-      sorted_pair, offsets, w.gate, static_cast<const uint16_t*>(w.gate_sb), w.up,
+      (uint32_t)((size_t)c.num_tokens * c.hidden * 2), sorted_pair, offsets, w.gate, static_cast<const uint16_t*>(w.gate_sb), w.up,
       static_cast<const uint16_t*>(w.up_sb), h, nch);
   return hipGetLastError();
 }
@@ -1206,7 +1349,7 @@ hipError_t launch_down_w4(const moe_config& c, const void* h, const int32_t* off
   const int nch = (c.hidden + 63) / 64;
   decode_w4_kernel<false><<<persistent_grid(), 256, 0, s>>>(
       c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
-      nullptr, offsets, w.down, static_cast<const uint16_t*>(w.down_sb), nullptr, nullptr, y,
+      (uint32_t)((size_t)c.num_tokens * c.top_k * c.intermediate * 2), nullptr, offsets, w.down, static_cast<const uint16_t*>(w.down_sb), nullptr, nullptr, y,
       nch);
   return hipGetLastError();
 }
