@@ -54,10 +54,10 @@ FETCH_SCALE = 1048576.0 / 524303.1
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("f1639145d1ac81c4428616f37148ed2994fb2e5d0465e4a26518f6523decfe44",
-                        5457803.7, 394373.8),
-    "decode128_bf16": ("f1639145d1ac81c4428616f37148ed2994fb2e5d0465e4a26518f6523decfe44",
-                       548879.0, 1552.7),
+    "prefill128_bf16": ("38247525e30b493c72825db44cded19f63f31a638cb9af9bcb5814ce7017a8e6",
+                        5380970.4, 394334.8),
+    "decode128_bf16": ("38247525e30b493c72825db44cded19f63f31a638cb9af9bcb5814ce7017a8e6",
+                       548882.6, 1556.0),
 }
 
 
