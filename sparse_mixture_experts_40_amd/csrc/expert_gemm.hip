@@ -263,8 +263,12 @@ __device__ __forceinline__ void tile_setup(int L, int n_tiles_n, int E, int K, i
   const int mt = s_scan[expert] - s_prev;
   const int local = L - n_tiles_n * s_prev;
   const int n_tile = local / mt, m_tile = local - n_tile * mt;
-  tl.row0 = s_scan[E + 1 + expert] + m_tile * BM;
-  tl.row_end = row_end;
+  // the expert's rows split evenly over its mt row tiles, in multiples of 32
+  // (q <= BM, and every tile is non-empty since n_e > BM (mt - 1) >= q (mt - 1))
+  const int e0 = s_scan[E + 1 + expert];
+  const int q = ((row_end - e0 + mt - 1) / mt + 31) & ~31;
+  tl.row0 = e0 + m_tile * q;
+  tl.row_end = min(tl.row0 + q, row_end);
   tl.n0 = n_tile * NCOL;
   tl.expert = expert;
 #pragma unroll
@@ -272,7 +276,7 @@ __device__ __forceinline__ void tile_setup(int L, int n_tiles_n, int E, int K, i
     const int r = (wave * LA + i) * RPI + lane / CPR;  // tile row written by this lane
     const int lc = (lane % CPR) ^ swz_f<BK>(r);       // logical chunk for its slot
     int gi = tl.row0 + r;
-    gi = gi < row_end ? gi : row_end - 1;
+    gi = gi < tl.row_end ? gi : tl.row_end - 1;
     const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
     a_off[i] = ((uint32_t)arow * (uint32_t)K + (uint32_t)lc * 8u) * 2u;
   }
