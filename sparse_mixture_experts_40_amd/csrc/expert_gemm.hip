@@ -577,9 +577,21 @@ __device__ __forceinline__ i32x4_t dec_rsrc(const void* base, uint32_t bytes) {
 // a value in it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// The descriptor and the scalar operands are wave-uniform by construction;
+// readfirstlane keeps them in SGPRs even where the compiler lost track of that.
+__device__ __forceinline__ i32x4_t uniform4(i32x4_t v) {
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(v.x);
+  r.y = __builtin_amdgcn_readfirstlane(v.y);
+  r.z = __builtin_amdgcn_readfirstlane(v.z);
+  r.w = __builtin_amdgcn_readfirstlane(v.w);
+  return r;
+}
+
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(uniform4(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -675,12 +687,63 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* ring, uint32_t
   }
 }
 
+// The loads of one work item as a wave sees them: weight descriptors and
+// per-lane offsets, token offsets of its (single) pass.
+struct DecItem {
+  i32x4_t rw0, rw1;
+  uint32_t w_off[8], t_off[8];
+};
+
+// One token block, one pass (the common decode item): the ring runs on across
+// items. pre: the item's groups 0 .. NBUF-2 are already in flight, in buffers
+// bq, bq+1, ... (mod NBUF). With nxt, the last NBUF-1 iterations load the
+// next item's groups 0 .. NBUF-2 instead of nothing, so its loads overlap this
+// item's last groups and its epilogue. Returns the buffer of the last group
+// (free when the loop ends; the next item starts at the one after it).
+__device__ __forceinline__ int dec_kloop_stream(int ng, const uint16_t* ring, uint32_t ring_lds,
+                                                const DecItem& cur, bool pre, int bq,
+                                                const DecItem& nxt, bool has_nxt, i32x4_t ract,
+                                                int rd, int sw, int h, f32x16_t (&acc)[2][2]) {
+  using R = DecRing<1>;
+  constexpr int NBUF = R::NBUF, BUF = R::BUF, NL = R::NL;
+  if (!pre) {
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (j < ng)
+        dec_dma<1>(ring_lds + ((bq + j) % NBUF) * BUF * 2, cur.rw0, cur.rw1, ract, cur.w_off,
+                   cur.t_off, j * (kDecK * 2u));
+  }
+  int bi = bq, bl = (bq + NBUF - 1) % NBUF;
+  for (int g = 0; g < ng; ++g) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int gl = g + NBUF - 1;
+    if (gl < ng) {
+      dec_dma<1>(ring_lds + bl * BUF * 2, cur.rw0, cur.rw1, ract, cur.w_off, cur.t_off,
+                 (uint32_t)gl * (kDecK * 2u));
+      wait_vmcnt(NL * (NBUF - 1));
+    } else if (has_nxt) {
+      dec_dma<1>(ring_lds + bl * BUF * 2, nxt.rw0, nxt.rw1, ract, nxt.w_off, nxt.t_off,
+                 (uint32_t)(gl - ng) * (kDecK * 2u));
+      wait_vmcnt(NL * (NBUF - 1));
+    } else {
+      wait_groups<NL, NBUF>(ng - 1 - g);
+    }
+    dec_compute<1>(ring + bi * BUF, rd, sw, h, acc);
+    bi = bi + 1 == NBUF ? 0 : bi + 1;
+    bl = bl + 1 == NBUF ? 0 : bl + 1;
+  }
+  return bi == 0 ? NBUF - 1 : bi - 1;
+}
+
 // Split-K reduction over the 4 waves in fixed order (waves 0..3), then the
 // epilogue of one pass: gate/up blocks (nb 0 = gate, 1 = up) -> h = silu(g) u
 // in bf16; down blocks -> y_sorted in fp32. Rows p0.. of the pass, r1 = end
 // of the expert's rows; the accumulators hold D[n][m] (n weight row, m token).
 // Wave w's partial sums sit at s_part + w * WST, [nb][tb][r][lane].
-template <bool GATEUP, int NB, int WST>
+// Only the partial sums of the first NT token blocks are written (with one
+// token block they take 12 KB: one ring buffer). The barriers are LDS-only,
+// so loads still in flight (the next item's first groups) are not waited for.
+template <bool GATEUP, int NB, int WST, int NT>
 __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2], float* s_part, int p0,
                                              int r1, int ntb, int c, int N_out,
                                              void* __restrict__ out) {
@@ -691,10 +754,10 @@ __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2], float
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) part(wave, nb, tb, r) = acc[nb][tb][r];
-  __syncthreads();
+  lds_barrier();
   {
     const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, lane, half of r)
     const int row = p0 + tb * 32 + (lane & 31);
@@ -770,43 +833,70 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
   const i32x4_t ract = dec_rsrc(act, act_bytes);
 
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int rank = it / n_chunks, c = __builtin_amdgcn_readfirstlane(it - rank * n_chunks);
-    int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
+  // item it: its expert (the (rank+1)-th expert with rows), column chunk,
+  // rows [r0, r1), and its load descriptors (token offsets for the pass at p0)
+  auto locate = [&](int it, int& c, int& e, int& r0, int& r1) {
+    const int rank = it / n_chunks;
+    c = __builtin_amdgcn_readfirstlane(it - rank * n_chunks);
+    int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
     }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
-    // weight rows of the item: gate/up rows [32c, 32c + 32) of both matrices,
-    // down rows [64c, 64c + 64); rows past N_out are clamped to the last one
+    e = __builtin_amdgcn_readfirstlane(lo);
+    r0 = s_scan[E + 1 + e];
+    r1 = s_scan[E + 2 + e];
+  };
+  // weight rows of an item: gate/up rows [32c, 32c + 32) of both matrices,
+  // down rows [64c, 64c + 64); rows past N_out are clamped to the last one
+  auto weights = [&](int c, int e, DecItem& d) {
     const int nrow0 = GATEUP ? c * 32 : c * 64;
     const int nrows = min(GATEUP ? 32 : 64, N_out - nrow0);
     const uint32_t wbytes = (uint32_t)nrows * (uint32_t)K * 2u;
-    const i32x4_t rw0 = dec_rsrc(w0 + ((size_t)e * N_out + nrow0) * K, wbytes);
-    const i32x4_t rw1 = GATEUP ? dec_rsrc(w1 + ((size_t)e * N_out + nrow0) * K, wbytes) : rw0;
-    uint32_t w_off[8];
+    d.rw0 = dec_rsrc(w0 + ((size_t)e * N_out + nrow0) * K, wbytes);
+    d.rw1 = GATEUP ? dec_rsrc(w1 + ((size_t)e * N_out + nrow0) * K, wbytes) : d.rw0;
 #pragma unroll
     for (int i = 0; i < kDecWRows / kDecRPI; ++i) {
       const int r = kDecRPI * i + lrow;  // LDS weight row (32 nb + row inside the block)
       int nl = GATEUP ? (r & 31) : r;
       nl = nl < nrows ? nl : nrows - 1;
-      w_off[i] = ((uint32_t)nl * (uint32_t)K + (uint32_t)(wave * kw) +
-                  (uint32_t)((lch ^ swz_f<kDecK>(r)) * 8)) * 2u;
+      d.w_off[i] = ((uint32_t)nl * (uint32_t)K + (uint32_t)(wave * kw) +
+                    (uint32_t)((lch ^ swz_f<kDecK>(r)) * 8)) * 2u;
     }
-    for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
-      uint32_t t_off[8];
+  };
+  auto tokens = [&](int p0, int r1, DecItem& d) {
 #pragma unroll
-      for (int j = 0; j < 64 / kDecRPI; ++j) {
-        const int t = kDecRPI * j + lrow;  // token row of the pass (LDS row 64 + t)
-        int gi = p0 + t;
-        gi = gi < r1 ? gi : r1 - 1;
-        const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
-        t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
+    for (int j = 0; j < 64 / kDecRPI; ++j) {
+      const int t = kDecRPI * j + lrow;  // token row of the pass (LDS row 64 + t)
+      int gi = p0 + t;
+      gi = gi < r1 ? gi : r1 - 1;
+      const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
+      d.t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
                     (uint32_t)((lch ^ swz_f<kDecK>(t)) * 8)) * 2u;
-      }
-      const int ntb = (r1 - p0) > 32 ? 2 : 1;
+    }
+  };
+
+  bool pre = false;  // the item's first groups are in flight (loaded by the previous item)
+  int bq = 0;        // ring buffer of the item's first group
+  DecItem cur, nxt;
+  int c, e, r0, r1;
+  if (blockIdx.x < items) {
+    locate(blockIdx.x, c, e, r0, r1);
+    weights(c, e, cur);
+  }
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const bool simple = r1 - r0 <= 32;  // one token block, one pass
+    // the next item of this block, prefetched when both are simple
+    const int itn = it + gridDim.x;
+    int cn = 0, en = 0, r0n = 0, r1n = 0;
+    if (itn < items) {
+      locate(itn, cn, en, r0n, r1n);
+      weights(cn, en, nxt);
+    }
+    const bool has_nxt = simple && itn < items && r1n - r0n <= 32 && ng >= DecRing<1>::NBUF;
+    if (simple) {
+      if (!pre) tokens(r0, r1, cur);
+      if (has_nxt) tokens(r0n, r1n, nxt);
       f32x16_t acc[NB][2];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -814,16 +904,51 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
-      if (ntb > 1)
-        dec_kloop<2>(ng, ring, ring_lds, rw0, rw1, ract, w_off, t_off, rd, sw, h, acc);
-      else
-        dec_kloop<1>(ng, ring, ring_lds, rw0, rw1, ract, w_off, t_off, rd, sw, h, acc);
-      // every ring buffer of this wave has landed and been read: the wave's
-      // partial sums may overwrite its ring
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      dec_epilogue<GATEUP, NB, kDecRegion / 2>(acc, s_part, p0, r1, ntb, c, N_out, out);
-      __syncthreads();  // the partial sums are read before the next pass loads
+      const int bz = dec_kloop_stream(ng, ring, ring_lds, cur, pre, bq, nxt, has_nxt, ract, rd,
+                                      sw, h, acc);
+      // this wave's reads are done; the buffer of its last group is free
+      // (loads still in flight target the other buffers)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dec_epilogue<GATEUP, NB, kDecRegion / 2, 1>(
+          acc, reinterpret_cast<float*>(s_ring + bz * DecRing<1>::BUF), r0, r1, 1, c, N_out,
+          out);
+      lds_barrier();  // the partial sums are read before that buffer is loaded again
+      pre = has_nxt;
+      bq = bz + 1 == DecRing<1>::NBUF ? 0 : bz + 1;
+    } else {
+      for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
+        tokens(p0, r1, cur);
+        const int ntb = (r1 - p0) > 32 ? 2 : 1;
+        f32x16_t acc[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
+        if (ntb > 1)
+          dec_kloop<2>(ng, ring, ring_lds, cur.rw0, cur.rw1, ract, cur.w_off, cur.t_off, rd, sw,
+                       h, acc);
+        else
+          dec_kloop<1>(ng, ring, ring_lds, cur.rw0, cur.rw1, ract, cur.w_off, cur.t_off, rd, sw,
+                       h, acc);
+        // every ring buffer of this wave has landed and been read: the
+        // wave's partial sums may overwrite its ring
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if (ntb > 1)
+          dec_epilogue<GATEUP, NB, kDecRegion / 2, 2>(acc, s_part, p0, r1, ntb, c, N_out, out);
+        else
+          dec_epilogue<GATEUP, NB, kDecRegion / 2, 1>(acc, s_part, p0, r1, ntb, c, N_out, out);
+        lds_barrier();  // the partial sums are read before the next pass loads
+      }
+      pre = false;
+      bq = 0;
     }
+    cur = nxt;
+    c = cn;
+    e = en;
+    r0 = r0n;
+    r1 = r1n;
   }
 }
 
