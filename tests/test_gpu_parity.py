@@ -169,6 +169,35 @@ def test_expert_swiglu_matches_oracle(orc, dtype, T, H, E, k, I):
     check_output(host(y), y_ref, dtype, "y_sorted", bf16_rounded=False)
 
 
+@pytest.mark.parametrize("H,I", [(512, 256), (1024, 512)])
+def test_decode_items_mixed_sizes(orc, H, I):
+    """Weight-streaming kernels over experts whose row counts alternate between
+    one token block (<= 32 rows, where the next item's loads overlap the
+    current one), two token blocks (33..64) and several passes (> 64), so that
+    every kind of item follows every other kind inside a block."""
+    E, k = 128, 1
+    pattern = [33, 2, 1, 40, 0, 5, 65, 3, 0, 31, 1, 1, 17, 0, 32, 4]
+    counts = np.array([pattern[(e * 5) % 16] for e in range(E)], np.int64)
+    T = int(counts.sum())
+    assert T * k <= 16 * E  # the decode kernels' regime
+    rng = np.random.default_rng(H + I)
+    idx = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, k)
+    cfg = MoEConfig("mixed_items", T=T, H=H, E=E, k=k, I=I, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=11)
+    g_counts, offsets, sp, pp = orc.dispatch(idx.astype(np.int32), E)
+    assert (g_counts == counts).all()
+    tok = sp // k
+    ex = np.repeat(np.arange(E, dtype=np.int32), counts)
+    y_ref = orc.expert_rows(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], tok, ex)
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    y = torch.empty(T * k, H, dtype=torch.float32, device="cuda")
+    binding.expert_swiglu(c, dev(inp["x"]), _i32(sp), _i32(offsets), dev(inp["w_gate"]),
+                          dev(inp["w_up"]), dev(inp["w_down"]), y, ws)
+    torch.cuda.synchronize()
+    check_output(host(y), y_ref, "bf16", "y_sorted", bf16_rounded=False)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_combine_matches_oracle(orc, dtype):
     T, H, E, k = 300, 256, 16, 4
