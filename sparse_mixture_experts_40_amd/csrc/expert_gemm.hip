@@ -34,56 +34,8 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt vmcnt(n) for the counts the pipelines need (n <= 32; larger
-// counts wait for everything, which is always safe)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
-    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
-    case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
-    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-    case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
-    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-    case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
-    case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
-    case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
-    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-    case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
-    case 26: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
-    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
-    case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
-    case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
-    case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
-    case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
-    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, not for its outstanding global loads (a __syncthreads() fence
-// would drain the whole load pipeline). Each wave waits for its own LDS-DMA
-// loads with wait_vmcnt before arriving, so after the barrier every wave's
-// stage data is in LDS.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // LDS row swizzle: 16-byte chunk c of tile row r is stored at chunk c ^ f(r).
 // f makes the fragment reads (16 consecutive rows at one chunk per 256-byte
@@ -555,45 +507,6 @@ struct DecRing {
   static_assert(NBUF >= 2 && NBUF <= 3 && NL * (NBUF - 1) <= 32, "ring depth");
 };
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor (raw addressing) whose fields are wave-uniform SGPRs.
-__device__ __forceinline__ i32x4_t dec_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-// One LDS-DMA instruction: lane l's 16 bytes at rsrc + voff + soff land at LDS
-// byte address m0 + 16 l. Written as asm so that the compiler does not tie the
-// LDS reads that follow to these writes (it cannot tell the ring buffers
-// apart and would drain every load in flight); the ring orders them with
-// explicit vmcnt / lgkmcnt waits. The instruction has no register result.
-// M0 is named as clobbered; no compiler-generated code in these kernels keeps
-// a value in it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// The descriptor and the scalar operands are wave-uniform by construction;
-// readfirstlane keeps them in SGPRs even where the compiler lost track of that.
-__device__ __forceinline__ i32x4_t uniform4(i32x4_t v) {
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane(v.x);
-  r.y = __builtin_amdgcn_readfirstlane(v.y);
-  r.z = __builtin_amdgcn_readfirstlane(v.z);
-  r.w = __builtin_amdgcn_readfirstlane(v.w);
-  return r;
-}
-
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(uniform4(rsrc)),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // LDS-DMA of one group (byte offset kb along this wave's K range) into the
 // buffer at LDS byte address dst: WI weight instructions (kDecRPI rows each;
