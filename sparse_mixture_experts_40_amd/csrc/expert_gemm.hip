@@ -858,6 +858,10 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
       bq = 0;
     }
     cur = nxt;
+    // the copy loses the compiler's knowledge that the descriptors are
+    // wave-uniform: make them SGPR values once per item
+    cur.rw0 = uniform4(cur.rw0);
+    cur.rw1 = uniform4(cur.rw1);
     c = cn;
     e = en;
     r0 = r0n;
