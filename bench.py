@@ -54,10 +54,10 @@ FETCH_SCALE = 1048576.0 / 524303.1
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("38247525e30b493c72825db44cded19f63f31a638cb9af9bcb5814ce7017a8e6",
-                        5380970.4, 394334.8),
-    "decode128_bf16": ("38247525e30b493c72825db44cded19f63f31a638cb9af9bcb5814ce7017a8e6",
-                       548882.6, 1556.0),
+    "prefill128_bf16": ("51a475b83bd336cf347bb2c951eccfb0569b1b8b1fec1e023b290cedf36a376a",
+                        3934794.4, 393947.3),
+    "decode128_bf16": ("51a475b83bd336cf347bb2c951eccfb0569b1b8b1fec1e023b290cedf36a376a",
+                       549182.2, 1557.5),
 }
 
 
