@@ -187,10 +187,14 @@ moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_r
                            float* topk_w, hipStream_t stream);
 
 /* moe_router_topk with the router options of moe_options (noise, w_noise,
- * select_bias; the other fields are ignored). Noise needs x (the noise logits
- * are computed from it) and a workspace of moe_workspace_size bytes; logits
- * (if non-NULL) receives the noisy logits. Without noise no workspace is used
- * (may be NULL). */
+ * select_bias, dynamic_k_min, k_per_token; the other fields are ignored).
+ * Noise needs x (the noise logits are computed from it) and a workspace of
+ * moe_workspace_size bytes; logits (if non-NULL) receives the noisy logits.
+ * Without noise the workspace may be NULL. When it is given and T is small
+ * (bf16, fewer than one router block per CU), the logits are computed split
+ * along H over many blocks and the partial sums added in a fixed order, the
+ * order moe_layer_forward uses; moe_router_topk (no workspace) sums along H in
+ * one block, so its logits may differ from these in the last bits. */
 moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, const void* x,
                               const void* w_router, const float* logit_bias, float* logits,
                               int32_t* topk_idx, float* topk_w, void* workspace,
