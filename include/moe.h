@@ -269,10 +269,12 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* 
                            size_t workspace_bytes, hipStream_t stream);
 
 /* moe_expert_gate_up / moe_expert_down with 4-bit weights (moe_w4_weights).
- * The kernels stream the codes of the experts that have rows and dequantise
- * them in registers (fp32 scale * q + bias, rounded once to bf16 as the MFMA
- * operand); they are built for few rows per expert (decode batches) and are
- * correct for any number of rows. */
+ * The kernels stream the codes of the experts that have rows. No weight is
+ * rounded: the MFMA multiplies the exact bf16 values 128 + q with the tokens,
+ * and each group of 128 is folded in fp32 as
+ *   scale * sum (128 + q) x + (bias - 128 scale) * sum x.
+ * They are built for few rows per expert (decode batches) and are correct for
+ * any number of rows (each 64 rows of an expert stream its codes once more). */
 moe_status moe_expert_gate_up_w4(const moe_config* cfg, const void* x,
                                  const int32_t* sorted_pair, const int32_t* expert_offsets,
                                  const moe_w4_weights* w, void* h, hipStream_t stream);
