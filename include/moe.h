@@ -140,12 +140,22 @@ typedef struct {
 /* 4-bit group-quantised expert weights, [MOE-128x8] 参数量化与存储优化 (4-bit
  * codes, group_size 128, an independent scale and bias per group; ~75% less
  * memory than 16-bit weights). For a matrix [E, N, K] (gate/up: N = I, K = H;
- * down: N = H, K = I):
- *   codes [E, N, K/2] uint8: element k of row (e, n) is the low nibble of byte
- *         (e*N + n)*K/2 + k/2 for even k and its high nibble for odd k;
- *   sb    [E, N, K/128, 2] bf16: (scale, bias) of the group of 128 consecutive
- *         k starting at 128 g;
+ * down: N = H, K = I), stored in tiles of 32 rows:
+ *   codes [E, N/32, K/64, 32, 32] uint8: tile (e, b, c) holds rows
+ *         [32b, 32b + 32) of expert e, elements [64c, 64c + 64): row r at
+ *         byte 32r, as 8 little-endian 32-bit words of 8 consecutive elements;
+ *         byte j (0..3) of a word holds element j of the word in its low
+ *         nibble and element j + 4 in its high nibble. So code q of element k
+ *         of row n is in byte ((e*N/32 + n/32)*K/64 + k/64)*1024 + (n%32)*32
+ *         + 4*((k%64)/8) + k%4, in its high nibble iff k%8 >= 4;
+ *   sb    [E, N/32, K/128, 32, 2] bf16: (scale, bias) of row 32b + r for the
+ *         group of the 128 elements starting at 128 g at [e, b, g, r];
  *   w[e,n,k] = scale * q + bias.
+ * A tile's codes for one 64-element chunk are one contiguous 1 KB, and a
+ * group's (scale, bias) for 32 rows one 128-byte line, so the kernels load
+ * them with fully used cache lines; one byte permute forms two bf16 operands
+ * from a word. (MLX's row-major packing, element i of a word at bits 4i,
+ * converts to this layout once, on the host.)
  * Device pointers, 16-byte aligned. Used by the *_w4 entry points, which need
  * dtype bf16 and H, I multiples of 512 (MOE_ERR_UNSUPPORTED otherwise). */
 typedef struct {

@@ -374,23 +374,27 @@ int orc_expert_rows(int H, int I, int dtype, const void* x, const void* wg, cons
 
 /* 4-bit group-quantised weights, [MOE-128x8] 参数量化与存储优化 (4-bit codes,
  * group_size 128, an independent scale and bias per group):
- *   w[e,n,k] = scale[e,n,g] * q[e,n,k] + bias[e,n,g],  g = k / 128,
- *   q = the 4-bit code of element k: byte (e*N + n)*K/2 + k/2 holds element 2i
- *   in its low nibble and 2i+1 in its high nibble;
- *   sb[((e*N + n)*G + g)*2 + {0,1}] = (scale, bias) as bf16, G = K/128. */
+ *   w[e,n,k] = scale[e,n,g] * q[e,n,k] + bias[e,n,g],  g = k / 128.
+ * Storage (the library's layout, moe.h), rows in blocks of 32 (b = n / 32,
+ * r = n % 32):
+ *   q: the 1024-byte tile of (e, b, chunk k / 64) holds row r at byte 32 r as
+ *      8 32-bit words of 8 consecutive elements, byte j of a word holding
+ *      element j in its low nibble and j + 4 in its high nibble;
+ *   sb: the (scale, bias) bf16 pair of (e, b, g, r), pairs in that order. */
 static double w4_elem(const uint8_t* codes, const uint16_t* sb, int N, int K, size_t e, size_t n,
                       size_t k) {
-  const size_t row = e * (size_t)N + n;
-  const uint8_t byte = codes[(row * (size_t)K + k) / 2];
-  const int q = (k & 1) ? (byte >> 4) : (byte & 0xF);
-  const size_t g = row * (size_t)(K / 128) + k / 128;
-  const double scale = elem(sb, 1, 2 * g), bias = elem(sb, 1, 2 * g + 1);
+  const size_t blk = e * (size_t)(N / 32) + n / 32, r = n % 32, j = k % 8;
+  const uint8_t byte = codes[(blk * (size_t)(K / 64) + k / 64) * 1024 + r * 32 +
+                             4 * ((k % 64) / 8) + j % 4];
+  const int q = (j >= 4) ? (byte >> 4) : (byte & 0xF);
+  const size_t pair = (blk * (size_t)(K / 128) + k / 128) * 32 + r;
+  const double scale = elem(sb, 1, 2 * pair), bias = elem(sb, 1, 2 * pair + 1);
   return scale * (double)q + bias;
 }
 
 /* The dequantised matrices [E,N,K] as double. */
 int orc_dequant_w4(int E, int N, int K, const uint8_t* codes, const uint16_t* sb, double* w) {
-  if (E < 1 || N < 1 || K < 128 || K % 128 || !codes || !sb || !w) return -1;
+  if (E < 1 || N < 32 || N % 32 || K < 128 || K % 128 || !codes || !sb || !w) return -1;
 #pragma omp parallel for schedule(static)
   for (int e = 0; e < E; ++e)
     for (int n = 0; n < N; ++n)
@@ -401,13 +405,14 @@ int orc_dequant_w4(int E, int N, int K, const uint8_t* codes, const uint16_t* sb
 
 /* orc_expert_rows with 4-bit weights, dequantised element by element (the
  * same definition as orc_dequant_w4 followed by orc_expert_rows):
- *   gate/up codes [E,I,H/2] with sb [E,I,H/128,2]; down codes [E,H,I/2] with
- *   sb [E,H,I/128,2]; x [*,H] of dtype (0 fp32, 1 bf16). */
+ *   gate/up codes and (scale, bias) of N = I rows by K = H, down of N = H by
+ *   K = I, in the tiles of w4_elem; x [*,H] of dtype (0 fp32, 1 bf16). */
 int orc_expert_rows_w4(int H, int I, int dtype, const void* x, const uint8_t* cg,
                        const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
                        const uint8_t* cd, const uint16_t* sd, int n, const int32_t* tok,
                        const int32_t* ex, int round_h, double* y) {
   if (H < 128 || I < 128 || H % 128 || I % 128 || n < 0 || !x || !cg || !sg || !cu || !su ||
+      H % 32 || I % 32 ||
       !cd || !sd || !tok || !ex || !y)
     return -1;
   int bad = 0;

@@ -304,12 +304,14 @@ def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_b
 
 
 def dequant_w4(codes: np.ndarray, sb: np.ndarray) -> np.ndarray:
-    """codes uint8 [E,N,K/2], sb uint16 (bf16 bits) [E,N,K/128,2] -> float64 [E,N,K]."""
+    """codes uint8 [E,N/32,K/64,32,32], sb uint16 (bf16 bits) [E,N/32,K/128,32,2]
+    (the tiled layout of moe.h) -> float64 [E,N,K]."""
     codes = _c(codes, np.uint8)
     sb = _c(sb, np.uint16)
-    E, N, K2 = codes.shape
-    K = 2 * K2
-    assert sb.shape == (E, N, K // 128, 2)
+    E, NB, KC, r32, b32 = codes.shape
+    assert (r32, b32) == (32, 32)
+    N, K = 32 * NB, 64 * KC
+    assert sb.shape == (E, NB, K // 128, 32, 2)
     w = np.empty((E, N, K), np.float64)
     _check(_load().orc_dequant_w4(E, N, K, _p(codes), _p(sb), _p(w)), "dequant_w4")
     return w
@@ -321,7 +323,7 @@ def expert_rows_w4(x, w4: dict, tok, ex, round_h: bool = False) -> np.ndarray:
     x = _c(x)
     tok, ex = _c(tok, np.int32), _c(ex, np.int32)
     H = x.shape[1]
-    E, I, _ = w4["gate"].shape
+    E, I = w4["gate"].shape[0], 32 * w4["gate"].shape[1]
     arrs = [_c(w4[n], np.uint8 if "sb" not in n else np.uint16)
             for n in ("gate", "gate_sb", "up", "up_sb", "down", "down_sb")]
     n = tok.shape[0]

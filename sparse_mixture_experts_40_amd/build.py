@@ -14,8 +14,13 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc -O3 must not form packed fp32 ops by itself.
+# amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs. Kernels with one
+# wave per SIMD may use 512 registers, and with inline asm in them the compiler
+# otherwise picks the AGPR form, whose results then cost a v_accvgpr move per
+# element before any VALU use (the 4-bit fold reads every accumulator).
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-result", "-Wno-unused-function"]
 
 

@@ -829,7 +829,7 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
       pre = has_nxt;
       bq = bz + 1 == DecRing<1>::NBUF ? 0 : bz + 1;
     } else {
-      for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
+      for (int p0 = r0; p0 < r1; p0 += 32) {  // 32 token rows per pass
         tokens(p0, r1, cur);
         const int ntb = (r1 - p0) > 32 ? 2 : 1;
         f32x16_t acc[NB][2];
@@ -872,59 +872,50 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
 // ---- 4-bit weights, weight-streaming path --------------------------------
 //
 // [MOE-128x8] 参数量化与存储优化: 4-bit codes in groups of 128 along K with an
-// independent scale and bias per group, w = scale * q + bias. Work items,
-// token passes and the 4-way split-K are those of decode_gemm_bf16_kernel.
+// independent scale and bias per group, w = scale * q + bias. Work items and
+// the 4-way split-K are those of decode_gemm_bf16_kernel.
 // No weight is rounded: the MFMA multiplies the exact bf16 values 128 + q
-// (built from the codes with one byte permute and one OR per pair) with the
-// tokens, a second MFMA against ones gives the group's token sums, and each
-// group of 128 is folded into the fp32 accumulators as
+// with the tokens, a second MFMA against ones gives the group's token sums,
+// and each group of 128 is folded into the fp32 accumulators as
 //   sum_k w x = scale * sum_k (128 + q) x + (bias - 128 scale) * sum_k x.
 // The tokens are the A operand and the weights the B operand, so a lane's
 // accumulators belong to one weight row (lane & 31) and one (scale, bias)
 // per group. K is taken in chunks of 64: lane half h covers elements
-// [32h, 32h + 32) of a chunk, i.e. 16 bytes of codes, in 4 MFMA k steps of 8;
-// the token fragments are read in the same order. As in the bf16 kernel, each
-// wave streams its chunks through a ring of LDS buffers filled by LDS-DMA
-// (codes: 2 lanes per 32-byte row piece; tokens: 8 lanes per 128-byte line;
-// the (scale, bias) dword of every row), so loads coalesce and all waits are
-// explicit counts.
+// [32h, 32h + 32) of a chunk (16 bytes of codes) in 4 MFMA k steps of 8 and
+// reads its token fragments in the same order.
+//
+// One wave runs per SIMD, so every instruction takes an issue slot of its
+// own, and the loop is laid out to issue few:
+//  - 16 codes unpack with 13 VALU: two masks and one 64-bit shift give the
+//    nibbles as bytes, and each byte permute forms two bf16 values, taking
+//    their exponent byte from a constant register;
+//  - each wave streams its chunks through a ring of NBUF LDS buffers filled
+//    by LDS-DMA: a steady loop keeps D = NBUF - 1 chunks in flight, then the
+//    last D chunks run unrolled (entered part-way when the wave has fewer),
+//    so every wait count and fragment register set is a compile-time
+//    constant;
+//  - the (scale, bias) dwords of a group come with its first chunk only, and
+//    token rows only in the 8-row groups that exist (TG of them).
 
-// 8 codes (element 2i in the low nibble of byte i) -> the bf16 values 128 + q.
-__device__ __forceinline__ bf16x8_t w4_unpack8(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  // dword j = elements (2j, 2j+1): bytes (lo.j, 0, hi.j, 0) | 0x43004300
-  const uint4 r = make_uint4(__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u,
-                             __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u,
-                             __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u,
-                             __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u);
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-
-// The 4 k steps of one chunk into the group accumulators: aq += tokens x
-// (128 + q), ax += tokens x 1. FIRST: the chunk opens a group (the first k
-// step starts from zero accumulators).
-template <int NTB, bool FIRST>
-__device__ __forceinline__ void w4_chunk(const uint4 (&cw)[2], const bf16x8_t (&tf)[4][2],
-                                         f32x16_t (&aq)[2][NTB], f32x16_t (&ax)[NTB]) {
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
-                                                                0x3F803F80u, 0x3F803F80u));
-  const f32x16_t zero = {};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint32_t w = j == 0 ? cw[nb].x : j == 1 ? cw[nb].y : j == 2 ? cw[nb].z : cw[nb].w;
-      const bf16x8_t wq = w4_unpack8(w);
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-        aq[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            tf[j][tb], wq, (FIRST && j == 0) ? zero : aq[nb][tb], 0, 0, 0);
-    }
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-      ax[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][tb], ones,
-                                                       (FIRST && j == 0) ? zero : ax[tb], 0, 0, 0);
-  }
+// 16 codes -> the bf16 values 128 + q. Byte b of a 32-bit code word holds
+// element b of the word's 8 in its low nibble and element b + 4 in its high
+// nibble; w holds two words (elements 0..7 low, 8..15 high).
+__device__ __forceinline__ void w4_unpack16(uint64_t w, uint32_t c43, bf16x8_t& e0_7,
+                                            bf16x8_t& e8_15) {
+  constexpr uint64_t m = 0x0F0F0F0F0F0F0F0Full;
+  const uint64_t lo = w & m, hi = (w >> 4) & m;
+  const uint32_t l0 = (uint32_t)lo, l1 = (uint32_t)(lo >> 32);
+  const uint32_t h0 = (uint32_t)hi, h1 = (uint32_t)(hi >> 32);
+  // perm(c43, x, s): byte i is x's byte s_i for s_i < 4, else 0x43; so
+  // (x_a, 0x43, x_b, 0x43) is the bf16 pair (128 + x_a, 128 + x_b)
+  e0_7 = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_amdgcn_perm(c43, l0, 0x04010400u),
+                                                 __builtin_amdgcn_perm(c43, l0, 0x04030402u),
+                                                 __builtin_amdgcn_perm(c43, h0, 0x04010400u),
+                                                 __builtin_amdgcn_perm(c43, h0, 0x04030402u)));
+  e8_15 = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_amdgcn_perm(c43, l1, 0x04010400u),
+                                                  __builtin_amdgcn_perm(c43, l1, 0x04030402u),
+                                                  __builtin_amdgcn_perm(c43, h1, 0x04010400u),
+                                                  __builtin_amdgcn_perm(c43, h1, 0x04030402u)));
 }
 
 // One LDS-DMA instruction of 4 bytes per lane: lane l's dword at
@@ -937,149 +928,217 @@ __device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t m0, uint32_t voff, u
 }
 #pragma clang diagnostic pop
 
-// Ring geometry of the 4-bit kernel, per chunk of 64 K elements (bytes): the
-// codes of the 64 weight rows (32 bytes each, 16-byte piece p of row r at
-// p ^ ((r >> 3) & 1)), the (scale, bias) dwords of rows 0..31 and 32..63
-// (256 bytes each, lane l's slot holding row l & 31 of its half), and 32 NTB
-// token rows of 128 bytes (chunk c of row t at c ^ swz_f<64>(t)).
-template <int NTB>
-struct W4Ring {
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Ring geometry for NTB token blocks of 32 rows with TG 8-row token groups
+// loaded. One buffer (bytes): the codes of the 64 weight rows (32 bytes
+// each, 16-byte piece p of row r at p ^ ((r >> 3) & 1)), the (scale, bias)
+// dwords of rows 0..31 and 32..63 (256 bytes each, lane l's slot holding row
+// l & 31 of its half), and 8 TG token rows of 128 bytes (chunk c of row t at
+// c ^ swz_f<64>(t)).
+template <int NTB, int TG>
+struct W4Cfg {
   static constexpr int CODE = 0, SB = 2048, TOK = 2560;
-  static constexpr int BUF = TOK + 32 * NTB * 128;
-  static constexpr int NBUF = (2 * kDecRegion) / BUF < 4 ? (2 * kDecRegion) / BUF : 4;
-  static constexpr int NL = 2 + 2 + 4 * NTB;  // DMA instructions per chunk
-  static_assert(NBUF >= 3 && NL * (NBUF - 1) <= 32, "ring depth (reads one chunk ahead)");
+  static constexpr int BUF = TOK + TG * 1024;
+  static constexpr int NLE = 4 + TG;  // DMA instructions of a group's first chunk
+  static constexpr int NLO = 2 + TG;  // and of its second
+  static constexpr int FIT = (2 * kDecRegion) / BUF < 9 ? (2 * kDecRegion) / BUF : 9;
+  static constexpr int NBUF = FIT % 2 ? FIT : FIT - 1;  // odd, so D is even
+  static constexpr int D = NBUF - 1;
+  // DMA instructions of n consecutive chunks, the first of them a group's
+  // first chunk (even) or second
+  static constexpr int run(bool even, int n) {
+    int s = 0;
+    for (int i = 0; i < n; ++i) s += ((i % 2 == 0) == even) ? NLE : NLO;
+    return s;
+  }
+  static_assert(D >= 2 && run(true, D - 1) <= 32, "ring depth and vmcnt range");
+  static_assert(8 * TG >= 32 * (NTB - 1) + 1 && 8 * TG <= 32 * NTB, "token groups");
+  // fragment reads cover 32 NTB token rows: rows past 8 TG read stale bytes of
+  // the wave's own region (they only reach output rows that are never stored)
+  static_assert((NBUF - 1) * BUF + TOK + 32 * NTB * 128 <= 2 * kDecRegion, "reads stay in the region");
 };
 
-// s_waitcnt vmcnt(NL * r), r in [0, NBUF - 1) wave-uniform.
-template <int NL, int NBUF>
-__device__ __forceinline__ void wait_chunks(int r) {
-  if (NBUF > 3 && r >= 2) wait_vmcnt(2 * NL);
-  else if (NBUF > 2 && r >= 1) wait_vmcnt(NL);
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// LDS-DMA of chunk ch of this wave's K range into the buffer at LDS byte
-// address dst (codes from rq0 / rq1, scale-bias dwords from rs0 / rs1).
 template <int NTB>
-__device__ __forceinline__ void w4_dma(uint32_t dst, i32x4_t rq0, i32x4_t rq1, i32x4_t rs0,
-                                       i32x4_t rs1, i32x4_t ract, const uint32_t (&q_off)[2],
-                                       const uint32_t (&s_off)[2], const uint32_t (&t_off)[8],
-                                       int ch) {
-  using R = W4Ring<NTB>;
-  dma16(rq0, dst + R::CODE, q_off[0], ch * 32u);
-  dma16(rq1, dst + R::CODE + 1024, q_off[1], ch * 32u);
-  dma4(rs0, dst + R::SB, s_off[0], (ch >> 1) * 4u);
-  dma4(rs1, dst + R::SB + 256, s_off[1], (ch >> 1) * 4u);
-#pragma unroll
-  for (int j = 0; j < 4 * NTB; ++j) dma16(ract, dst + R::TOK + j * 1024, t_off[j], ch * 128u);
-}
+struct W4Frag {
+  uint4 cw[2];            // codes of the lane's rows in weight blocks 0, 1
+  bf16x8_t tf[4][NTB];    // token fragments of the 4 k steps
+};
 
-// Fragments of the chunk in buffer src (LDS bytes): this lane's codes of its
-// two weight rows and the token fragments of the 4 k steps.
-template <int NTB>
-__device__ __forceinline__ void w4_frag(const uint8_t* src, int lane, uint4 (&cw)[2],
-                                        bf16x8_t (&tf)[4][2]) {
-  using R = W4Ring<NTB>;
-  const int n = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-    cw[nb] = *reinterpret_cast<const uint4*>(src + R::CODE + (nb * 32 + n) * 32 +
-                                             ((h ^ ((n >> 3) & 1)) * 16));
-  const int sw = swz_f<64>(n);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-      tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(src + R::TOK + (tb * 32 + n) * 128 +
-                                                     (((4 * h + j) ^ sw) * 16));
-}
-
-// Fold of one group of 128 (two chunks) into acc with the (scale, bias) of
-// this lane's weight rows, read from buffer src.
-template <int NTB>
-__device__ __forceinline__ void w4_fold(const uint8_t* src, int lane, const f32x16_t (&aq)[2][NTB],
-                                        const f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) {
-  using R = W4Ring<NTB>;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(src + R::SB + nb * 256 + (lane & 31) * 4);
-    const float scale = __uint_as_float(sbw << 16);
-    const float bias2 = fmaf(-128.0f, scale, __uint_as_float(sbw & 0xFFFF0000u));
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc[nb][tb][r] = fmaf(scale, aq[nb][tb][r], fmaf(bias2, ax[tb][r], acc[nb][tb][r]));
-  }
-}
-
-// The ring state of one wave's K loop.
-template <int NTB>
-struct W4Stream {
-  const uint8_t* ring;
-  uint32_t ring_lds;
+// One wave's K loop over its nch chunks (an even number, two per group).
+template <int NTB, int TG>
+struct W4Loop {
+  using C = W4Cfg<NTB, TG>;
+  const uint8_t* ring;  // the wave's LDS region, for the fragment reads
+  uint32_t ring_lds;    // its LDS byte address, for the DMA
   i32x4_t rq0, rq1, rs0, rs1, ract;
   const uint32_t (&q_off)[2];
   const uint32_t (&s_off)[2];
-  const uint32_t (&t_off)[8];
-  int nch, lane;
+  const uint32_t (&t_off)[4];
+  int lane;
+  uint32_t c43;
 
-  __device__ __forceinline__ void dma(int ch, int buf) const {
-    w4_dma<NTB>(ring_lds + buf * W4Ring<NTB>::BUF, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off,
-                ch);
-  }
-  // Chunk ch (in buffer bi): start the loads of chunk ch + NBUF - 1, wait for
-  // chunk ch + 1 and read its fragments into the other set (nc, nt) while
-  // chunk ch is multiplied from (cc, ct); FIRST opens a group, otherwise the
-  // group is folded into acc.
-  template <bool FIRST>
-  __device__ __forceinline__ void step(int ch, int bi, const uint4 (&cc)[2],
-                                       const bf16x8_t (&ct)[4][2], uint4 (&nc)[2],
-                                       bf16x8_t (&nt)[4][2], f32x16_t (&aq)[2][NTB],
-                                       f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) const {
-    constexpr int NBUF = W4Ring<NTB>::NBUF, NL = W4Ring<NTB>::NL;
-    // the buffer loaded next held chunk ch - 1, whose reads are complete
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int gl = ch + NBUF - 1;
-    if (gl < nch) dma(gl, (bi + NBUF - 1) % NBUF);
-    if (ch + 1 < nch) {
-      wait_chunks<NL, NBUF>((gl < nch ? gl : nch - 1) - (ch + 1));
-      w4_frag<NTB>(ring + ((bi + 1) % NBUF) * W4Ring<NTB>::BUF, lane, nc, nt);
+  // LDS-DMA of chunk ch into buffer b; EVEN: ch opens its group and also
+  // brings the group's (scale, bias) dwords.
+  template <bool EVEN>
+  __device__ __forceinline__ void dma(int ch, int b) const {
+    const uint32_t dst = ring_lds + (uint32_t)b * C::BUF;
+    dma16(rq0, dst + C::CODE, q_off[0], (uint32_t)ch * 1024u);
+    dma16(rq1, dst + C::CODE + 1024, q_off[1], (uint32_t)ch * 1024u);
+    if constexpr (EVEN) {
+      dma4(rs0, dst + C::SB, s_off[0], (uint32_t)(ch >> 1) * 128u);
+      dma4(rs1, dst + C::SB + 256, s_off[1], (uint32_t)(ch >> 1) * 128u);
     }
-    w4_chunk<NTB, FIRST>(cc, ct, aq, ax);
-    if (!FIRST) w4_fold<NTB>(ring + bi * W4Ring<NTB>::BUF, lane, aq, ax, acc);
+#pragma unroll
+    for (int j = 0; j < TG; ++j) dma16(ract, dst + C::TOK + j * 1024, t_off[j], (uint32_t)ch * 128u);
+  }
+
+  __device__ __forceinline__ void frag(int b, W4Frag<NTB>& f) const {
+    const uint8_t* src = ring + b * C::BUF;
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      f.cw[nb] = *reinterpret_cast<const uint4*>(src + C::CODE + (nb * 32 + n) * 32 +
+                                                 ((h ^ ((n >> 3) & 1)) * 16));
+    const int sw = swz_f<64>(n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        f.tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(src + C::TOK + (tb * 32 + n) * 128 +
+                                                         (((4 * h + j) ^ sw) * 16));
+  }
+
+  __device__ __forceinline__ void sb(int b, uint32_t (&v)[2]) const {
+    const uint8_t* src = ring + b * C::BUF + C::SB + (lane & 31) * 4;
+    v[0] = *reinterpret_cast<const uint32_t*>(src);
+    v[1] = *reinterpret_cast<const uint32_t*>(src + 256);
+  }
+
+  // aq += tokens x (128 + q), ax += tokens x 1 over the 4 k steps of a chunk;
+  // FIRST: the chunk opens a group (the first k step starts from zero).
+  template <bool FIRST>
+  __device__ __forceinline__ void mult(const W4Frag<NTB>& f, f32x16_t (&aq)[2][NTB],
+                                       f32x16_t (&ax)[NTB]) const {
+    const bf16x8_t ones = __builtin_bit_cast(
+        bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const f32x16_t zero = {};
+    bf16x8_t wq[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      w4_unpack16(((uint64_t)f.cw[nb].y << 32) | f.cw[nb].x, c43, wq[nb][0], wq[nb][1]);
+      w4_unpack16(((uint64_t)f.cw[nb].w << 32) | f.cw[nb].z, c43, wq[nb][2], wq[nb][3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          aq[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              f.tf[j][tb], wq[nb][j], (FIRST && j == 0) ? zero : aq[nb][tb], 0, 0, 0);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        ax[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.tf[j][tb], ones,
+                                                         (FIRST && j == 0) ? zero : ax[tb], 0, 0,
+                                                         0);
+    }
+  }
+
+  // acc += scale aq + (bias - 128 scale) ax with this lane's rows' (scale,
+  // bias) dwords (bf16 scale in the low half, bias in the high half).
+  __device__ __forceinline__ void fold(const uint32_t (&sbv)[2], const f32x16_t (&aq)[2][NTB],
+                                       const f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float scale = __uint_as_float(sbv[nb] << 16);
+      const float bias2 = fmaf(-128.0f, scale, __uint_as_float(sbv[nb] & 0xFFFF0000u));
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[nb][tb][r] = fmaf(scale, aq[nb][tb][r], fmaf(bias2, ax[tb][r], acc[nb][tb][r]));
+    }
+  }
+
+  // Chunk ch, in buffer b (EVEN: it opens a group): (ISSUE) start the loads
+  // of chunk ch + D into the buffer of chunk ch - 1, whose reads have
+  // completed; (WAITN >= 0) wait until chunk ch + 1 has landed, WAITN DMA
+  // instructions of later chunks still in flight, and read its fragments;
+  // multiply chunk ch; when ch closes its group, fold it and read the next
+  // group's (scale, bias) (the fold has consumed the previous ones).
+  template <bool EVEN, bool ISSUE, int WAITN>
+  __device__ __forceinline__ void step(int ch, int b, const W4Frag<NTB>& cur, W4Frag<NTB>& nxt,
+                                       uint32_t (&sbv)[2], f32x16_t (&aq)[2][NTB],
+                                       f32x16_t (&ax)[NTB], f32x16_t (&acc)[2][NTB]) const {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int bn = b + 1 == C::NBUF ? 0 : b + 1;
+    if constexpr (ISSUE) dma<EVEN>(ch + C::D, b == 0 ? C::NBUF - 1 : b - 1);
+    if constexpr (WAITN >= 0) {
+      wait_vm<WAITN>();
+      frag(bn, nxt);
+    }
+    mult<EVEN>(cur, aq, ax);
+    if constexpr (!EVEN) {
+      fold(sbv, aq, ax, acc);
+      if constexpr (WAITN >= 0) sb(bn, sbv);
+    }
+  }
+
+  // The last chunks, R of them left at the step (chunk nch - R, whose
+  // fragments are in fA when R is even, else in fB); entered at R = r0.
+  template <int R>
+  __device__ __forceinline__ void drain(int r0, int nch, int& b, W4Frag<NTB>& fA,
+                                        W4Frag<NTB>& fB, uint32_t (&sbv)[2],
+                                        f32x16_t (&aq)[2][NTB], f32x16_t (&ax)[NTB],
+                                        f32x16_t (&acc)[2][NTB]) const {
+    if constexpr (R > 0) {
+      if (r0 >= R) {
+        constexpr bool EVEN = R % 2 == 0;
+        if constexpr (EVEN)
+          step<true, false, (R > 1 ? C::run(true, R - 2) : -1)>(nch - R, b, fA, fB, sbv, aq, ax,
+                                                                 acc);
+        else
+          step<false, false, (R > 1 ? C::run(false, R - 2) : -1)>(nch - R, b, fB, fA, sbv, aq,
+                                                                   ax, acc);
+        b = b + 1 == C::NBUF ? 0 : b + 1;
+      }
+      drain<R - 1>(r0, nch, b, fA, fB, sbv, aq, ax, acc);
+    }
+  }
+
+  __device__ __forceinline__ void run_k(int nch, f32x16_t (&acc)[2][NTB]) const {
+    const int n0 = nch < C::D ? nch : C::D;  // chunks loaded ahead
+#pragma unroll
+    for (int c = 0; c < C::D; ++c)
+      if (c < n0) {
+        if (c % 2 == 0)
+          dma<true>(c, c);
+        else
+          dma<false>(c, c);
+      }
+    // chunk 0 has landed once the loads of chunks 1 .. n0-1 are all that remain
+    wait_vmcnt((n0 / 2) * C::NLO + ((n0 - 1) / 2) * C::NLE);
+    W4Frag<NTB> fA, fB;
+    uint32_t sbv[2];
+    frag(0, fA);
+    sb(0, sbv);
+    f32x16_t aq[2][NTB], ax[NTB];
+    int b = 0;
+    for (int ch = 0; ch < nch - C::D; ch += 2) {
+      step<true, true, C::run(true, C::D - 1)>(ch, b, fA, fB, sbv, aq, ax, acc);
+      b = b + 1 == C::NBUF ? 0 : b + 1;
+      step<false, true, C::run(false, C::D - 1)>(ch + 1, b, fB, fA, sbv, aq, ax, acc);
+      b = b + 1 == C::NBUF ? 0 : b + 1;
+    }
+    drain<C::D>(n0, nch, b, fA, fB, sbv, aq, ax, acc);
   }
 };
-
-// This wave's nch chunks (an even number: two per group of 128) through its
-// ring; ring is the byte pointer of the wave's LDS region, ring_lds its LDS
-// address.
-template <int NTB>
-__device__ __forceinline__ void w4_kloop(int nch, const uint8_t* ring, uint32_t ring_lds,
-                                         i32x4_t rq0, i32x4_t rq1, i32x4_t rs0, i32x4_t rs1,
-                                         i32x4_t ract, const uint32_t (&q_off)[2],
-                                         const uint32_t (&s_off)[2], const uint32_t (&t_off)[8],
-                                         int lane, f32x16_t (&acc)[2][NTB]) {
-  constexpr int NBUF = W4Ring<NTB>::NBUF, NL = W4Ring<NTB>::NL;
-  const W4Stream<NTB> st{ring, ring_lds, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off, nch,
-                         lane};
-#pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j)
-    if (j < nch) st.dma(j, j);
-  wait_chunks<NL, NBUF>((NBUF - 2 < nch - 1 ? NBUF - 2 : nch - 1));  // chunk 0 has landed
-  uint4 c0[2], c1[2];
-  bf16x8_t t0[4][2], t1[4][2];
-  w4_frag<NTB>(ring, lane, c0, t0);
-  f32x16_t aq[2][NTB], ax[NTB];
-  int bi = 0;  // buffer of the even chunk
-  for (int ch = 0; ch < nch; ch += 2) {
-    st.template step<true>(ch, bi, c0, t0, c1, t1, aq, ax, acc);
-    const int bo = bi + 1 == NBUF ? 0 : bi + 1;
-    st.template step<false>(ch + 1, bo, c1, t1, c0, t0, aq, ax, acc);
-    bi = bo + 1 == NBUF ? 0 : bo + 1;
-  }
-}
 
 // Split-K reduction and epilogue for accumulators in the tokens-x-weights
 // orientation: (r, lane) of block (nb, tb) holds token row
@@ -1169,7 +1228,9 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
   uint8_t* ring = s_ring + wave * 2 * kDecRegion;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
   float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kDecRegion / 2
-  const i32x4_t ract = dec_rsrc(act, act_bytes);
+  i32x4_t ract = dec_rsrc(act, act_bytes);
+  asm volatile("" : "+s"(ract));
+  const uint32_t c43 = 0x43434343u;
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int rank = it / n_chunks, c = __builtin_amdgcn_readfirstlane(it - rank * n_chunks);
@@ -1180,33 +1241,34 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
     }
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
-    // weight rows of the item (gate/up: rows [32c, 32c + 32) of both matrices;
-    // down: rows [64c, 64c + 64)); rows past N_out are clamped to the last one
-    const int nrow0 = GATEUP ? c * 32 : c * 64;
-    const int nrows = min(GATEUP ? 32 : 64, N_out - nrow0);
-    const size_t row0 = (size_t)e * N_out + nrow0;
-    const i32x4_t rq0 = dec_rsrc(q0 + row0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2));
-    const i32x4_t rq1 =
-        GATEUP ? dec_rsrc(q1 + row0 * (K / 2), (uint32_t)nrows * (uint32_t)(K / 2)) : rq0;
-    const i32x4_t rs0 = dec_rsrc(sb0 + row0 * G * 2, (uint32_t)nrows * (uint32_t)G * 4u);
-    const i32x4_t rs1 =
-        GATEUP ? dec_rsrc(sb1 + row0 * G * 2, (uint32_t)nrows * (uint32_t)G * 4u) : rs0;
-    uint32_t q_off[2], s_off[2];
+    // weight rows of the item: gate/up rows [32c, 32c + 32) of both matrices,
+    // down rows [64c, 64c + 64): 32-row blocks rb0 and rb1 of the codes and
+    // (scale, bias) tiles (N_out is a multiple of 512)
+    const int rb0 = GATEUP ? c : 2 * c, rb1 = GATEUP ? c : 2 * c + 1;
+    const size_t blk0 = (size_t)e * (N_out / 32) + rb0, blk1 = (size_t)e * (N_out / 32) + rb1;
+    const uint32_t qbytes = (uint32_t)K * 16u, sbytes = (uint32_t)G * 128u;  // per block
+    i32x4_t rq0 = dec_rsrc(q0 + blk0 * qbytes, qbytes);
+    i32x4_t rq1 = dec_rsrc((GATEUP ? q1 : q0) + blk1 * qbytes, qbytes);
+    i32x4_t rs0 = dec_rsrc(reinterpret_cast<const uint8_t*>(sb0) + blk0 * sbytes, sbytes);
+    i32x4_t rs1 = dec_rsrc(reinterpret_cast<const uint8_t*>(GATEUP ? sb1 : sb0) + blk1 * sbytes,
+                           sbytes);
+    // opaque to the compiler from here on: each descriptor stays one aligned
+    // SGPR quad instead of being reassembled from shared fields at every load
+    asm volatile("" : "+s"(rq0), "+s"(rq1), "+s"(rs0), "+s"(rs1));
+    // lane l of a code DMA fills LDS row l / 2 (its slot l % 2 holding piece
+    // (l % 2) ^ ((row >> 3) & 1)) from the 1 KB tile of the chunk; the
+    // (scale, bias) DMA gives lane l row l % 32 of the group's 128 bytes
+    const int qr = lane >> 1;
+    const uint32_t q_lane = (uint32_t)(qr * 32 + (((lane & 1) ^ ((qr >> 3) & 1)) * 16)) +
+                            (uint32_t)(wave * nch) * 1024u;
+    const uint32_t q_off[2] = {q_lane, q_lane};
+    const uint32_t s_lane = (uint32_t)((lane & 31) * 4) + (uint32_t)(wave * (nch / 2)) * 128u;
+    const uint32_t s_off[2] = {s_lane, s_lane};
+    for (int p0 = r0; p0 < r1; p0 += 32) {  // 32 token rows per pass
+      const int rows = min(r1 - p0, 32);
+      uint32_t t_off[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 32 * i + (lane >> 1);  // LDS code row: 32 nb + row inside the block
-      int nl = GATEUP ? (r & 31) : r;
-      nl = nl < nrows ? nl : nrows - 1;
-      q_off[i] = (uint32_t)nl * (uint32_t)(K / 2) + (uint32_t)(wave * kw / 2) +
-                 (uint32_t)(((lane & 1) ^ ((r >> 3) & 1)) * 16);
-      int ns = (GATEUP || i == 0) ? (lane & 31) : 32 + (lane & 31);
-      ns = ns < nrows ? ns : nrows - 1;
-      s_off[i] = ((uint32_t)ns * (uint32_t)G + (uint32_t)(wave * kw / 128)) * 4u;
-    }
-    for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
-      uint32_t t_off[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int t = 8 * j + (lane >> 3);  // token row of the pass
         int gi = p0 + t;
         gi = gi < r1 ? gi : r1 - 1;
@@ -1214,10 +1276,9 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
         t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
                     (uint32_t)(((lane & 7) ^ swz_f<64>(t)) * 8)) * 2u;
       }
-      const int ntb = (r1 - p0) > 32 ? 2 : 1;
-      // one pass with NT token blocks (accumulators sized for them)
-      auto pass = [&](auto ntb_c) {
-        constexpr int NT = decltype(ntb_c)::value;
+      // one pass with TG token groups of 8 rows loaded
+      auto pass = [&](auto tg_c) {
+        constexpr int NT = 1, TG = decltype(tg_c)::value;
         f32x16_t acc[NB][NT];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -1225,14 +1286,19 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
           for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[nb][tb][r] = 0.0f;
-        w4_kloop<NT>(nch, ring, ring_lds, rq0, rq1, rs0, rs1, ract, q_off, s_off, t_off, lane,
-                     acc);
+        const W4Loop<NT, TG> lp{ring, ring_lds, rq0, rq1, rs0, rs1, ract,
+                                q_off, s_off, t_off, lane, c43};
+        lp.run_k(nch, acc);
         // every ring buffer of this wave has landed and been read: its
         // partial sums may overwrite its ring
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        w4_epilogue<GATEUP, NB, NT, kDecRegion / 2>(acc, s_part, p0, r1, ntb, c, N_out, out);
+        w4_epilogue<GATEUP, NB, NT, kDecRegion / 2>(acc, s_part, p0, r1, NT, c, N_out, out);
       };
-      if (ntb > 1)
+      if (rows > 24)
+        pass(std::integral_constant<int, 4>{});
+      else if (rows > 16)
+        pass(std::integral_constant<int, 3>{});
+      else if (rows > 8)
         pass(std::integral_constant<int, 2>{});
       else
         pass(std::integral_constant<int, 1>{});

@@ -155,18 +155,22 @@ def uniform_bytes(shape, seed: int, tensor_id: int) -> np.ndarray:
 
 
 def make_w4_inputs(cfg: MoEConfig, seed: int | None = None) -> dict:
-    """4-bit expert weights: gate/up codes uint8 [E,I,H/2], down [E,H,I/2]
-    (element 2i in the low nibble of byte i), and *_sb uint16 bf16 bits
-    [E,N,K/128,2] = (scale, bias) per group of 128 consecutive K."""
+    """4-bit expert weights in the tiled layout of moe.h: codes uint8
+    [E,N/32,K/64,32,32] (gate/up N = I, K = H; down N = H, K = I) and *_sb
+    uint16 bf16 bits [E,N/32,K/128,32,2] = (scale, bias) per row and group of
+    128 consecutive K. The codes are uniform random bytes."""
     seed = cfg.seed if seed is None else seed
     H, E, I = cfg.H, cfg.E, cfg.I
     d = {}
     for name, N, K in (("gate", I, H), ("up", I, H), ("down", H, I)):
-        d[name] = uniform_bytes((E, N, K // 2), seed, TENSOR_IDS[name + "_q"])
+        d[name] = uniform_bytes((E, N, K // 2), seed, TENSOR_IDS[name + "_q"]).reshape(
+            E, N // 32, K // 64, 32, 32)
         G = K // 128
         n1 = normal_tensor((E, N, G), seed, TENSOR_IDS[name + "_s"], 1.0, False)
         n2 = normal_tensor((E, N, G), seed, TENSOR_IDS[name + "_b"], 1.0, False)
         scale = (np.abs(1.0 + 0.2 * n1) / (4.6 * math.sqrt(K))).astype(np.float32)
         bias = (-scale * (7.5 + 0.5 * n2)).astype(np.float32)
-        d[name + "_sb"] = np.stack([bf16_bits(scale), bf16_bits(bias)], axis=-1)
+        sbn = np.stack([bf16_bits(scale), bf16_bits(bias)], axis=-1)  # [E,N,G,2]
+        d[name + "_sb"] = np.ascontiguousarray(
+            sbn.reshape(E, N // 32, 32, G, 2).transpose(0, 1, 3, 2, 4))
     return d

@@ -18,12 +18,18 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-W4_SHAPES = [  # (T, H, E, k, I): H and I multiples of 512
+# (T, H, E, k, I): H and I multiples of 512. The shapes cover K/256 chunks
+# per wave of 2 to 16 (fewer than, as many as and more than the ring keeps in
+# flight) and 1 to 75 rows per expert (each count of 8-row token groups, and
+# several 32-row passes).
+W4_SHAPES = [
     (40, 512, 16, 4, 512),
     (7, 1024, 64, 8, 512),
     (64, 512, 8, 2, 1536),
     (300, 512, 32, 8, 512),
     (1, 2048, 4, 1, 1024),
+    (40, 1024, 8, 4, 1024),
+    (100, 4096, 16, 4, 512),
 ]
 
 
@@ -88,7 +94,7 @@ def test_layer_forward_w4(orc, cfg):
 
 
 def test_w4_hot_expert_multi_pass(orc):
-    """An expert with more than 64 rows: several token passes over the same codes."""
+    """An expert with more than 32 rows: several token passes over the same codes."""
     cfg = MoEConfig("hot_w4", T=150, H=512, E=8, k=1, I=512, norm=False, dtype="bf16")
     inp = make_inputs(cfg, seed=6, weights=False)
     bias = np.zeros(cfg.E, np.float32)
