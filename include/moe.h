@@ -284,7 +284,7 @@ moe_status moe_expert_down(const moe_config* cfg, const void* h, const int32_t* 
  * and each group of 128 is folded in fp32 as
  *   scale * sum (128 + q) x + (bias - 128 scale) * sum x.
  * They are built for few rows per expert (decode batches) and are correct for
- * any number of rows (each 64 rows of an expert stream its codes once more). */
+ * any number of rows (each 32 rows of an expert stream its codes once more). */
 moe_status moe_expert_gate_up_w4(const moe_config* cfg, const void* x,
                                  const int32_t* sorted_pair, const int32_t* expert_offsets,
                                  const moe_w4_weights* w, void* h, hipStream_t stream);

@@ -829,7 +829,7 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
       pre = has_nxt;
       bq = bz + 1 == DecRing<1>::NBUF ? 0 : bz + 1;
     } else {
-      for (int p0 = r0; p0 < r1; p0 += 32) {  // 32 token rows per pass
+      for (int p0 = r0; p0 < r1; p0 += 64) {  // 64 token rows per pass
         tokens(p0, r1, cur);
         const int ntb = (r1 - p0) > 32 ? 2 : 1;
         f32x16_t acc[NB][2];
@@ -1140,57 +1140,38 @@ struct W4Loop {
   }
 };
 
-// Split-K reduction and epilogue for accumulators in the tokens-x-weights
-// orientation: (r, lane) of block (nb, tb) holds token row
-// (r / 4) * 8 + (lane / 32) * 4 + r % 4 and weight row lane & 31. Wave w's
-// partial sums sit at s_part + w * WST, [nb][tb][r][lane].
-template <bool GATEUP, int NB, int NTB, int WST>
-__device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[NB][NTB], float* s_part, int p0,
-                                            int r1, int ntb, int c, int N_out,
-                                            void* __restrict__ out) {
+// Split-K reduction and stores of one pass of nr <= 8 TG token rows, for
+// accumulators in the tokens-x-weights orientation: register r of block nb
+// holds token row (r / 4) * 8 + (lane / 32) * 4 + r % 4 and weight row
+// lane & 31, so only registers r < 4 TG hold rows of the pass. Each wave
+// writes those to its slab s_part + w * WST ([nb][r][lane]); then every
+// thread takes whole outputs (gate/up: nr rows x 32 columns of h; down: nr
+// rows x 64 columns of y), adding the four waves' partial sums in wave order.
+template <bool GATEUP, int TG, int WST>
+__device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[2][1], float* s_part, int p0,
+                                            int nr, int c, int N_out, void* __restrict__ out) {
+  constexpr int NR = 4 * TG;  // registers holding rows of the pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto part = [&](int w, int nb, int tb, int r, int ln) -> float& {
-    return s_part[w * WST + ((nb * 2 + tb) * 16 + r) * 64 + ln];
-  };
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part(wave, nb, tb, r, lane) = acc[nb][tb][r];
+    for (int r = 0; r < NR; ++r) s_part[wave * WST + (nb * NR + r) * 64 + lane] = acc[nb][0][r];
   __syncthreads();
-  {
-    const int tb = (tid >> 6) & 1, half = tid >> 7;  // thread: (tb, token m, half of columns)
-    const int m = lane & 31, row = p0 + tb * 32 + m;
-    const int r_m = (m >> 3) * 4 + (m & 3), l_m = ((m >> 2) & 1) * 32;  // where token m sits
-    if (tb < ntb && row < r1) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int n_in = (lane >> 5) * 16 + half * 8 + qq * 2;  // 2 columns of a 32-block
-        float v[NB][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int ln = l_m + n_in + j;
-            v[nb][j] = ((part(0, nb, tb, r_m, ln) + part(1, nb, tb, r_m, ln)) +
-                        part(2, nb, tb, r_m, ln)) + part(3, nb, tb, r_m, ln);
-          }
-        if (GATEUP) {
-          const int col = c * 32 + n_in;
-          if (col < N_out)
-            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (size_t)row * N_out + col) =
-                pack_bf16x2(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1]);
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int col = c * 64 + nb * 32 + n_in;
-            if (col < N_out)
-              *reinterpret_cast<float2*>(static_cast<float*>(out) + (size_t)row * N_out + col) =
-                  make_float2(v[nb][0], v[nb][1]);
-          }
-        }
-      }
+  constexpr int NC = GATEUP ? 32 : 64;  // output columns of the item
+  for (int o = tid; o < nr * NC; o += 256) {
+    const int m = o / NC, col = o % NC, nb = GATEUP ? 0 : col >> 5, n = col & 31;
+    // token m sits in register (m / 8) * 4 + m % 4 of lane half (m / 4) % 2
+    const int at = (nb * NR + (m >> 3) * 4 + (m & 3)) * 64 + ((m >> 2) & 1) * 32 + n;
+    auto sum = [&](int off) {
+      return ((s_part[at + off] + s_part[WST + at + off]) + s_part[2 * WST + at + off]) +
+             s_part[3 * WST + at + off];
+    };
+    const size_t row = (size_t)(p0 + m);
+    if (GATEUP) {
+      const float g = sum(0), u = sum(NR * 64);
+      static_cast<uint16_t*>(out)[row * N_out + c * 32 + n] = f32_to_bf16(silu(g) * u);
+    } else {
+      static_cast<float*>(out)[row * N_out + c * 64 + col] = sum(0);
     }
   }
 }
@@ -1292,7 +1273,7 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
         // every ring buffer of this wave has landed and been read: its
         // partial sums may overwrite its ring
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        w4_epilogue<GATEUP, NB, NT, kDecRegion / 2>(acc, s_part, p0, r1, NT, c, N_out, out);
+        w4_epilogue<GATEUP, TG, kDecRegion / 2>(acc, s_part, p0, rows, c, N_out, out);
       };
       if (rows > 24)
         pass(std::integral_constant<int, 4>{});
