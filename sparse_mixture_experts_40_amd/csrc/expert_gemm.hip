@@ -941,13 +941,25 @@ __device__ __forceinline__ void wait_vm() {
 // dwords of rows 0..31 and 32..63 (256 bytes each, lane l's slot holding row
 // l & 31 of its half), and 8 TG token rows of 128 bytes (chunk c of row t at
 // c ^ swz_f<64>(t)).
+// LDS per wave of the 4-bit kernel (bytes) and token rows per pass: two
+// 4-wave blocks share a CU (two waves per SIMD), so one wave's VALU work
+// overlaps the other's MFMAs, loads and waits.
+#ifndef MOE_W4_REGION
+#define MOE_W4_REGION 19456
+#endif
+#ifndef MOE_W4_ROWS
+#define MOE_W4_ROWS 24
+#endif
+constexpr int kW4Region = MOE_W4_REGION, kW4Rows = MOE_W4_ROWS;
+static_assert(kW4Rows % 8 == 0 && kW4Rows <= 32, "rows per pass");
+
 template <int NTB, int TG>
 struct W4Cfg {
   static constexpr int CODE = 0, SB = 2048, TOK = 2560;
   static constexpr int BUF = TOK + TG * 1024;
   static constexpr int NLE = 4 + TG;  // DMA instructions of a group's first chunk
   static constexpr int NLO = 2 + TG;  // and of its second
-  static constexpr int FIT = (2 * kDecRegion) / BUF < 9 ? (2 * kDecRegion) / BUF : 9;
+  static constexpr int FIT = kW4Region / BUF < 9 ? kW4Region / BUF : 9;
   static constexpr int NBUF = FIT % 2 ? FIT : FIT - 1;  // odd, so D is even
   static constexpr int D = NBUF - 1;
   // DMA instructions of n consecutive chunks, the first of them a group's
@@ -959,9 +971,7 @@ struct W4Cfg {
   }
   static_assert(D >= 2 && run(true, D - 1) <= 32, "ring depth and vmcnt range");
   static_assert(8 * TG >= 32 * (NTB - 1) + 1 && 8 * TG <= 32 * NTB, "token groups");
-  // fragment reads cover 32 NTB token rows: rows past 8 TG read stale bytes of
-  // the wave's own region (they only reach output rows that are never stored)
-  static_assert((NBUF - 1) * BUF + TOK + 32 * NTB * 128 <= 2 * kDecRegion, "reads stay in the region");
+  static_assert(NBUF * BUF <= kW4Region, "ring fits the wave's region");
 };
 
 template <int NTB>
@@ -1005,12 +1015,15 @@ struct W4Loop {
     for (int nb = 0; nb < 2; ++nb)
       f.cw[nb] = *reinterpret_cast<const uint4*>(src + C::CODE + (nb * 32 + n) * 32 +
                                                  ((h ^ ((n >> 3) & 1)) * 16));
-    const int sw = swz_f<64>(n);
+    // MFMA rows past the pass's 8 TG token rows read row n % 8 instead: their
+    // outputs are never stored, and the reads stay in the buffer
+    const int nt = n < 8 * TG ? n : (n & 7);
+    const int sw = swz_f<64>(nt);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb)
-        f.tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(src + C::TOK + (tb * 32 + n) * 128 +
+        f.tf[j][tb] = *reinterpret_cast<const bf16x8_t*>(src + C::TOK + (tb * 32 + nt) * 128 +
                                                          (((4 * h + j) ^ sw) * 16));
   }
 
@@ -1180,15 +1193,15 @@ __device__ __forceinline__ void w4_epilogue(const f32x16_t (&acc)[2][1], float* 
 // is a whole number of 128-groups. act holds act_bytes bytes; every byte
 // offset formed below is smaller (the launcher checks it fits 32 bits).
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 1) void decode_w4_kernel(
+__global__ __launch_bounds__(256, 2) void decode_w4_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ q0, const uint16_t* __restrict__ sb0,
     const uint8_t* __restrict__ q1, const uint16_t* __restrict__ sb1, void* __restrict__ out,
     int n_chunks) {
   constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
-  static_assert(NB * 2 * 16 * 64 <= kDecRegion / 2, "partial sums fit the wave's ring");
-  __shared__ __align__(1024) uint8_t s_ring[4 * 2 * kDecRegion];
+  static_assert(NB * (kW4Rows / 2) * 64 * 4 <= kW4Region, "partial sums fit the wave's ring");
+  __shared__ __align__(1024) uint8_t s_ring[4 * kW4Region];
   __shared__ int s_scan[2 * 256 + 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1206,9 +1219,9 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
   const int kw = K / 4;      // this wave's K range [wave*kw, wave*kw + kw)
   const int nch = kw / 64;   // chunks of 64 (an even number)
   const int G = K / 128;     // (scale, bias) groups per row
-  uint8_t* ring = s_ring + wave * 2 * kDecRegion;
+  uint8_t* ring = s_ring + wave * kW4Region;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t*)ring;
-  float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kDecRegion / 2
+  float* s_part = reinterpret_cast<float*>(s_ring);  // wave w at + w * kW4Region / 4
   i32x4_t ract = dec_rsrc(act, act_bytes);
   asm volatile("" : "+s"(ract));
   const uint32_t c43 = 0x43434343u;
@@ -1245,8 +1258,8 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
     const uint32_t q_off[2] = {q_lane, q_lane};
     const uint32_t s_lane = (uint32_t)((lane & 31) * 4) + (uint32_t)(wave * (nch / 2)) * 128u;
     const uint32_t s_off[2] = {s_lane, s_lane};
-    for (int p0 = r0; p0 < r1; p0 += 32) {  // 32 token rows per pass
-      const int rows = min(r1 - p0, 32);
+    for (int p0 = r0; p0 < r1; p0 += kW4Rows) {  // kW4Rows token rows per pass
+      const int rows = min(r1 - p0, kW4Rows);
       uint32_t t_off[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1273,10 +1286,10 @@ __global__ __launch_bounds__(256, 1) void decode_w4_kernel(
         // every ring buffer of this wave has landed and been read: its
         // partial sums may overwrite its ring
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        w4_epilogue<GATEUP, TG, kDecRegion / 2>(acc, s_part, p0, rows, c, N_out, out);
+        w4_epilogue<GATEUP, TG, kW4Region / 4>(acc, s_part, p0, rows, c, N_out, out);
       };
       if (rows > 24)
-        pass(std::integral_constant<int, 4>{});
+        pass(std::integral_constant<int, (kW4Rows > 24 ? 4 : 3)>{});
       else if (rows > 16)
         pass(std::integral_constant<int, 3>{});
       else if (rows > 8)
@@ -1430,7 +1443,7 @@ hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* 
                              const int32_t* offsets, const moe_w4_weights& w, void* h,
                              hipStream_t s) {
   const int nch = (c.intermediate + 31) / 32;
-  decode_w4_kernel<true><<<persistent_grid(), 256, 0, s>>>(
+  decode_w4_kernel<true><<<2 * persistent_grid(), 256, 0, s>>>(
       c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
       (uint32_t)((size_t)c.num_tokens * c.hidden * 2), sorted_pair, offsets, w.gate, static_cast<const uint16_t*>(w.gate_sb), w.up,
       static_cast<const uint16_t*>(w.up_sb), h, nch);
@@ -1440,7 +1453,7 @@ hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* 
 hipError_t launch_down_w4(const moe_config& c, const void* h, const int32_t* offsets,
                           const moe_w4_weights& w, void* y, hipStream_t s) {
   const int nch = (c.hidden + 63) / 64;
-  decode_w4_kernel<false><<<persistent_grid(), 256, 0, s>>>(
+  decode_w4_kernel<false><<<2 * persistent_grid(), 256, 0, s>>>(
       c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
       (uint32_t)((size_t)c.num_tokens * c.top_k * c.intermediate * 2), nullptr, offsets, w.down, static_cast<const uint16_t*>(w.down_sb), nullptr, nullptr, y,
       nch);
