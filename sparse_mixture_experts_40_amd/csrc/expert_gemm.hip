@@ -319,6 +319,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                                                  s_scan, sorted_pair, wave, lane, cur, a_off,
                                                  b_off);
   bool staged = false;  // first stage of `cur` already loaded by the previous tile
+  // store instructions this wave surely issued in the previous tile's
+  // epilogue, after that prefetch: the counter completes in order, so the
+  // prefetched stage has landed once no more than these remain
+  int st_after = 0;
   while (have) {
     const int tn = t + nper;
     const bool have_n = tn < chunk && xcd * chunk + tn < R;
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                               b_off, (uint32_t)(st * BK) * 2u, wave);
       wait_vmcnt((LA + LB) * ((nk - 1 < NST - 2 ? nk - 1 : NST - 2)));
     } else {
-      wait_vmcnt(0);
+      wait_vmcnt(st_after);
     }
     lds_barrier();
 
@@ -387,6 +391,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
 
     // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
     if constexpr (GATEUP) {
+    // per token block: 4 NB / 2 stores, issued at least when all 32 rows of
+    // the wave's block are in the tile
+    st_after = 0;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      st_after += (row0 + wm * 32 + mb * 64 + 31 < row_end) ? 4 * (NB / 2) : 0;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = row0 + trow0 + mb * 64;
@@ -420,6 +430,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       static_assert(BN * 64 * 4 <= STAGE * 2, "slab must fit in one stage");
       float* slab = reinterpret_cast<float*>(smem + ((nk - 1) % NST) * STAGE);
       const int srow_w = wm * 32 + (lane & 31);
+      // one store per slab row of this wave inside the tile
+      st_after = 0;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        st_after += min(max(row_end - (row0 + mb * 64 + wave * (64 / NW)), 0), 64 / NW);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
