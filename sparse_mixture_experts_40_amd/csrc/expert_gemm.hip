@@ -454,8 +454,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
           const float4 v =
               *reinterpret_cast<const float4*>(slab + sr * BN + ((lane ^ (sr & 15)) << 2));
           const int col = n0 + lane * 4;
+          // y_sorted is read once, by the combine: non-temporal stores keep it
+          // from displacing the operands in L2 (-2.5% down at 16K tokens)
           if (row < row_end && col < N_out)
-            *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)row * N_out + col) = v;
+            __builtin_nontemporal_store(
+                f32x4_t{v.x, v.y, v.z, v.w},
+                reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)row * N_out + col));
         }
         lds_barrier();
       }
