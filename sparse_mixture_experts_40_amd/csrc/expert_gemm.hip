@@ -536,7 +536,8 @@ __device__ __forceinline__ void dec_dma(uint32_t dst, i32x4_t rw0, i32x4_t rw1, 
                                         uint32_t kb) {
   constexpr int WI = DecRing<NTB>::WI, TI = DecRing<NTB>::TI;
 #pragma unroll
-  for (int i = 0; i < WI; ++i) dma16(i < WI / 2 ? rw0 : rw1, dst + i * 1024, w_off[i], kb);
+  for (int i = 0; i < WI; ++i)  // weights: read once per pass, non-temporal
+    dma16_nt(i < WI / 2 ? rw0 : rw1, dst + i * 1024, w_off[i], kb);
 #pragma unroll
   for (int j = 0; j < TI * NTB; ++j)
     dma16(ract, dst + kDecWRows * kDecK * 2 + j * 1024, t_off[j], kb);

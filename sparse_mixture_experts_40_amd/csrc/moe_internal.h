@@ -119,6 +119,14 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, 
                :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(uniform4(rsrc)),
                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
+
+// dma16 with the non-temporal hint, for data read exactly once (streamed
+// expert weights), so it does not displace the rows read again (tokens).
+__device__ __forceinline__ void dma16_nt(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(uniform4(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // XCD-aware block order. Hardware block ids are dealt round-robin to the 8
