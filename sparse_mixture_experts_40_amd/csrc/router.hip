@@ -28,6 +28,8 @@
 // and marks the others empty (-1, weight 0).
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -48,31 +50,76 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 }
 
 // Reductions over the 64 lanes of N tokens at once (independent chains).
+// Wave-wide reductions whose result every lane receives. Inside each row of
+// 16 lanes four DPP exchanges (xor 1, xor 2, mirror within 8, mirror within
+// 16) combine all 16 values without LDS traffic; the four row results are
+// then read with readlane and combined in row order 0..3.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <int N>
 __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1)
-#pragma unroll
-    for (int u = 0; u < N; ++u) v[u] = fmaxf(v[u], __shfl_xor(v[u], msk, 64));
+  for (int u = 0; u < N; ++u) {
+    float x = v[u];
+    x = fmaxf(x, dpp_f32<kDppXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppMirror>(x));
+    v[u] = fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
+  }
 }
 
 template <int N>
 __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
 #pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1)
-#pragma unroll
-    for (int u = 0; u < N; ++u) v[u] += __shfl_xor(v[u], msk, 64);
+  for (int u = 0; u < N; ++u) {
+    float x = v[u];
+    x += dpp_f32<kDppXor1>(x);
+    x += dpp_f32<kDppXor2>(x);
+    x += dpp_f32<kDppHalfMirror>(x);
+    x += dpp_f32<kDppMirror>(x);
+    v[u] = ((lane_f32(x, 0) + lane_f32(x, 16)) + lane_f32(x, 32)) + lane_f32(x, 48);
+  }
 }
 
 template <int N>
 __device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[N]) {
+  auto step = [](unsigned long long x, auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const unsigned long long o =
+        (static_cast<unsigned long long>(dpp_u32<C>((uint32_t)(x >> 32))) << 32) |
+        dpp_u32<C>((uint32_t)x);
+    return o > x ? o : x;
+  };
+  auto lane64 = [](unsigned long long x, int l) {
+    return (static_cast<unsigned long long>(
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l)) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  };
 #pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1)
-#pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const unsigned long long o = __shfl_xor(v[u], msk, 64);
-      v[u] = (o > v[u]) ? o : v[u];
-    }
+  for (int u = 0; u < N; ++u) {
+    unsigned long long x = v[u];
+    x = step(x, std::integral_constant<int, kDppXor1>{});
+    x = step(x, std::integral_constant<int, kDppXor2>{});
+    x = step(x, std::integral_constant<int, kDppHalfMirror>{});
+    x = step(x, std::integral_constant<int, kDppMirror>{});
+    const unsigned long long a = lane64(x, 0), b = lane64(x, 16), c = lane64(x, 32),
+                             d = lane64(x, 48);
+    const unsigned long long ab = a > b ? a : b, cd = c > d ? c : d;
+    v[u] = ab > cd ? ab : cd;
+  }
 }
 
 // swizzled [rows][64] bf16 tile: 16-byte chunk c of row r lives at chunk c ^ (r & 7)
