@@ -136,55 +136,55 @@ __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, 
   uint16_t* s_w = s_x + kTok * kBK;                     // [EP][64]
   const int ntiles = (EP / 32) * 2;                     // (expert block, token block)
 
-  f32x16_t acc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+  // tiles of this wave: (expert block, token block) q * 4 + wave for q < nq
+  const int nq = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
 
-  uint4 rx[2], rw[8];
-  auto gload = [&](int k0) {
+  // Two register sets: the loads of steps kt + 1 and kt + 2 are in flight
+  // while step kt is multiplied. The loads are unconditional (rows clamped)
+  // and the tile count is a compile-time constant of the loop, so the
+  // compiler's load counting stays exact and each set is waited for only
+  // where it is stored. Barriers order LDS only.
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 16 bytes in registers
+  auto gload = [&](int k0, v4u (&rx)[2], v4u (&rw)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      rx[i] = make_uint4(0, 0, 0, 0);
-      if (t0 + row < T)
-        rx[i] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + row) * H + k0 + ch * 8);
+      const int gt = t0 + row < T ? t0 + row : T - 1;  // rows past T are never stored
+      rx[i] = *reinterpret_cast<const v4u*>(x + (size_t)gt * H + k0 + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      rw[i] = make_uint4(0, 0, 0, 0);
-      if (row < E) rw[i] = *reinterpret_cast<const uint4*>(wr + (size_t)row * H + k0 + ch * 8);
+      const int gr = row < E ? row : E - 1;  // slots past E re-read row E-1 (one line)
+      rw[i] = *reinterpret_cast<const v4u*>(wr + (size_t)gr * H + k0 + ch * 8);
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](const v4u (&rx)[2], const v4u (&rw)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(s_x + swz(row, ch)) = rx[i];
+      *reinterpret_cast<v4u*>(s_x + swz(row, ch)) = rx[i];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      if (row < EP) *reinterpret_cast<uint4*>(s_w + swz(row, ch)) = rw[i];
+      if (32 * i < EP) *reinterpret_cast<v4u*>(s_w + swz(row, ch)) = rw[i];
     }
   };
-
-  const int nk = (kend - kbeg) / kBK;
-  gload(kbeg);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();  // previous compute done with the tile
-    sstore();
-    __syncthreads();
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * kBK);
+  auto kloop = [&](auto nq_c) __attribute__((always_inline)) {
+    constexpr int NQ = decltype(nq_c)::value;
+    f32x16_t acc[NQ > 0 ? NQ : 1];
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int tile = q * 4 + wave;
-        if (tile < ntiles) {
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+    auto compute = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int tile = q * 4 + wave;
           const int eb = tile >> 1, tb = tile & 1;
           const int er = eb * 32 + (lane & 31), tr = tb * 32 + (lane & 31);
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
@@ -192,13 +192,29 @@ __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, 
           acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
         }
       }
+    };
+    const int nk = (kend - kbeg) / kBK;
+    v4u rxa[2], rwa[8], rxb[2], rwb[8];  // the two load sets
+    gload(kbeg, rxa, rwa);
+    if (nk > 1) gload(kbeg + kBK, rxb, rwb);
+    for (int kt = 0; kt < nk; kt += 2) {
+      lds_barrier();  // previous compute done with the tile
+      sstore(rxa, rwa);
+      lds_barrier();
+      if (kt + 2 < nk) gload(kbeg + (kt + 2) * kBK, rxa, rwa);
+      compute();
+      if (kt + 1 < nk) {
+        lds_barrier();
+        sstore(rxb, rwb);
+        lds_barrier();
+        if (kt + 3 < nk) gload(kbeg + (kt + 3) * kBK, rxb, rwb);
+        compute();
+      }
     }
-  }
-  __syncthreads();  // tiles dead; s_log aliases them
+    __syncthreads();  // tiles dead; s_log aliases them
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tile = q * 4 + wave;
-    if (tile < ntiles) {
+    for (int q = 0; q < NQ; ++q) {
+      const int tile = q * 4 + wave;
       const int eb = tile >> 1, tb = tile & 1;
       const int t = tb * 32 + (lane & 31);
 #pragma unroll
@@ -207,6 +223,13 @@ __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, 
         if (e < E) s_log[t * ls + e] = acc[q][r] + (bias ? bias[e] : 0.0f);
       }
     }
+  };
+  switch (nq) {  // wave-uniform
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    default: kloop(std::integral_constant<int, 4>{}); break;
   }
 }
 
