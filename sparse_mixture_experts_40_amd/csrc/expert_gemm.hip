@@ -965,10 +965,10 @@ __device__ __forceinline__ void wait_vm() {
 // 4-wave blocks share a CU (two waves per SIMD), so one wave's VALU work
 // overlaps the other's MFMAs, loads and waits.
 #ifndef MOE_W4_REGION
-#define MOE_W4_REGION 19456
+#define MOE_W4_REGION 19968
 #endif
 #ifndef MOE_W4_ROWS
-#define MOE_W4_ROWS 24
+#define MOE_W4_ROWS 32
 #endif
 constexpr int kW4Region = MOE_W4_REGION, kW4Rows = MOE_W4_ROWS;
 static_assert(kW4Rows % 8 == 0 && kW4Rows <= 32, "rows per pass");
@@ -1222,20 +1222,23 @@ __global__ __launch_bounds__(256, 2) void decode_w4_kernel(
   constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
   static_assert(NB * (kW4Rows / 2) * 64 * 4 <= kW4Region, "partial sums fit the wave's ring");
   __shared__ __align__(1024) uint8_t s_ring[4 * kW4Region];
-  __shared__ int s_scan[2 * 256 + 2];
+  // offsets, and the inclusive count of experts with rows (16 bits: E <= 256),
+  // so that two blocks with 3 ring buffers of 32 token rows per wave fit a CU
+  __shared__ int s_off[256 + 1];
+  __shared__ uint16_t s_cnt[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  for (int i = tid; i <= E; i += blockDim.x) s_off[i] = offsets[i];
   __syncthreads();
-  if (tid < E) s_scan[tid] = (s_scan[E + 2 + tid] > s_scan[E + 1 + tid]) ? 1 : 0;
+  if (tid < E) s_cnt[tid] = (s_off[tid + 1] > s_off[tid]) ? 1 : 0;
   __syncthreads();
   for (int d = 1; d < E; d <<= 1) {
-    const int add = (tid < E && tid >= d) ? s_scan[tid - d] : 0;
+    const int add = (tid < E && tid >= d) ? s_cnt[tid - d] : 0;
     __syncthreads();
-    if (tid < E) s_scan[tid] += add;
+    if (tid < E) s_cnt[tid] = (uint16_t)(s_cnt[tid] + add);
     __syncthreads();
   }
-  const int items = s_scan[E - 1] * n_chunks;
+  const int items = s_cnt[E - 1] * n_chunks;
   const int kw = K / 4;      // this wave's K range [wave*kw, wave*kw + kw)
   const int nch = kw / 64;   // chunks of 64 (an even number)
   const int G = K / 128;     // (scale, bias) groups per row
@@ -1251,10 +1254,10 @@ __global__ __launch_bounds__(256, 2) void decode_w4_kernel(
     int lo = 0, hi = E - 1;  // expert = the (rank+1)-th expert with rows
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (s_scan[mid] > rank) hi = mid; else lo = mid + 1;
+      if (s_cnt[mid] > rank) hi = mid; else lo = mid + 1;
     }
     const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int r0 = s_scan[E + 1 + e], r1 = s_scan[E + 2 + e];
+    const int r0 = s_off[e], r1 = s_off[e + 1];
     // weight rows of the item: gate/up rows [32c, 32c + 32) of both matrices,
     // down rows [64c, 64c + 64): 32-row blocks rb0 and rb1 of the codes and
     // (scale, bias) tiles (N_out is a multiple of 512)
