@@ -893,7 +893,9 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
 //
 // [MOE-128x8] 参数量化与存储优化: 4-bit codes in groups of 128 along K with an
 // independent scale and bias per group, w = scale * q + bias. Work items and
-// the 4-way split-K are those of decode_gemm_bf16_kernel.
+// the 4-way split-K are those of decode_gemm_bf16_kernel; the codes and
+// (scale, bias) pairs are stored in tiles of 32 rows (moe.h), so one chunk of
+// a 32-row block is 1 KB contiguous and its DMA uses whole cache lines.
 // No weight is rounded: the MFMA multiplies the exact bf16 values 128 + q
 // with the tokens, a second MFMA against ones gives the group's token sums,
 // and each group of 128 is folded into the fp32 accumulators as
@@ -904,8 +906,9 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
 // [32h, 32h + 32) of a chunk (16 bytes of codes) in 4 MFMA k steps of 8 and
 // reads its token fragments in the same order.
 //
-// One wave runs per SIMD, so every instruction takes an issue slot of its
-// own, and the loop is laid out to issue few:
+// The loop is bound by instruction issue more than by memory, so it is laid
+// out to issue few instructions, and two 4-wave blocks share each CU (two
+// waves per SIMD: one wave's VALU work overlaps the other's MFMAs and waits):
 //  - 16 codes unpack with 13 VALU: two masks and one 64-bit shift give the
 //    nibbles as bytes, and each byte permute forms two bf16 values, taking
 //    their exponent byte from a constant register;
