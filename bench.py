@@ -54,10 +54,10 @@ FETCH_SCALE = 1048576.0 / 524303.1
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("ef8b9244c4602ec255c131686336a78f96d37c7d59e560c6aec88f1c35afc7f7",
-                        3881995.1, 393507.1),
-    "decode128_bf16": ("ef8b9244c4602ec255c131686336a78f96d37c7d59e560c6aec88f1c35afc7f7",
-                       542900.8, 1561.5),
+    "prefill128_bf16": ("ad9e6413489fcf29d920db32a1043b70cffb38e34ed744f29d6b49458f621058",
+                        3861866.4, 393522.8),
+    "decode128_bf16": ("ad9e6413489fcf29d920db32a1043b70cffb38e34ed744f29d6b49458f621058",
+                       542917.6, 1563.5),
 }
 
 
