@@ -157,12 +157,18 @@ __device__ __forceinline__ void gemm_step(
   }
 }
 
-// The K loop of one tile for a wave with MBV active token blocks: first
-// fragments, the steps, and (prefetch) the last step that loads the next
-// tile's first stage into buffer 0. Waves without active blocks still issue
-// their loads and take every barrier.
+// The K loop of one tile for a wave with MBV active token blocks. The LDS
+// stages form a ring that runs on across tiles: global stage g sits in buffer
+// g % NST, the tile's K stage kt is global stage g0 + kt, and each step loads
+// the stage NST - 1 ahead, which in the tile's last NST - 1 steps is a first
+// stage of the next tile (pf), so the pipeline never drains between tiles.
+// Waves without active blocks still issue their loads and take every barrier.
+// The wait before a step's barrier lets the stages issued after the awaited
+// one stay in flight, and for the stages of this tile loaded before the
+// previous epilogue (kt < NST - 1 when the tile was prefetched) also st_allow,
+// a lower bound of that epilogue's stores: the counter completes in order.
 template <int BK, int BM, int NST, int NW, int MB, int NB, int MBV>
-__device__ __forceinline__ void tile_k(uint16_t* smem, int nk, bool prefetch,
+__device__ __forceinline__ void tile_k(uint16_t* smem, int nk, int g0, bool pf, int st_allow,
                                        __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase,
                                        __amdgpu_buffer_rsrc_t bbase_n, const uint32_t* a_off,
                                        const uint32_t* b_off, const uint32_t* a_offn,
@@ -172,27 +178,30 @@ __device__ __forceinline__ void tile_k(uint16_t* smem, int nk, bool prefetch,
   constexpr int LA = BM * BK / (512 * NW), LB = 256 * BK / (512 * NW);
   constexpr int STAGE = (BM + 256) * BK;
   bf16x8_t fa[2][NB], fb[2][MB];
-  stage_frag<BK, MB, NB, MBV>(smem, smem + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
-  const int nk_main = prefetch ? nk - 1 : nk;
-  for (int kt = 0; kt < nk_main; ++kt) {
-    uint16_t* dA = smem + ((kt + NST - 1) % NST) * STAGE;
-    const uint16_t* cA = smem + (kt % NST) * STAGE;
-    const uint16_t* nA = smem + ((kt + 1) % NST) * STAGE;
-    const int last = (kt + NST - 1 < nk - 1) ? kt + NST - 1 : nk - 1;
-    const int ahead = last - (kt + 1);  // stages still loading after stage kt+1
-    gemm_step<BK, BM, NW, MB, NB, MBV>(dA, dA + BM * BK, kt + NST - 1 < nk, abase, bbase, a_off,
-                                       b_off, (uint32_t)((kt + NST - 1) * BK) * 2u, cA,
-                                       cA + BM * BK, nA, nA + BM * BK,
-                                       ahead > 0 ? (LA + LB) * ahead : 0, acc, fa, fb, wrow,
-                                       trow0, lane, sw, wave);
-  }
-  if (prefetch) {
-    // last K stage (buffer 1) while the next tile's stage 0 loads into buffer 0;
-    // the fragments read after its barrier are stale and unused
-    gemm_step<BK, BM, NW, MB, NB, MBV>(smem, smem + BM * BK, true, abase, bbase_n, a_offn, b_offn,
-                                       0u, smem + STAGE, smem + STAGE + BM * BK, smem,
-                                       smem + BM * BK, LA + LB, acc, fa, fb, wrow, trow0, lane,
-                                       sw, wave);
+  const uint16_t* c0 = smem + (g0 % NST) * STAGE;
+  stage_frag<BK, MB, NB, MBV>(c0, c0 + BM * BK, 0, fa[0], fb[0], wrow, trow0, lane, sw);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int g = g0 + kt;
+    const int is = kt + NST - 1;  // stage loaded by this step, counted from the tile start
+    const bool in_cur = is < nk;
+    // stages issued after the awaited stage kt + 1 once this step's loads are
+    // out. The last step awaits nothing (its post-barrier fragment reads are
+    // unused): the next tile's stages stay in flight through the epilogue.
+    const int last = (in_cur || pf) ? is : nk - 1;
+    const int vm = kt + 1 < nk ? (LA + LB) * (last - (kt + 1)) + (kt + 1 < NST - 1 ? st_allow : 0)
+                               : (pf ? (LA + LB) * (NST - 1) : 0);
+    uint32_t ao[LA], bo[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ao[i] = in_cur ? a_off[i] : a_offn[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) bo[i] = in_cur ? b_off[i] : b_offn[i];
+    uint16_t* dA = smem + ((g + NST - 1) % NST) * STAGE;
+    const uint16_t* cA = smem + (g % NST) * STAGE;
+    const uint16_t* nA = smem + ((g + 1) % NST) * STAGE;
+    gemm_step<BK, BM, NW, MB, NB, MBV>(
+        dA, dA + BM * BK, in_cur || pf, abase, in_cur ? bbase : bbase_n, ao, bo,
+        (uint32_t)((in_cur ? is : is - nk) * BK) * 2u, cA, cA + BM * BK, nA, nA + BM * BK, vm,
+        acc, fa, fb, wrow, trow0, lane, sw, wave);
   }
 }
 
@@ -304,12 +313,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
   // B rows [0, 128) of a gate/up tile come from W_gate, [128, 256) from W_up
   const uint16_t* wsel = (GATEUP && wave >= NW / 2) ? w1 : w0;
   const uint32_t wbytes = (uint32_t)N_out * (uint32_t)K * 2u;  // one expert's matrix
-  // With two stages and an even number of K stages, the last K stage of a tile
-  // computes from buffer 1 while buffer 0 is free: the next tile's first stage
-  // is loaded there during that step, and its latency hides behind the
-  // epilogue (no pipeline drain between tiles).
-  const bool can_prefetch = (NST == 2) && (nk % 2 == 0);
-
   int t = blockIdx.x >> 3;
   bool have = t < chunk && xcd * chunk + t < R;
   GemmTile cur;
@@ -318,11 +321,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     tile_setup<GATEUP, BM, BK, NW, NCOL, LA, LB>(xcd * chunk + t, n_tiles_n, E, K, N_out, k_top,
                                                  s_scan, sorted_pair, wave, lane, cur, a_off,
                                                  b_off);
-  bool staged = false;  // first stage of `cur` already loaded by the previous tile
+  bool staged = false;  // first NST - 1 stages of `cur` loaded by the previous tile
   // store instructions this wave surely issued in the previous tile's
-  // epilogue, after that prefetch: the counter completes in order, so the
-  // prefetched stage has landed once no more than these remain
+  // epilogue, after those prefetched stages
   int st_after = 0;
+  int g0 = 0;  // ring position (global stage index) of the tile's first K stage
   while (have) {
     const int tn = t + nper;
     const bool have_n = tn < chunk && xcd * chunk + tn < R;
@@ -336,7 +339,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       tile_setup<GATEUP, BM, BK, NW, NCOL, LA, LB>(xcd * chunk + tn, n_tiles_n, E, K, N_out,
                                                    k_top, s_scan, sorted_pair, wave, lane, nxt,
                                                    a_offn, b_offn);
-    const bool prefetch = can_prefetch && have_n;
+    // the last NST - 1 steps load the next tile's first stages
+    const bool prefetch = have_n && nk >= NST - 1;
     const __amdgpu_buffer_rsrc_t bbase =
         make_rsrc(wsel + (size_t)__builtin_amdgcn_readfirstlane(cur.expert) * N_out * K, wbytes);
     const __amdgpu_buffer_rsrc_t bbase_n =
@@ -350,16 +354,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
-    // prologue: NST - 1 stages in flight (unless prefetched)
+    // prologue: NST - 1 stages in flight (unless prefetched), then wait for
+    // the first
+    const int npro = nk < NST - 1 ? nk : NST - 1;
     if (!staged) {
-      for (int st = 0; st < NST - 1 && st < nk; ++st)
-        dma_stage<BK, BM, NW>(smem + st * STAGE, smem + st * STAGE + BM * BK, abase, bbase, a_off,
-                              b_off, (uint32_t)(st * BK) * 2u, wave);
-      wait_vmcnt((LA + LB) * ((nk - 1 < NST - 2 ? nk - 1 : NST - 2)));
+      for (int st = 0; st < npro; ++st) {
+        uint16_t* d = smem + ((g0 + st) % NST) * STAGE;
+        dma_stage<BK, BM, NW>(d, d + BM * BK, abase, bbase, a_off, b_off,
+                              (uint32_t)(st * BK) * 2u, wave);
+      }
+      wait_vmcnt((LA + LB) * (npro - 1));
     } else {
-      wait_vmcnt(st_after);
+      wait_vmcnt((LA + LB) * (NST - 2) + st_after);
     }
     lds_barrier();
+    const int st_allow = staged ? st_after : 0;
 
     // token blocks of this wave with at least one row of the expert: the
     // MFMAs (and fragment reads) of the others are skipped, so the last,
@@ -367,21 +376,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     const int live = min(BM, cur.row_end - cur.row0) - wm * 32;
     const int mbv = live <= 0 ? 0 : min(MB, (live + 63) / 64);
     if (mbv >= MB)
-      tile_k<BK, BM, NST, NW, MB, NB, MB>(smem, nk, prefetch, abase, bbase, bbase_n, a_off,
-                                          b_off, a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
+      tile_k<BK, BM, NST, NW, MB, NB, MB>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n,
+                                          a_off, b_off, a_offn, b_offn, acc, wrow, trow0, lane,
+                                          sw, wave);
     else if (mbv == 3)
-      tile_k<BK, BM, NST, NW, MB, NB, (MB > 3 ? 3 : MB)>(smem, nk, prefetch, abase, bbase,
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 3 ? 3 : MB)>(smem, nk, g0, prefetch, st_allow, abase, bbase,
                                                          bbase_n, a_off, b_off, a_offn, b_offn,
                                                          acc, wrow, trow0, lane, sw, wave);
     else if (mbv == 2)
-      tile_k<BK, BM, NST, NW, MB, NB, (MB > 2 ? 2 : MB)>(smem, nk, prefetch, abase, bbase,
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 2 ? 2 : MB)>(smem, nk, g0, prefetch, st_allow, abase, bbase,
                                                          bbase_n, a_off, b_off, a_offn, b_offn,
                                                          acc, wrow, trow0, lane, sw, wave);
     else if (mbv == 1)
-      tile_k<BK, BM, NST, NW, MB, NB, 1>(smem, nk, prefetch, abase, bbase, bbase_n, a_off, b_off,
+      tile_k<BK, BM, NST, NW, MB, NB, 1>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
                                          a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
     else
-      tile_k<BK, BM, NST, NW, MB, NB, 0>(smem, nk, prefetch, abase, bbase, bbase_n, a_off, b_off,
+      tile_k<BK, BM, NST, NW, MB, NB, 0>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
                                          a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
     // No barrier here: the only LDS the epilogue touches is the stage computed
     // last (its reads finished before the last stage barrier), and the next
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       // c ^ (s & 15): conflict-free for the column writes (16 rows, one chunk)
       // and the row reads (one row, 16 chunks).
       static_assert(BN * 64 * 4 <= STAGE * 2, "slab must fit in one stage");
-      float* slab = reinterpret_cast<float*>(smem + ((nk - 1) % NST) * STAGE);
+      float* slab = reinterpret_cast<float*>(smem + ((g0 + nk - 1) % NST) * STAGE);
       const int srow_w = wm * 32 + (lane & 31);
       // one store per slab row of this wave inside the tile
       st_after = 0;
@@ -466,6 +476,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     }
 
     staged = prefetch;
+    g0 += nk;
     cur = nxt;
 #pragma unroll
     for (int i = 0; i < LA; ++i) a_off[i] = a_offn[i];
@@ -476,15 +487,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
   }
 }
 
-#ifndef MOE_GEMM_NW
-#define MOE_GEMM_NW 8
-#endif
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-// tile height, K step, LDS stages, waves per block, blocks per CU
-constexpr int kGemmBM = 256, kGemmBK = MOE_GEMM_BK, kGemmStages = MOE_GEMM_BK == 64 ? 2 : 4,
-              kGemmWaves = MOE_GEMM_NW, kGemmOcc = 1;
+// tile height, K step, LDS stages (2 x 64 KB), waves per block, blocks per CU.
+// The stage ring also runs with BK = 32 and 4 stages (1.5x the bytes in
+// flight): gate/up was 8% slower at 128 experts x 16K tokens.
+constexpr int kGemmBM = 256, kGemmBK = 64, kGemmStages = 2, kGemmWaves = 8, kGemmOcc = 1;
 
 // ---- bf16 decode path (few rows per expert: weight streaming) -------------
 //

@@ -32,8 +32,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt vmcnt(n) for the counts the pipelines need (n <= 32; larger
-// counts wait for everything, which is always safe)
+// s_waitcnt vmcnt(n) for the counts the pipelines need (n <= 32; a larger
+// count waits for 32, which is stricter and so always safe)
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
     case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
@@ -68,7 +68,10 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
     case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
     case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    default:
+      if (n > 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      break;
   }
 }
 
