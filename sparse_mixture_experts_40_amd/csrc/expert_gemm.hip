@@ -24,6 +24,7 @@
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
 #include "moe_internal.h"
 
+
 namespace moe {
 
 namespace {
@@ -55,21 +56,25 @@ __device__ __forceinline__ int swz_f(int r) {
 // LDS counter, which makes the compiler wait for every LDS read in full
 // (lgkmcnt(0)) while stage loads are in flight; with buffer loads it waits
 // only for the fragments it needs.
+// Loads [i0, i1) of the wave's LA + LB (A first, then B); the whole stage by
+// default.
 template <int BK, int BM, int NW>
 __device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* __restrict__ dB,
                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
-                                          int wave) {
+                                          int wave, int i0 = 0, int i1 = 1 << 30) {
   constexpr int CPR = BK / 8, RPI = 64 / CPR;
   constexpr int LA = BM * BK / (512 * NW), LB = 256 * BK / (512 * NW);  // per wave
 #pragma unroll
   for (int i = 0; i < LA; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dA + (wave * LA + i) * RPI * BK), 16,
-                                             a_off[i], kb, 0, 0);
+    if (i >= i0 && i < i1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dA + (wave * LA + i) * RPI * BK),
+                                               16, a_off[i], kb, 0, 0);
 #pragma unroll
   for (int i = 0; i < LB; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dB + (wave * LB + i) * RPI * BK), 16,
-                                             b_off[i], kb, 0, 0);
+    if (LA + i >= i0 && LA + i < i1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dB + (wave * LB + i) * RPI * BK),
+                                               16, b_off[i], kb, 0, 0);
 }
 
 // Fragments of k step kk of a stage: NB weight blocks (A operand) and the MBV
@@ -114,9 +119,18 @@ __device__ __forceinline__ void gemm_step(
   constexpr int KK = BK / 16;
   constexpr int L = (KK - 1) & 1;  // fragment buffer of the last k step
   constexpr int NH = NB / 2;       // last k step: blocks [0, NH) before the barrier
-  if (issue_next) dma_stage<BK, BM, NW>(dA, dB, abase, bbase, a_off, b_off, kb, wave);
+  // The stage loads are issued in two halves (the A rows, then the B rows), at
+  // the start of k steps 0 and 1. A wave issues in order, and a burst of all
+  // its loads stalled it at issue, MFMAs included, while the memory pipeline
+  // took them in (-4% gate/up and down at 128 experts x 16K tokens). Later
+  // or finer splits leave the last loads too little time to land (+5%).
+  constexpr int NL = BM * BK / (512 * NW) + 256 * BK / (512 * NW);
+  constexpr int KD = KK < 2 ? KK : 2;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
+    if (kk < KD && issue_next)
+      dma_stage<BK, BM, NW>(dA, dB, abase, bbase, a_off, b_off, kb, wave, NL * kk / KD,
+                            NL * (kk + 1) / KD);
     if (kk + 1 < KK)
       stage_frag<BK, MB, NB, MBV>(cA, cB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wrow,
                                   trow0, lane, sw);
@@ -127,17 +141,16 @@ __device__ __forceinline__ void gemm_step(
       for (int mb = 0; mb < MBV; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][nb], fb[kk & 1][mb],
                                                               acc[nb][mb], 0, 0, 0);
-  }
-  // per k step: first all fragment reads of the next k step, then this step's
-  // MFMAs, so each read has a whole step of MFMAs to land before its use
-  if constexpr (MBV > 0) {
-    constexpr int NR = NB + MBV;
-#pragma unroll
-    for (int kk = 0; kk + 1 < KK; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NB * MBV, 0);
+    // first the fragment reads of the next k step, then this step's MFMAs, so
+    // each read has a whole step of MFMAs to land before its use
+    if constexpr (MBV > 0) {
+      if (kk + 1 < KK) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NB + MBV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NB * MBV, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NH * MBV, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NH * MBV, 0);
   }
   wait_vmcnt(vm_allow);
   lds_barrier();
