@@ -50,14 +50,14 @@ PEAK_HBM_GBS = 8000.0
 # sources they were taken on (sha256 below); otherwise traffic is null.
 TRAFFIC_SOURCES = ("sparse_mixture_experts_40_amd/csrc/expert_gemm.hip",
                    "sparse_mixture_experts_40_amd/csrc/moe_internal.h")
-FETCH_SCALE = 1048576.0 / 524303.1
+FETCH_SCALE = 1048576.0 / 524302.4
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("ad9e6413489fcf29d920db32a1043b70cffb38e34ed744f29d6b49458f621058",
-                        3861866.4, 393522.8),
-    "decode128_bf16": ("ad9e6413489fcf29d920db32a1043b70cffb38e34ed744f29d6b49458f621058",
-                       542917.6, 1563.5),
+    "prefill128_bf16": ("a5bab0ba3c60c8cf2d7df93fac1650cbc09550cd7b8cb8ad8c13a9d450b3bba3",
+                        3798049.5, 394143.9),
+    "decode128_bf16": ("a5bab0ba3c60c8cf2d7df93fac1650cbc09550cd7b8cb8ad8c13a9d450b3bba3",
+                       542903.0, 1561.8),
 }
 
 
