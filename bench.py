@@ -54,9 +54,9 @@ FETCH_SCALE = 1048576.0 / 524302.4
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("a5bab0ba3c60c8cf2d7df93fac1650cbc09550cd7b8cb8ad8c13a9d450b3bba3",
+    "prefill128_bf16": ("c0d26d3282615d2236a0a8b652fb62ce38fd6358e72396d3861d09cbe5cf063e",
                         3798049.5, 394143.9),
-    "decode128_bf16": ("a5bab0ba3c60c8cf2d7df93fac1650cbc09550cd7b8cb8ad8c13a9d450b3bba3",
+    "decode128_bf16": ("c0d26d3282615d2236a0a8b652fb62ce38fd6358e72396d3861d09cbe5cf063e",
                        542903.0, 1561.8),
 }
 

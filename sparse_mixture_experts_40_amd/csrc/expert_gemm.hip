@@ -11,7 +11,7 @@
 // is found on the device from `offsets` (no host sync, no tile list). Empty
 // experts own no tiles, so their weights are never read.
 //
-// bf16 path (persistent, one 256-thread block per CU):
+// bf16 path (persistent, one 512-thread block of 8 waves per CU):
 //   tile  256 token rows x 256 weight rows; MFMA v_mfma_f32_32x32x16_bf16 with
 //         the WEIGHT rows as the A operand and the token rows as B, so D[n][m]
 //         puts 4 consecutive output columns of one token row in each lane;
@@ -21,6 +21,8 @@
 //         rounding). The token rows are gathered through sorted_pair / k;
 //   down: y_sorted = h W_down^T over contiguous h rows, stored in fp32 (the
 //         combine adds the k rows of a token in fp32 and rounds once).
+// Decode-sized batches (few rows per expert) take the weight-streaming
+// kernels further down instead.
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
 #include "moe_internal.h"
 
