@@ -9,7 +9,7 @@
 // Statistics: [MOE-128x8] "MoE架构深度解析：128专家与8激活的智能路由" (csdn),
 // load-balancing section: f_e = n_e / (T*k), P_e = mean softmax probability,
 // aux = E * sum_e f_e P_e. Sums run in a fixed order.
-#include "moe_internal.h"
+#include "aux_small.h"
 
 namespace moe {
 
@@ -145,62 +145,10 @@ __global__ __launch_bounds__(kThreads) void aux_final_kernel(int T, int E,
 }
 
 // Few router blocks (np <= kAuxSmall): both kernels above in one block.
-// Thread e sums expert e's partials in block order (fixed order, double);
-// the rest is as above.
-constexpr int kAuxSmall = 64;
-__global__ __launch_bounds__(kThreads) void aux_small_kernel(
-    int T, int E, int want_stats, const int32_t* __restrict__ counts,
-    const float* __restrict__ partials, int np, int32_t* __restrict__ c_out,
-    float* __restrict__ f_out, float* __restrict__ p_out, const float* __restrict__ zpart,
-    int nz, float* __restrict__ aux_out, float* __restrict__ z_out) {
-  __shared__ double s[kThreads];
-  __shared__ int s_routed;
+__global__ __launch_bounds__(kThreads) void aux_small_kernel(AuxSmallArgs a,
+                                                             const int32_t* __restrict__ counts) {
   const int e = threadIdx.x;
-  if (e == 0) s_routed = 0;
-  __syncthreads();
-  const int n = (want_stats && e < E) ? counts[e] : 0;
-  if (want_stats && e < E) atomicAdd(&s_routed, n);  // integer: exact, order-free
-  double acc = 0.0;
-  if (want_stats && e < E) {
-    // unconditional loads (row index clamped into [0, np)), so that all of
-    // them are in flight together; only rows b < np are added, in order
-    float r[kAuxSmall];
-#pragma unroll
-    for (int b = 0; b < kAuxSmall; ++b) r[b] = partials[(size_t)min(b, np - 1) * E + e];
-#pragma unroll
-    for (int b = 0; b < kAuxSmall; ++b) acc += b < np ? (double)r[b] : 0.0;
-  }
-  __syncthreads();
-  double fp = 0.0;
-  if (want_stats && e < E) {
-    const double f = s_routed > 0 ? (double)n / (double)s_routed : 0.0;
-    const double P = acc / (double)T;
-    if (c_out) c_out[e] = n;
-    if (f_out) f_out[e] = (float)f;
-    if (p_out) p_out[e] = (float)P;
-    fp = f * P;
-  }
-  if (aux_out) {
-    s[e] = fp;
-    __syncthreads();
-    for (int d = kThreads / 2; d > 0; d >>= 1) {
-      if (e < d) s[e] += s[e + d];
-      __syncthreads();
-    }
-    if (e == 0) aux_out[0] = (float)((double)E * s[0]);
-    __syncthreads();
-  }
-  if (z_out) {
-    double z = 0.0;
-    for (int b = e; b < nz; b += kThreads) z += (double)zpart[b];
-    s[e] = z;
-    __syncthreads();
-    for (int d = kThreads / 2; d > 0; d >>= 1) {
-      if (e < d) s[e] += s[e + d];
-      __syncthreads();
-    }
-    if (e == 0) z_out[0] = (float)(s[0] / (double)T);
-  }
+  aux_small_body(a, (a.want_stats && e < a.E) ? counts[e] : 0);
 }
 
 }  // namespace
@@ -228,16 +176,27 @@ hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pai
   return hipGetLastError();
 }
 
+bool aux_small_fits(const moe_config& c, int n_partials) {
+  return n_partials <= kAuxSmall && c.num_experts <= kThreads;
+}
+
+AuxSmallArgs aux_small_args(const moe_config& c, const float* prob_partials, int n_partials,
+                            moe_aux_out out, const float* zpart, int n_zpart) {
+  const bool stats = out.counts || out.f || out.P || out.aux;
+  return AuxSmallArgs{c.num_tokens, c.num_experts, stats ? 1 : 0, prob_partials, n_partials,
+                      out.counts, out.f, out.P, zpart, n_zpart, out.aux,
+                      zpart ? out.z_loss : nullptr};
+}
+
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
                       int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s,
                       const float* zpart, int n_zpart) {
   const bool stats = out.counts || out.f || out.P || out.aux;
   float* z_out = zpart ? out.z_loss : nullptr;
-  if (n_partials <= kAuxSmall && c.num_experts <= kThreads) {
+  if (aux_small_fits(c, n_partials)) {
     if (stats || z_out)
-      aux_small_kernel<<<1, kThreads, 0, s>>>(c.num_tokens, c.num_experts, stats ? 1 : 0, counts,
-                                              prob_partials, n_partials, out.counts, out.f,
-                                              out.P, zpart, n_zpart, out.aux, z_out);
+      aux_small_kernel<<<1, kThreads, 0, s>>>(
+          aux_small_args(c, prob_partials, n_partials, out, zpart, n_zpart), counts);
     return hipGetLastError();
   }
   if (stats)

@@ -15,7 +15,8 @@
 //             bit of the expert id), wave counts go through LDS, so pairs of an
 //             expert land in ascending pair order (a stable sort).
 // With a single chunk (P <= kChunk, the decode case) the three steps run in
-// one block and one launch.
+// one block and one launch, followed (do_aux) by the load-balance statistics
+// from these counts, which then need no launch of their own.
 // Capacity ([MOE-128x8] 容量因子设计; [QWEN3-ROUTE] §四, tokens taken in order,
 // an expert accepts while below its capacity): the pair of rank r inside its
 // expert is kept iff r < capacity, i.e. each expert keeps its first
@@ -24,7 +25,7 @@
 // token routed to fewer than k experts): it is not a pair and gets
 // pair_pos = -1.
 // No device-to-host traffic; everything stays on the stream.
-#include "moe_internal.h"
+#include "aux_small.h"
 
 namespace moe {
 
@@ -170,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
 __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
     int P, int E, int cap, const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dropped, int scatter,
-    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos, int do_aux,
+    AuxSmallArgs aux) {
   __shared__ int s_h[256];
   __shared__ int s_c[256];
   __shared__ int s_off[256];
@@ -202,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
     if (offsets && e == E - 1) offsets[E] = s_c[e];
   }
   if (dropped && e == 0) *dropped = s_drop;
-  if (!scatter) return;  // block-uniform
+  if (do_aux) aux_small_body(aux, e < E ? tot : 0);  // block-uniform
+  if (!scatter) return;                              // block-uniform
   s_off[e] = excl;
   s_h[e] = 0;  // becomes the running rank of each expert
   __syncthreads();
@@ -224,7 +227,8 @@ hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t
   const int nch = dispatch_num_chunks(c);
   if (nch == 1) {
     dispatch_single_kernel<<<1, kThreads, 0, s>>>(P, E, capacity, topk_idx, counts, offsets,
-                                                  dropped, scatter ? 1 : 0, sorted_pair, pair_pos);
+                                                  dropped, scatter ? 1 : 0, sorted_pair, pair_pos,
+                                                  0, AuxSmallArgs{});
     return hipGetLastError();
   }
   dispatch_hist_kernel<<<nch, kThreads, 0, s>>>(P, E, topk_idx, hist);
@@ -233,6 +237,20 @@ hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t
   if (scatter)
     dispatch_scatter_kernel<<<nch, kThreads, 0, s>>>(P, E, capacity, topk_idx, rank0, offsets,
                                                      sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_aux(const moe_config& c, const int32_t* topk_idx, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               int32_t* hist, int32_t* rank0, int capacity, int32_t* dropped,
+                               const AuxSmallArgs& aux, bool* fused, hipStream_t s) {
+  *fused = dispatch_num_chunks(c) == 1;
+  if (!*fused)
+    return launch_dispatch(c, topk_idx, counts, offsets, sorted_pair, pair_pos, hist, rank0, true,
+                           capacity, dropped, s);
+  dispatch_single_kernel<<<1, kThreads, 0, s>>>(c.num_tokens * c.top_k, c.num_experts, capacity,
+                                                topk_idx, counts, offsets, dropped, 1,
+                                                sorted_pair, pair_pos, 1, aux);
   return hipGetLastError();
 }
 

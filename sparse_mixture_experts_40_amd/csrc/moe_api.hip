@@ -5,7 +5,7 @@
 
 #include <cmath>
 
-#include "moe_internal.h"
+#include "aux_small.h"
 
 using namespace moe;
 
@@ -180,8 +180,18 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
     router_blocks = router_num_blocks(c, false);
   }
   if (st != MOE_OK) return st;
-  st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
-                                L.base, true, o.capacity, o.dropped, stream));
+  // with few router blocks and one dispatch chunk (decode batches) the
+  // statistics come out of the dispatch block itself
+  bool aux_done = false;
+  if ((want_aux || aux.z_loss) && aux_small_fits(c, router_blocks)) {
+    st = launched(launch_dispatch_aux(
+        c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist, L.base, o.capacity,
+        o.dropped, aux_small_args(c, L.partials, router_blocks, aux, ex.zpart, router_blocks),
+        &aux_done, stream));
+  } else {
+    st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
+                                  L.base, true, o.capacity, o.dropped, stream));
+  }
   if (st != MOE_OK) return st;
   if (w4) {
     st = launched(launch_gate_up_w4(c, x, L.sorted_pair, L.offsets, *w4, L.h, stream));
@@ -195,7 +205,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   if (st != MOE_OK) return st;
   st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
   if (st != MOE_OK) return st;
-  if (want_aux || aux.z_loss)
+  if ((want_aux || aux.z_loss) && !aux_done)
     st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, aux, stream, ex.zpart,
                              router_blocks));
   return st;
