@@ -146,6 +146,9 @@ EXPERT_SHAPES = [  # (T, H, E, k, I)
     (300, 256, 64, 8, 128),
     (41, 192, 40, 3, 320),
     (9, 64, 4, 1, 64),
+    # tiled GEMMs with several tiles per block and odd K-stage counts (7 and 5
+    # stages of 64): the LDS stage ring runs on from one tile into the next
+    (512, 448, 256, 4, 320),
 ]
 
 
