@@ -54,9 +54,9 @@ FETCH_SCALE = 1048576.0 / 524302.4
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("c0d26d3282615d2236a0a8b652fb62ce38fd6358e72396d3861d09cbe5cf063e",
+    "prefill128_bf16": ("f569da93d9a4ba92e69975a45e9acfe54e18d7da914d8fe90a12ae8c27feacb0",
                         3798049.5, 394143.9),
-    "decode128_bf16": ("c0d26d3282615d2236a0a8b652fb62ce38fd6358e72396d3861d09cbe5cf063e",
+    "decode128_bf16": ("f569da93d9a4ba92e69975a45e9acfe54e18d7da914d8fe90a12ae8c27feacb0",
                        542903.0, 1561.8),
 }
 

@@ -100,8 +100,9 @@ __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
   }
 }
 
-// One K stage of the pipeline: start the loads of stage (dA, dB), multiply
-// stage (cA, cB), wait for stage (nA, nB) and read its first fragments.
+// One K stage of the pipeline: start the loads of stage (dA, dB) (in two
+// halves, see below), multiply stage (cA, cB), wait for stage (nA, nB) and
+// read its first fragments.
 // Half of the last k step's MFMAs are issued after the stage barrier, so the
 // MFMA pipe stays busy while the wave waits at the barrier and while the next
 // stage's first fragments arrive from LDS. (On the last stage the "next"
@@ -503,8 +504,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
 }
 
 // tile height, K step, LDS stages (2 x 64 KB), waves per block, blocks per CU.
-// The stage ring also runs with BK = 32 and 4 stages (1.5x the bytes in
-// flight): gate/up was 8% slower at 128 experts x 16K tokens.
+// The gate/up kernel also runs with BK = 32 and 4 stages (1.5x the bytes in
+// flight; the down epilogue needs a 64 KB stage): 8% slower at 128 experts x
+// 16K tokens.
 constexpr int kGemmBM = 256, kGemmBK = 64, kGemmStages = 2, kGemmWaves = 8, kGemmOcc = 1;
 
 // ---- bf16 decode path (few rows per expert: weight streaming) -------------
