@@ -182,7 +182,9 @@ __device__ __forceinline__ void gemm_step(
 // The wait before a step's barrier lets the stages issued after the awaited
 // one stay in flight, and for the stages of this tile loaded before the
 // previous epilogue (kt < NST - 1 when the tile was prefetched) also st_allow,
-// a lower bound of that epilogue's stores: the counter completes in order.
+// the number of store instructions that epilogue issued: the counter
+// completes in order, so the stage has landed once no more than those stores
+// remain. The count must never exceed the stores actually issued.
 template <int BK, int BM, int NST, int NW, int MB, int NB, int MBV>
 __device__ __forceinline__ void tile_k(uint16_t* smem, int nk, int g0, bool pf, int st_allow,
                                        __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase,
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
                                                  s_scan, sorted_pair, wave, lane, cur, a_off,
                                                  b_off);
   bool staged = false;  // first NST - 1 stages of `cur` loaded by the previous tile
-  // store instructions this wave surely issued in the previous tile's
-  // epilogue, after those prefetched stages
+  // store instructions this wave issued in the previous tile's epilogue,
+  // after those prefetched stages (exact: see the epilogues)
   int st_after = 0;
   int g0 = 0;  // ring position (global stage index) of the tile's first K stage
   while (have) {
@@ -413,16 +415,40 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     // last (its reads finished before the last stage barrier), and the next
     // tile's first LDS writes are ordered by the barriers of its prologue and
     // first step.
+    // At the next tile's start the compiler waits for every outstanding load
+    // and store anyway (for the sorted_pair loads of the tile after it, and
+    // before the first fragment read, which it cannot tell apart from the
+    // prefetched stage's LDS writes), so the epilogue's stores do not stay in
+    // flight into the next tile. Both ways of avoiding that (the loads issued
+    // from inline asm, and the sorted_pair rows turned into offsets only
+    // before the tile's last step) measured 1-2% slower in an A/B in one
+    // process: every K step waits for its own stage (vmcnt(0)) in any case.
+    // The explicit waits alone are nevertheless correct (exact store counts).
     const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
 
     // epilogue: lane holds D[n][m], m = lane & 31, n = (r/4)*8 + (lane/32)*4 + r%4
     if constexpr (GATEUP) {
-    // per token block: 4 NB / 2 stores, issued at least when all 32 rows of
-    // the wave's block are in the tile
+    // Store instructions this wave issues: one per (token block, column
+    // group) in which lane 0 has a row inside the tile and a column inside
+    // the matrix. Lane 0 holds the block's first row and the group's first
+    // column, so exactly those instructions run with a non-empty exec mask;
+    // the others are branched over. The count must never exceed what is
+    // issued: the next tile's first wait lets that many operations stay in
+    // flight. Columns matter on an expert's last column tile when N_out is
+    // not a multiple of 128 (waves whose columns all lie past N_out store
+    // nothing there).
     st_after = 0;
+    {
+      int ncg = 0;  // column groups (nb, q) of this wave with a column inside the matrix
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      st_after += (row0 + wm * 32 + mb * 64 + 31 < row_end) ? 4 * (NB / 2) : 0;
+      for (int nb = 0; nb < NB / 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ncg += (n0 + wn * (NB / 2) * 32 + nb * 32 + q * 8 < N_out) ? 1 : 0;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        st_after += (row0 + wm * 32 + mb * 64 < row_end) ? ncg : 0;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = row0 + trow0 + mb * 64;
