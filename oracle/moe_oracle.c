@@ -74,7 +74,9 @@ int orc_logits(int T, int H, int E, int dtype, const void* x, const void* wr,
  *   w[t,j] = p[t,e_j] / sum_j' p[t,e_j']  if norm (Qwen3), else p[t,e_j]
  *   (Mixtral keeps the unrenormalised probabilities, [QWEN3-READ] §三).
  * forced_idx (nullable): use these experts instead of selecting (weights are
- * computed the same way from them).
+ * computed the same way from them). A negative forced id is an empty slot,
+ * as entropy-driven k leaves them ([QWEN3-ROUTE] §二): weight 0, and the
+ * renormalisation runs over the slots that hold an expert.
  * probs (nullable) receives the full softmax [T,E]. */
 int orc_route_sel(int T, int E, int k, int norm, const float* logits, const float* sel_bias,
                   const int32_t* forced_idx, int32_t* idx, double* w, double* probs);
@@ -108,7 +110,7 @@ int orc_route_sel(int T, int E, int k, int norm, const float* logits, const floa
     if (forced_idx) {
       for (int j = 0; j < k; ++j) {
         sel[j] = forced_idx[(size_t)t * k + j];
-        if (sel[j] < 0 || sel[j] >= E) bad = 1;
+        if (sel[j] >= E) bad = 1;
       }
     } else {
       /* k passes of "largest remaining key, lowest index on ties"; the key is
@@ -132,8 +134,13 @@ int orc_route_sel(int T, int E, int k, int norm, const float* logits, const floa
     }
     if (bad) continue;
     double psum = 0.0;
-    for (int j = 0; j < k; ++j) psum += exp((double)l[sel[j]] - m) / s;
+    for (int j = 0; j < k; ++j)
+      if (sel[j] >= 0) psum += exp((double)l[sel[j]] - m) / s;
     for (int j = 0; j < k; ++j) {
+      if (sel[j] < 0) { /* empty slot (forced routing only) */
+        w[(size_t)t * k + j] = 0.0;
+        continue;
+      }
       double p = exp((double)l[sel[j]] - m) / s;
       w[(size_t)t * k + j] = norm ? p / psum : p;
     }
@@ -529,8 +536,9 @@ int orc_aux(int T, int E, int k, const int32_t* counts, const double* probs, dou
  * NULL): logits -> route -> experts -> combine, [QWEN3-READ] forward code.
  * n = number of listed tokens. Outputs are per listed token:
  *   logits [n,E] fp32, idx [n,k], w [n,k], out [n,H] double.
- * forced_idx [n,k] (nullable) replaces the selection; keep [n,k] (nullable)
- * marks the slots a capacity limit kept (the others contribute nothing). */
+ * forced_idx [n,k] (nullable) replaces the selection (negative ids: empty
+ * slots, weight 0); keep [n,k] (nullable) marks the slots a capacity limit
+ * kept (the others contribute nothing). */
 int orc_forward_tokens(int T, int H, int E, int k, int I, int norm, int dtype, const void* x,
                        const void* wr, const float* bias, const void* wg, const void* wu,
                        const void* wd, int n, const int32_t* tokens, const int32_t* forced_idx,
@@ -555,7 +563,8 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int norm, int dtype, c
   for (int r = 0; r < n; ++r)
     for (int j = 0; j < k; ++j) {
       tok[r * k + j] = r;
-      ex[r * k + j] = idx[r * k + j];
+      /* an empty forced slot has weight 0: any expert's row serves */
+      ex[r * k + j] = idx[r * k + j] < 0 ? 0 : idx[r * k + j];
     }
   if (orc_expert_rows(H, I, dtype, xs, wg, wu, wd, n * k, tok, ex, round_h, y)) goto done;
   if (orc_combine_kept(n, H, k, w, y, keep, out)) goto done;

@@ -270,13 +270,14 @@ def forward_tokens(inp: dict, cfg, tokens=None, forced_idx=None, round_h: bool =
 
 
 def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_bias=None,
-                    keep=None, round_h: bool = False, k_min: int = 0):
+                    keep=None, round_h: bool = False, k_min: int = 0, forced_idx=None):
     """Block forward of the listed tokens with the router variants, composed
     from the steps above: logits (+ bias), noisy logits if `noise` [T,E] and
     `w_noise` [E,H] are given (the noise rows of the listed tokens are used),
     selection with the optional selection-only bias, experts, combine over
-    the kept slots. Returns dict(logits (the ones the softmax saw), idx, w,
-    out)."""
+    the kept slots. forced_idx [n,k] (optional) replaces the selection (with
+    k_min: negative ids are the empty slots). Returns dict(logits (the ones
+    the softmax saw), idx, w, out)."""
     x = _c(inp["x"])
     T = x.shape[0]
     if tokens is None:
@@ -288,7 +289,12 @@ def forward_variant(inp: dict, cfg, tokens=None, noise=None, w_noise=None, sel_b
         nlg = logits(xs, w_noise)
         lg = noisy_logits(lg, nlg, np.asarray(noise, np.float32)[tokens])
     kt = None
-    if k_min:  # entropy-driven k (no selection bias with it)
+    if forced_idx is not None:
+        idx, w, _ = route(lg, cfg.k, cfg.norm, forced_idx=forced_idx)
+        live = idx >= 0
+        keep = live if keep is None else (np.asarray(keep, bool) & live)
+        kt = live.sum(1).astype(np.int32)
+    elif k_min:  # entropy-driven k (no selection bias with it)
         assert sel_bias is None
         idx, w, kt, _ = route_dynamic(lg, cfg.k, k_min, cfg.norm)
         live = idx >= 0
@@ -347,9 +353,11 @@ def expert_rows_f64w(x, wg, wu, wd, tok, ex) -> np.ndarray:
     return y
 
 
-def forward_w4(inp: dict, w4: dict, cfg, tokens=None, round_h: bool = False, keep=None):
+def forward_w4(inp: dict, w4: dict, cfg, tokens=None, round_h: bool = False, keep=None,
+               forced_idx=None):
     """Block forward of the listed tokens with 4-bit expert weights (router as
-    forward_variant, experts dequantised element by element)."""
+    forward_variant, experts dequantised element by element); forced_idx
+    [n,k] (optional) replaces the selection."""
     x = _c(inp["x"])
     T = x.shape[0]
     if tokens is None:
@@ -357,7 +365,7 @@ def forward_w4(inp: dict, w4: dict, cfg, tokens=None, round_h: bool = False, kee
     tokens = _c(tokens, np.int32)
     xs = np.ascontiguousarray(x[tokens])
     lg = logits(xs, inp["w_router"], inp.get("logit_bias"))
-    idx, w, _ = route(lg, cfg.k, cfg.norm)
+    idx, w, _ = route(lg, cfg.k, cfg.norm, forced_idx=forced_idx)
     n = tokens.shape[0]
     tok = np.repeat(np.arange(n, dtype=np.int32), cfg.k)
     y = expert_rows_w4(xs, w4, tok, idx.ravel(), round_h=round_h)

@@ -126,13 +126,16 @@ def check_capacity_block(orc, cfg, inp, cf, tokens):
     assert keep_diff <= 2 * cfg.k * len(mism), (keep_diff, len(mism))
     if len(mism) == 0:
         assert keep_diff == 0 and g_drop == o_drop
-    ok = ~((g_idx != o_idx).any(1) | (g_keep != o_keep).any(1))
-    sel = tokens[ok[tokens]]
-    r = orc.forward_tokens(inp, cfg, tokens=sel, keep=o_keep[sel])
-    mx, rm = check_output(host(blk.out)[sel], r["out"], cfg.dtype)
+    # every listed token against the oracle run with the GPU's selection and
+    # the keep mask that selection implies (the oracle's own, wherever the
+    # selections agree and no earlier near tie moved a capacity boundary)
+    r = orc.forward_tokens(inp, cfg, tokens=tokens, forced_idx=g_idx[tokens],
+                           keep=g_keep[tokens])
+    np.testing.assert_allclose(host(blk.topk_w)[tokens], r["w"], rtol=0, atol=1e-5)
+    mx, rm = check_output(host(blk.out)[tokens], r["out"], cfg.dtype)
     print(f"{cfg.name} cf={cf} cap={cap}: dropped {g_drop}/{cfg.T * cfg.k}, selection "
-          f"mismatches {len(mism)}, keep differences {keep_diff}, compared {len(sel)} tokens, "
-          f"max|d|/RMS {mx:.4f}", flush=True)
+          f"mismatches {len(mism)}, keep differences {keep_diff}, compared {len(tokens)} "
+          f"tokens, max|d|/RMS {mx:.4f}", flush=True)
     return g_drop
 
 

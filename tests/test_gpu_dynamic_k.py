@@ -93,6 +93,13 @@ def check_dynamic_block(orc, cfg, inp, k_min, tokens, cap=0):
     # selections of tokens with the same k_t: equal sets except on near ties
     for t in np.flatnonzero(same_kt & (g_idx != o_idx).any(1)):
         check_selection_row(lg[t], g_idx[t][: o_kt[t]], o_idx[t][: o_kt[t]], int(o_kt[t]), t)
+    # a token whose k_t differs (on an integer boundary) keeps the first g_kt
+    # experts of the oracle's full order, with the same near-tie rule
+    full_idx, _, _ = orc.route(lg, cfg.k, cfg.norm)
+    for t in np.flatnonzero(~same_kt):
+        kt = int(g_kt[t])
+        assert (g_idx[t][kt:] == -1).all()
+        check_selection_row(lg[t], g_idx[t][:kt], full_idx[t][:kt], kt, t)
     ok = same_kt & (g_idx == o_idx).all(1)
     live = g_idx >= 0
     counts = host(blk.counts)
@@ -102,16 +109,23 @@ def check_dynamic_block(orc, cfg, inp, k_min, tokens, cap=0):
     keep = live.copy()
     if cap:
         _, _, _, pp, dropped = orc.dispatch_capacity(o_idx, cfg.E, cap)
-        keep = (pp >= 0).reshape(o_idx.shape)
         if ok.all():
             assert int(host(blk.dropped)[0]) == dropped
-    sel = tokens[ok[tokens]]
-    r = orc.forward_variant(inp, cfg, tokens=sel, k_min=k_min, keep=keep[sel])
-    np.testing.assert_allclose(host(blk.topk_w)[sel], r["w"], rtol=0, atol=1e-5)
-    mx, rm = check_output(host(blk.out)[sel], r["out"], cfg.dtype)
+        # the keep mask the GPU's own selection implies (the oracle's own
+        # wherever the selections agree)
+        _, _, _, gpp, g_dropped = orc.dispatch_capacity(g_idx, cfg.E, cap)
+        assert int(host(blk.dropped)[0]) == g_dropped
+        keep = (gpp >= 0).reshape(g_idx.shape)
+    # the k_t and near-tie differences checked above are the only allowed
+    # ones: every listed token is compared with the oracle run on the GPU's
+    # selection (its empty slots included)
+    r = orc.forward_variant(inp, cfg, tokens=tokens, forced_idx=g_idx[tokens], keep=keep[tokens])
+    np.testing.assert_allclose(host(blk.topk_w)[tokens], r["w"], rtol=0, atol=1e-5)
+    mx, rm = check_output(host(blk.out)[tokens], r["out"], cfg.dtype)
     print(f"{cfg.name} k_min={k_min} cap={cap}: k_t histogram "
           f"{np.bincount(g_kt, minlength=cfg.k + 1)[k_min:].tolist()}, k_t differences "
-          f"{int((~same_kt).sum())}, compared {len(sel)} tokens, max|d|/RMS {mx:.4f}", flush=True)
+          f"{int((~same_kt).sum())}, near ties {int((same_kt & ~ok).sum())}, compared "
+          f"{len(tokens)} tokens, max|d|/RMS {mx:.4f}", flush=True)
     return blk
 
 

@@ -30,11 +30,11 @@ def test_full_size_block(orc, name):
 
     tokens = sample_tokens(cfg.T, 48, seed=1)
     gi, gw = host(blk.topk_idx), host(blk.topk_w)
-    r, match = compare_selection(orc, cfg, inp, tokens, gi[tokens], gw[tokens])
-    mx, rm = check_output(host(blk.out)[tokens][match], r["out"][match], cfg.dtype)
+    r, nmis = compare_selection(orc, cfg, inp, tokens, gi[tokens], gw[tokens])
+    mx, rm = check_output(host(blk.out)[tokens], r["out"], cfg.dtype)
     np.testing.assert_allclose(host(blk.logits)[tokens], r["logits"], rtol=0, atol=5e-5)
-    print(f"[{name}] sampled {len(tokens)} tokens: selection mismatches {int((~match).sum())}, "
-          f"max|d|/RMS {mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
+    print(f"[{name}] sampled {len(tokens)} tokens: near-tie selections {nmis} (compared with "
+          f"forced routing), max|d|/RMS {mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
 
     # properties over all tokens
     T, E, k = cfg.T, cfg.E, cfg.k

@@ -126,6 +126,33 @@ def test_forced_routing_weights(orc):
     np.testing.assert_allclose(w, pf / pf.sum(1, keepdims=True), rtol=1e-12)
 
 
+@pytest.mark.parametrize("norm", [True, False])
+def test_forced_routing_with_empty_slots(orc, norm):
+    """Forced routing with empty slots (-1, as entropy-driven k leaves them):
+    weight 0 there, the others scipy softmax probabilities, renormalised over
+    the live slots when norm; forcing the dynamic router's own selection gives
+    back its weights."""
+    rng = _rng(8)
+    T, E, k = 12, 10, 4
+    lg = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    forced = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    nlive = rng.integers(1, k + 1, T)
+    for t in range(T):
+        forced[t, nlive[t]:] = -1
+    idx, w, _ = orc.route(lg, k, norm=norm, forced_idx=forced)
+    assert (idx == forced).all()
+    live = forced >= 0
+    assert (w[~live] == 0.0).all()
+    full = sp_softmax(lg.astype(np.float64), axis=1)
+    pf = np.where(live, np.take_along_axis(full, np.maximum(forced, 0).astype(np.int64), 1), 0.0)
+    ref = pf / pf.sum(1, keepdims=True) if norm else pf
+    np.testing.assert_allclose(w, ref, rtol=1e-12)
+    d_idx, d_w, _, _ = orc.route_dynamic(lg, k, 2, norm)
+    f_idx, f_w, _ = orc.route(lg, k, norm=norm, forced_idx=d_idx)
+    assert (f_idx == d_idx).all()
+    np.testing.assert_allclose(f_w, d_w, rtol=1e-12, atol=0)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_logits_match_numpy_matmul(orc, dtype):
     cfg = MoEConfig("t", T=33, H=192, E=12, k=3, I=64, norm=True, dtype=dtype, zipf_s=1.2)
@@ -384,6 +411,25 @@ def test_forward_keep_mask(orc):
                                       for n in ("w_gate", "w_up", "w_down")))
         np.testing.assert_allclose(top["out"][t], full["w"][t, 0] * mlp[0], rtol=1e-10,
                                    atol=1e-12)
+
+
+def test_forward_forced_single_live_slot(orc):
+    """Forced routing with one live slot and renormalisation: the weight is 1
+    and the output is that expert's MLP (numpy matmuls), wherever the live
+    slot sits; the empty slots contribute nothing."""
+    cfg = MoEConfig("forced1", T=9, H=64, E=6, k=3, I=64, norm=True, dtype="f32")
+    inp = make_inputs(cfg, seed=5)
+    forced = np.full((cfg.T, cfg.k), -1, np.int32)
+    ex = np.arange(cfg.T, dtype=np.int32) % cfg.E
+    forced[np.arange(cfg.T), np.arange(cfg.T) % cfg.k] = ex
+    r = orc.forward_tokens(inp, cfg, forced_idx=forced)
+    assert (r["idx"] == forced).all()
+    np.testing.assert_allclose(r["w"].sum(1), 1.0, rtol=1e-15)
+    x = as_f32(inp["x"]).astype(np.float64)
+    for t in range(cfg.T):
+        mlp = _swiglu_np(x[t:t + 1], *(as_f32(inp[n][ex[t]]).astype(np.float64)
+                                      for n in ("w_gate", "w_up", "w_down")))
+        np.testing.assert_allclose(r["out"][t], mlp[0], rtol=1e-10, atol=1e-12)
 
 
 # ------------------------------------------------------------- 4-bit weights
