@@ -82,7 +82,6 @@ typedef struct {
 } moe_config;
 
 /* Load-balance outputs; every field may be NULL (then it is not written).
- * z_loss is described at the field.
  *   counts[E] int32 : n_e = number of pairs routed to expert e
  *   f[E]      fp32  : f_e = n_e / sum_e' n_e', the fraction of routed pairs
  *                     (= n_e / (T*k) unless some slots are empty)
@@ -95,10 +94,6 @@ typedef struct {
   float* f;
   float* P;
   float* aux;
-  float* z_loss; /* [1] fp32: (1/T) sum_t (ln sum_e exp l[t,e])^2 over the logits the
-                    softmax used. [MOE-128x8] (challenge 3: a router z-loss for
-                    training stability) names the statistic without a formula;
-                    this is the form taken. */
 } moe_aux_out;
 
 /* Options of moe_layer_forward_ex / moe_router_topk_ex. Zero-initialised =
@@ -135,6 +130,11 @@ typedef struct {
    * select_bias (MOE_ERR_UNSUPPORTED). */
   int32_t dynamic_k_min;
   int32_t* k_per_token; /* [T] int32 out or NULL: k_t of every token */
+  /* [1] fp32 out or NULL: the router z-loss (1/T) sum_t (ln sum_e exp l[t,e])^2
+   * over the logits the softmax used (noisy ones with noise). [MOE-128x8]
+   * (challenge 3: a router z-loss for training stability) names the
+   * statistic without a formula; this is the form taken (see moe_z_loss). */
+  float* z_loss;
 } moe_options;
 
 /* 4-bit group-quantised expert weights, [MOE-128x8] 参数量化与存储优化 (4-bit
@@ -315,6 +315,14 @@ moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const int32_
 moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32_t* topk_idx,
                          moe_aux_out out, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Router z-loss from logits: z_loss[0] = (1/T) sum_t (ln sum_e exp l[t,e])^2
+ * (fp32 out), with ln sum exp taken stably (max subtracted) and the sum over
+ * tokens in a fixed order. [MOE-128x8] (challenge 3) names a router z-loss
+ * for training stability but gives no formula; this is the form taken.
+ *   logits [T,E] fp32 (bias included); workspace of moe_workspace_size. */
+moe_status moe_z_loss(const moe_config* cfg, const float* logits, float* z_loss,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 
 /* The whole block: router -> dispatch -> experts -> combine -> statistics,

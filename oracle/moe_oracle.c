@@ -17,6 +17,10 @@
  *   [LAB17]       "项目 17：稀疏性的调度艺术：实现双专家 MoE 路由" (sshipanoo),
  *                 第二阶段 实现流程.
  *
+ * Parity unpinned: orc_z_loss (the page names the statistic without a
+ * formula; see there). Every other function is pinned by the CPU tests to
+ * something outside itself.
+ *
  * Element types: dtype 0 = fp32 array, dtype 1 = bf16 array given as the
  * 16-bit patterns (widened to double exactly).
  * All functions return 0 on success, -1 on a bad argument.
@@ -214,7 +218,9 @@ int orc_noisy_logits(int T, int E, const float* logits, const float* nlogits, co
 /* Router z-loss statistic. [MOE-128x8] names a router z-loss for training
  * stability without a formula; the one taken here is the mean over tokens of
  * the squared log-sum-exp of the router logits:
- *   z = (1/T) sum_t ( ln sum_e exp(l[t,e]) )^2 */
+ *   z = (1/T) sum_t ( ln sum_e exp(l[t,e]) )^2
+ * PARITY UNPINNED: the page fixes no formula, so the pins (closed forms,
+ * scipy logsumexp) check only this chosen definition. */
 int orc_z_loss(int T, int E, const float* logits, double* z) {
   if (T < 1 || E < 1 || !logits || !z) return -1;
   double acc = 0.0;

@@ -24,7 +24,7 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_router_topk_ex",
            "moe_dispatch",
            "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
-           "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_layer_forward",
+           "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_z_loss", "moe_layer_forward",
            "moe_layer_forward_ex", "moe_expert_gate_up_w4", "moe_expert_down_w4",
            "moe_layer_forward_w4")
 
@@ -40,7 +40,7 @@ class moe_options(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p),
                 ("noise", ctypes.c_void_p), ("w_noise", ctypes.c_void_p),
                 ("select_bias", ctypes.c_void_p), ("dynamic_k_min", ctypes.c_int32),
-                ("k_per_token", ctypes.c_void_p)]
+                ("k_per_token", ctypes.c_void_p), ("z_loss", ctypes.c_void_p)]
 
 
 class moe_w4_weights(ctypes.Structure):
@@ -51,7 +51,7 @@ class moe_w4_weights(ctypes.Structure):
 
 class moe_aux_out(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("f", ctypes.c_void_p), ("P", ctypes.c_void_p),
-                ("aux", ctypes.c_void_p), ("z_loss", ctypes.c_void_p)]
+                ("aux", ctypes.c_void_p)]
 
 
 _lib = None
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "moe_expert_swiglu": [C, V, V, V, V, V, V, V, V, S, V],
         "moe_combine": [C, V, V, V, V, V],
         "moe_aux_stats": [C, V, V, moe_aux_out, V, S, V],
+        "moe_z_loss": [C, V, V, V, S, V],
         "moe_layer_forward": [C, V, V, V, V, V, V, V, V, V, V, moe_aux_out, V, S, V],
         "moe_layer_forward_ex": [C, ctypes.POINTER(moe_options), V, V, V, V, V, V, V, V, V, V,
                                  moe_aux_out, V, S, V],
@@ -142,10 +143,10 @@ def router_topk(c: moe_config, x, w_router, logit_bias, logits, topk_idx, topk_w
 
 
 def options(capacity: int = 0, dropped=None, noise=None, w_noise=None, select_bias=None,
-            dynamic_k_min: int = 0, k_per_token=None) -> moe_options:
+            dynamic_k_min: int = 0, k_per_token=None, z_loss=None) -> moe_options:
     """moe_options from tensors (the tensors must outlive the calls)."""
     return moe_options(int(capacity), _ptr(dropped), _ptr(noise), _ptr(w_noise),
-                       _ptr(select_bias), int(dynamic_k_min), _ptr(k_per_token))
+                       _ptr(select_bias), int(dynamic_k_min), _ptr(k_per_token), _ptr(z_loss))
 
 
 def router_topk_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, logits,
@@ -202,16 +203,23 @@ def combine(c: moe_config, y_sorted, pair_pos, topk_w, out):
                               _ptr(out), _stream()), "moe_combine")
 
 
-def _aux(counts=None, f=None, P=None, aux=None, z_loss=None) -> moe_aux_out:
-    return moe_aux_out(_ptr(counts), _ptr(f), _ptr(P), _ptr(aux), _ptr(z_loss))
+def _aux(counts=None, f=None, P=None, aux=None) -> moe_aux_out:
+    return moe_aux_out(_ptr(counts), _ptr(f), _ptr(P), _ptr(aux))
 
 
 def aux_stats(c: moe_config, logits, topk_idx, ws, counts=None, f=None, P=None, aux=None,
               z_loss=None):
+    """moe_aux_stats, and moe_z_loss when z_loss is given."""
     _check(load().moe_aux_stats(ctypes.byref(c), _ptr(logits), _ptr(topk_idx),
-                                _aux(counts, f, P, aux, z_loss), _ptr(ws), ws.numel(),
-                                _stream()),
+                                _aux(counts, f, P, aux), _ptr(ws), ws.numel(), _stream()),
            "moe_aux_stats")
+    if z_loss is not None:
+        z_loss_stat(c, logits, z_loss, ws)
+
+
+def z_loss_stat(c: moe_config, logits, z_loss, ws):
+    _check(load().moe_z_loss(ctypes.byref(c), _ptr(logits), _ptr(z_loss), _ptr(ws), ws.numel(),
+                             _stream()), "moe_z_loss")
 
 
 def layer_forward(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, out, ws,
@@ -224,14 +232,25 @@ def layer_forward(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, 
            "moe_layer_forward")
 
 
+def _with_z_loss(opts: moe_options | None, z_loss) -> moe_options | None:
+    """opts with its z_loss output set to z_loss (a copy; opts is unchanged)."""
+    if z_loss is None:
+        return opts
+    o = moe_options()
+    if opts is not None:
+        ctypes.pointer(o)[0] = opts
+    o.z_loss = _ptr(z_loss)
+    return o
+
+
 def layer_forward_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, w_gate,
                      w_up, w_down, out, ws, router_logits=None, topk_idx=None, topk_w=None,
                      counts=None, f=None, P=None, aux=None, z_loss=None):
+    opts = _with_z_loss(opts, z_loss)
     _check(load().moe_layer_forward_ex(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
                                        _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate),
                                        _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(router_logits),
-                                       _ptr(topk_idx), _ptr(topk_w),
-                                       _aux(counts, f, P, aux, z_loss),
+                                       _ptr(topk_idx), _ptr(topk_w), _aux(counts, f, P, aux),
                                        _ptr(ws), ws.numel(), _stream()),
            "moe_layer_forward_ex")
 
@@ -270,10 +289,11 @@ def expert_down_w4(c: moe_config, h, offsets, w4: moe_w4_weights, y_sorted):
 def layer_forward_w4(c: moe_config, opts: moe_options | None, x, w_router, logit_bias,
                      w4: moe_w4_weights, out, ws, router_logits=None, topk_idx=None, topk_w=None,
                      counts=None, f=None, P=None, aux=None, z_loss=None):
+    opts = _with_z_loss(opts, z_loss)
     _check(load().moe_layer_forward_w4(ctypes.byref(c), None if opts is None else ctypes.byref(opts),
                                        _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(w4),
                                        _ptr(out), _ptr(router_logits), _ptr(topk_idx),
-                                       _ptr(topk_w), _aux(counts, f, P, aux, z_loss), _ptr(ws),
+                                       _ptr(topk_w), _aux(counts, f, P, aux), _ptr(ws),
                                        ws.numel(), _stream()),
            "moe_layer_forward_w4")
 

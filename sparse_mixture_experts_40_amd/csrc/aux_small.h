@@ -85,7 +85,7 @@ __device__ __forceinline__ void aux_small_body(const AuxSmallArgs& a, int n) {
 // (then launch_dispatch_aux may produce them with a one-chunk dispatch).
 bool aux_small_fits(const moe_config& c, int n_partials);
 AuxSmallArgs aux_small_args(const moe_config& c, const float* prob_partials, int n_partials,
-                            moe_aux_out out, const float* zpart, int n_zpart);
+                            const AuxOut& out, const float* zpart, int n_zpart);
 
 // launch_dispatch, and for a one-chunk dispatch the statistics in the same
 // block (*fused = true); otherwise only the dispatch (*fused = false).

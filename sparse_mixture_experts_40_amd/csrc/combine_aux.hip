@@ -181,7 +181,7 @@ bool aux_small_fits(const moe_config& c, int n_partials) {
 }
 
 AuxSmallArgs aux_small_args(const moe_config& c, const float* prob_partials, int n_partials,
-                            moe_aux_out out, const float* zpart, int n_zpart) {
+                            const AuxOut& out, const float* zpart, int n_zpart) {
   const bool stats = out.counts || out.f || out.P || out.aux;
   return AuxSmallArgs{c.num_tokens, c.num_experts, stats ? 1 : 0, prob_partials, n_partials,
                       out.counts, out.f, out.P, zpart, n_zpart, out.aux,
@@ -189,7 +189,7 @@ AuxSmallArgs aux_small_args(const moe_config& c, const float* prob_partials, int
 }
 
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s,
+                      int n_partials, double* fp_scratch, const AuxOut& out, hipStream_t s,
                       const float* zpart, int n_zpart) {
   const bool stats = out.counts || out.f || out.P || out.aux;
   float* z_out = zpart ? out.z_loss : nullptr;

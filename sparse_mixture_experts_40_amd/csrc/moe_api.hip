@@ -150,11 +150,12 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   const moe_config& c = *cfg;
   int32_t* idx = topk_idx ? topk_idx : L.idx;
   float* w = topk_w ? topk_w : L.w;
-  const bool want_aux = aux.counts || aux.f || aux.P || aux.aux;
+  const AuxOut ao{aux.counts, aux.f, aux.P, aux.aux, o.z_loss};
+  const bool want_aux = ao.counts || ao.f || ao.P || ao.aux;
   float* partials = want_aux ? L.partials : nullptr;
   RouterExtras ex;
   ex.sel_bias = o.select_bias;
-  ex.zpart = aux.z_loss ? L.zpart : nullptr;
+  ex.zpart = ao.z_loss ? L.zpart : nullptr;
   ex.k_min = o.dynamic_k_min;
   ex.kt_out = o.k_per_token;
 
@@ -183,10 +184,10 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   // with few router blocks and one dispatch chunk (decode batches) the
   // statistics come out of the dispatch block itself
   bool aux_done = false;
-  if ((want_aux || aux.z_loss) && aux_small_fits(c, router_blocks)) {
+  if ((want_aux || ao.z_loss) && aux_small_fits(c, router_blocks)) {
     st = launched(launch_dispatch_aux(
         c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist, L.base, o.capacity,
-        o.dropped, aux_small_args(c, L.partials, router_blocks, aux, ex.zpart, router_blocks),
+        o.dropped, aux_small_args(c, L.partials, router_blocks, ao, ex.zpart, router_blocks),
         &aux_done, stream));
   } else {
     st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
@@ -205,8 +206,8 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   if (st != MOE_OK) return st;
   st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
   if (st != MOE_OK) return st;
-  if ((want_aux || aux.z_loss) && !aux_done)
-    st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, aux, stream, ex.zpart,
+  if ((want_aux || ao.z_loss) && !aux_done)
+    st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, ao, stream, ex.zpart,
                              router_blocks));
   return st;
 }
@@ -374,19 +375,38 @@ moe_status moe_aux_stats(const moe_config* cfg, const float* logits, const int32
   if (!logits || !topk_idx) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = carve(*cfg, workspace);
   if (!workspace || workspace_bytes < L.aux_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!out.counts && !out.f && !out.P && !out.aux && !out.z_loss) return MOE_OK;
-  // per-block softmax (and z-loss) sums from the logits (selection skipped)
-  RouterExtras ex;
-  ex.zpart = out.z_loss ? L.zpart : nullptr;
+  if (!out.counts && !out.f && !out.P && !out.aux) return MOE_OK;
+  // per-block softmax sums from the logits (selection skipped)
   st = launched(launch_router(*cfg, nullptr, nullptr, nullptr, const_cast<float*>(logits), false,
-                              L.idx, L.w, L.partials, false, stream, ex));
+                              L.idx, L.w, L.partials, false, stream));
   if (st != MOE_OK) return st;
   // expert counts from the given selection (histogram + scan only)
   st = launched(launch_dispatch(*cfg, topk_idx, L.counts, L.offsets, nullptr, nullptr, L.hist,
                                 nullptr, false, 0, nullptr, stream));
   if (st != MOE_OK) return st;
   const int nb = router_num_blocks(*cfg, true);
-  return launched(launch_aux(*cfg, L.counts, L.partials, nb, L.fp, out, stream, ex.zpart, nb));
+  const AuxOut ao{out.counts, out.f, out.P, out.aux, nullptr};
+  return launched(launch_aux(*cfg, L.counts, L.partials, nb, L.fp, ao, stream));
+}
+
+moe_status moe_z_loss(const moe_config* cfg, const float* logits, float* z_loss,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!logits || !z_loss) return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = carve(*cfg, workspace);
+  if (!workspace || workspace_bytes < L.aux_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  // per-block sums of (ln sum_e exp l)^2 from the logits (selection skipped),
+  // then their fixed-order total
+  RouterExtras ex;
+  ex.zpart = L.zpart;
+  st = launched(launch_router(*cfg, nullptr, nullptr, nullptr, const_cast<float*>(logits), false,
+                              L.idx, L.w, nullptr, false, stream, ex));
+  if (st != MOE_OK) return st;
+  const int nb = router_num_blocks(*cfg, true);
+  AuxOut ao;
+  ao.z_loss = z_loss;
+  return launched(launch_aux(*cfg, L.counts, L.partials, nb, L.fp, ao, stream, L.zpart, nb));
 }
 
 moe_status moe_layer_forward_ex(const moe_config* cfg, const moe_options* opt, const void* x,

@@ -242,6 +242,16 @@ hipError_t launch_gate_up_w4(const moe_config& c, const void* x, const int32_t* 
 hipError_t launch_down_w4(const moe_config& c, const void* h, const int32_t* offsets,
                           const moe_w4_weights& w, void* y, hipStream_t s);
 
+// Statistics outputs inside the library: the public moe_aux_out plus the
+// z-loss output of moe_options (each nullable).
+struct AuxOut {
+  int32_t* counts = nullptr;
+  float* f = nullptr;
+  float* P = nullptr;
+  float* aux = nullptr;
+  float* z_loss = nullptr;
+};
+
 // Combine and statistics.
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
                           const float* topk_w, void* out, hipStream_t s);
@@ -249,7 +259,7 @@ hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pai
 // zpart [n_zpart] (nullable): per router block sums of (ln sum_e exp l)^2 for
 // out.z_loss.
 hipError_t launch_aux(const moe_config& c, const int32_t* counts, const float* prob_partials,
-                      int n_partials, double* fp_scratch, moe_aux_out out, hipStream_t s,
+                      int n_partials, double* fp_scratch, const AuxOut& out, hipStream_t s,
                       const float* zpart = nullptr, int n_zpart = 0);
 
 }  // namespace moe

@@ -127,3 +127,35 @@ def test_w4_validation(lib):
     ws = ctypes.c_void_p(256)
     assert lib.moe_layer_forward_w4(ctypes.byref(ok), None, d, d, None, ctypes.byref(w4), d, None,
                                     None, None, binding.moe_aux_out(), ws, 16, None) == 3
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes structs of the binding have the sizes and field offsets a C
+    compiler gives the structs of include/moe.h (moe_aux_out is the four
+    statistics pointers: counts, f, P, aux)."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    structs = {"moe_config": binding.moe_config, "moe_options": binding.moe_options,
+               "moe_aux_out": binding.moe_aux_out, "moe_w4_weights": binding.moe_w4_weights}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{fname} %zu\\n", offsetof({name}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    # the HIP runtime header, compiled by a plain C compiler, takes the
+    # preprocessor flags ROCm gives for that (hipconfig --cpp_config)
+    hip_cpp = subprocess.run(["hipconfig", "--cpp_config"], capture_output=True, text=True,
+                             check=True).stdout.split()
+    subprocess.run(["gcc", "-std=c11", *hip_cpp, "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(got[f"{name} size"]) == ctypes.sizeof(cls), name
+        for fname, _ in cls._fields_:
+            assert int(got[f"{name}.{fname}"]) == getattr(cls, fname).offset, (name, fname)
+    assert [f for f, _ in binding.moe_aux_out._fields_] == ["counts", "f", "P", "aux"]
+

@@ -78,6 +78,8 @@ def test_noisy_router_from_x(orc, dtype, T, H, E, k):
 
 @pytest.mark.parametrize("T,E", [(64, 8), (1000, 128), (77, 256), (3, 4)])
 def test_aux_stats_z_loss(orc, T, E):
+    """moe_z_loss against the oracle's z-loss. Parity unpinned: the page names
+    a router z-loss without a formula; both sides compute the one taken."""
     rng = np.random.default_rng(T + E)
     lg = (rng.standard_normal((T, E)) * 3).astype(np.float32)
     k = min(E, 4)

@@ -218,6 +218,8 @@ def test_noisy_logits_match_softplus_and_keep_topk_formula(orc):
 
 
 def test_z_loss_closed_forms(orc):
+    """Parity unpinned: MoE架构深度解析… (挑战3) names a router z-loss without a
+    formula, so this checks only the definition taken, (1/T) sum_t lse_t^2."""
     from scipy.special import logsumexp
     for E in (1, 8, 128):
         assert orc.z_loss(np.zeros((5, E), np.float32)) == pytest.approx(math.log(E) ** 2,
