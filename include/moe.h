@@ -35,7 +35,9 @@
  *  - The library never allocates device memory, never synchronises the host
  *    with the device, and keeps no mutable global state: all work is enqueued
  *    on `stream` in call order. Scratch space is the caller's `workspace`,
- *    of at least moe_workspace_size(cfg) bytes, 256-byte aligned.
+ *    of at least moe_workspace_size(cfg) bytes, 256-byte aligned. (The one
+ *    exception, moe_layer_forward_noalloc at the end, uses a scratch array
+ *    of the library's own instead, and caches its per-device address.)
  *  - Argument checks run on the host before any launch and return a status;
  *    on error nothing is enqueued. MOE_ERR_HIP means a launch failed
  *    (hipGetLastError); faults inside kernels surface at the caller's next
@@ -356,6 +358,34 @@ moe_status moe_layer_forward_w4(const moe_config* cfg, const moe_options* opt, c
                                 const moe_w4_weights* w, void* out, float* router_logits,
                                 int32_t* topk_idx, float* topk_w, moe_aux_out aux,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the library-owned scratch of moe_layer_forward_noalloc, per GPU. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (without workspace / workspace_bytes), kernels and results as
+ * moe_layer_forward: on the same inputs every output is bitwise identical.
+ * The scratch is a file-scope __device__ array of MOE_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; nothing in it
+ * needs to start at zero and no call allocates or frees (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *  - Limit: configurations whose moe_workspace_size exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL before any
+ *    launch. Decode-sized batches fit (T = 64, H = 4096, E = 128, k = 8,
+ *    I = 1536 needs about 11 MB); prefill batches take moe_layer_forward.
+ *  - The first call on a device looks up the array's address on the current
+ *    device (hipGetSymbolAddress) and keeps it; make that first call outside
+ *    graph capture. The current device must be the stream's device.
+ *  - Every call on a GPU shares that GPU's array: calls that overlap on one
+ *    GPU (on different streams, or from several threads) race and give
+ *    undefined results; calls ordered on one stream do not.
+ *  - MOE_ERR_HIP if the address lookup fails. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* logit_bias, const void* w_gate,
+                                     const void* w_up, const void* w_down, void* out,
+                                     float* router_logits, int32_t* topk_idx, float* topk_w,
+                                     moe_aux_out aux, hipStream_t stream);
 
 #ifdef __cplusplus
 }

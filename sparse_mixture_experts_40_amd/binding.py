@@ -26,7 +26,10 @@ EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_ro
            "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_z_loss", "moe_layer_forward",
            "moe_layer_forward_ex", "moe_expert_gate_up_w4", "moe_expert_down_w4",
-           "moe_layer_forward_w4")
+           "moe_layer_forward_w4", "moe_layer_forward_noalloc")
+
+# bytes of the library-owned scratch of moe_layer_forward_noalloc (moe.h)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class moe_config(ctypes.Structure):
@@ -87,6 +90,7 @@ def load(path: str = LIB_PATH):
                                  moe_aux_out, V, S, V],
         "moe_expert_gate_up_w4": [C, V, V, V, ctypes.POINTER(moe_w4_weights), V, V],
         "moe_expert_down_w4": [C, V, V, ctypes.POINTER(moe_w4_weights), V, V],
+        "moe_layer_forward_noalloc": [C, V, V, V, V, V, V, V, V, V, V, moe_aux_out, V],
         "moe_layer_forward_w4": [C, ctypes.POINTER(moe_options), V, V, V,
                                  ctypes.POINTER(moe_w4_weights), V, V, V, V, moe_aux_out, V, S,
                                  V],
@@ -230,6 +234,18 @@ def layer_forward(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, 
                                     _ptr(router_logits), _ptr(topk_idx), _ptr(topk_w),
                                     _aux(counts, f, P, aux), _ptr(ws), ws.numel(), _stream()),
            "moe_layer_forward")
+
+
+def layer_forward_noalloc(c: moe_config, x, w_router, logit_bias, w_gate, w_up, w_down, out,
+                          router_logits=None, topk_idx=None, topk_w=None, counts=None, f=None,
+                          P=None, aux=None):
+    """moe_layer_forward without a workspace (the library's own scratch array)."""
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(c), _ptr(x), _ptr(w_router),
+                                            _ptr(logit_bias), _ptr(w_gate), _ptr(w_up),
+                                            _ptr(w_down), _ptr(out), _ptr(router_logits),
+                                            _ptr(topk_idx), _ptr(topk_w), _aux(counts, f, P, aux),
+                                            _stream()),
+           "moe_layer_forward_noalloc")
 
 
 def _with_z_loss(opts: moe_options | None, z_loss) -> moe_options | None:

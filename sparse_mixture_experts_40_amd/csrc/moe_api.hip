@@ -1,15 +1,46 @@
 // moe_api.hip — the C ABI of include/moe.h: argument checks, workspace
 // carving and the launch sequence on the caller's stream. No allocation, no
-// host synchronisation, no global state.
+// host synchronisation. The only global state is the per-device address of
+// the no-allocation entry point's scratch array (looked up once per device).
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "aux_small.h"
 
 using namespace moe;
 
+// Scratch of moe_layer_forward_noalloc, for callers that cannot allocate:
+// one copy per GPU, in the library's device code object. In host code this
+// name is a host-side stand-in, never a device address: the host uses only
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Per device: the device address of `scratch` (null until the first
+// moe_layer_forward_noalloc call on that device looks it up).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+moe_status noalloc_scratch(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MOE_ERR_HIP;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();  // leave no error behind for the next launch check
+      return MOE_ERR_HIP;
+    }
+    g_scratch_addr[dev].store(p, std::memory_order_release);  // same value from any thread
+  }
+  *addr = p;
+  return MOE_OK;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -458,6 +489,24 @@ moe_status moe_expert_down_w4(const moe_config* cfg, const void* h,
   if (st != MOE_OK) return st;
   if (!h || !expert_offsets || !y_sorted) return MOE_ERR_INVALID_ARGUMENT;
   return launched(launch_down_w4(*cfg, h, expert_offsets, *w, y_sorted, stream));
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                                     const float* logit_bias, const void* w_gate,
+                                     const void* w_up, const void* w_down, void* out,
+                                     float* router_logits, int32_t* topk_idx, float* topk_w,
+                                     moe_aux_out aux, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (carve(*cfg, nullptr).layer_end > MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return layer_forward_impl(cfg, nullptr, x, w_router, logit_bias, w_gate, w_up, w_down, nullptr,
+                            out, router_logits, topk_idx, topk_w, aux, ws,
+                            MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,

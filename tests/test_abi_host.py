@@ -159,3 +159,20 @@ def test_struct_layouts_match_header(tmp_path):
             assert int(got[f"{name}.{fname}"]) == getattr(cls, fname).offset, (name, fname)
     assert [f for f, _ in binding.moe_aux_out._fields_] == ["counts", "f", "P", "aux"]
 
+
+def test_noalloc_rejects_before_any_launch(lib):
+    """moe_layer_forward_noalloc: bad arguments and configurations whose
+    workspace exceeds the library's scratch return a status on the host."""
+    d = ctypes.c_void_p(16)  # never dereferenced: checks fail first
+    aux = binding.moe_aux_out()
+    big = binding.make_config(WORKLOADS["prefill128_bf16"])
+    assert binding.workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(big), d, d, None, d, d, d, d, None, None,
+                                         None, aux, None) == 3
+    small = binding.make_config(WORKLOADS["decode128_bf16"])
+    assert binding.workspace_size(small) <= binding.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(small), d, None, None, d, d, d, d, None,
+                                         None, None, aux, None) == 1
+    bad = binding.moe_config(16, 64, 8, 9, 64, 1, 1)  # k > E
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(bad), d, d, None, d, d, d, d, None, None,
+                                         None, aux, None) == 1
