@@ -1,6 +1,7 @@
 """Benchmark of the MoE block forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--decode-workload NAME|none] [--decode-steps N]
                     [--capacity-factor CF]   # capacity-limited dispatch, C = ceil(T*k*CF/E)
                     [--router noise|bias|noise+bias]   # router variants (seeded inputs)
                     [--dynamic-k-min KMIN]   # entropy-driven k in [KMIN, k]
@@ -19,6 +20,12 @@ workloads the same steps (and the gate/up launch) with 512 MB of other data
 touched between them, outside the timed events: read (no weight byte can then
 come from the 256 MB MALL) and, separately, written (the MALL is then full of
 dirty lines that the next kernel's reads evict with write-backs).
+
+The default run also times the 64-token, 128-expert decode workload after the
+main one, and reports it as the line's "decode" object (ms/step, tokens/s, the
+layer's fraction of HBM bandwidth, the gate/up roofline, stages, and the
+MALL-scrubbed variants); `value` and the rest of the line stay the main
+workload's.
 """
 from __future__ import annotations
 
@@ -232,12 +239,231 @@ def time_per_call(torch, stream, fn, reps):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
 
 
+def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="plain",
+            dynamic_k_min=0):
+    """Everything the JSON line reports about one workload, except the CPU
+    baseline: the timed steps, the dominant kernel's roofline, the stages,
+    the clock, and for weight-streaming workloads the MALL-scrubbed variants.
+    Returns (report dict, inputs, 4-bit inputs or None)."""
+    from sparse_mixture_experts_40_amd.inputs import (make_inputs, make_router_variant_inputs,
+                                                      make_w4_inputs)
+    log(f"workload {cfg}")
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg, weights=not w4)
+    w4in = make_w4_inputs(cfg) if w4 else None
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    cap = binding.capacity(binding.make_config(cfg), cap_factor) if cap_factor > 0 else 0
+    var = make_router_variant_inputs(cfg) if router != "plain" else {}
+    blk = binding.MoEBlock(cfg, inp, capacity=cap,
+                           noise=var.get("noise") if "noise" in router else None,
+                           w_noise=var.get("w_noise") if "noise" in router else None,
+                           select_bias=var.get("select_bias") if "bias" in router else None,
+                           dynamic_k_min=dynamic_k_min, w4=w4in)
+    x = binding.to_device(inp["x"])
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        blk.forward(x)
+    torch.cuda.synchronize()
+
+    # the timed steps, one event before each (and one after the last)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    with ClockSampler(clock_files(torch)) as clk:
+        w0 = time.perf_counter()
+        for i in range(steps):
+            evs[i].record(stream)
+            blk.forward(x)
+        evs[steps].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    ms_step = evs[0].elapsed_time(evs[steps]) / steps
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    log(f"{cfg.name}: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / steps:.4f} ms/step")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    streaming = uses_decode_kernel(cfg) or w4
+    scrub = torch.ones(1 << 27, dtype=torch.float32, device="cuda") if streaming else None
+    scrubs = {"read": lambda i: scrub.sum(), "write": lambda i: scrub.fill_(float(i))}
+
+    def scrubbed_times(fn, how):
+        """Per-call times of fn with 512 MB of other data read or written before
+        each call (outside the events)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            scrubs[how](i)
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    scrubbed = None
+    if streaming:
+        scrubbed = {"scrub_bytes": 4 << 27}
+        for how in ("read", "write"):
+            sm = scrubbed_times(lambda: blk.forward(x), how)
+            scrubbed[f"after_{how}"] = {**dist(sm), "tokens_per_s": cfg.T / (pct(sm, 50) * 1e-3)}
+
+    # dominant kernel: gate/up grouped GEMM on its own, same inputs, same stream
+    c = blk.c
+    T, E, k = cfg.T, cfg.E, cfg.k
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    wts = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    h = torch.empty(T * k, cfg.I, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
+    # the same router (variants included) as the timed block
+    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, None, idx, wts, blk.ws)
+    if cap:
+        binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
+    else:
+        binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+
+    def gate_up():
+        if w4:
+            binding.expert_gate_up_w4(c, x, sp, offsets, blk.w4_struct, h)
+        else:
+            binding.expert_gate_up(c, x, sp, offsets, blk.w_gate, blk.w_up, h)
+
+    for _ in range(2):
+        gate_up()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        gate_up()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    gu_ms = ev0.elapsed_time(ev1) / steps
+    gu_scrubbed = {}
+    if streaming:
+        for how in ("read", "write"):
+            gu_scrubbed[how] = pct(scrubbed_times(gate_up, how), 50)
+    # every stage on its own, same inputs and stream (median of per-call times)
+    y = torch.empty(T * k, cfg.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, cfg.H, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
+    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, lg, idx, wts, blk.ws)
+
+    def down():
+        if w4:
+            binding.expert_down_w4(c, h, offsets, blk.w4_struct, y)
+        else:
+            binding.expert_down(c, h, offsets, blk.w_down, y)
+
+    def disp():
+        if cap:
+            binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
+        else:
+            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+    stage_fns = [
+        ("router", lambda: binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias,
+                                                  None, idx, wts, blk.ws)),
+        ("dispatch", disp),
+        ("gate_up", gate_up),
+        ("down", down),
+        ("combine", lambda: binding.combine(c, y, pp, wts, out)),
+        ("aux_stats_from_logits", lambda: binding.aux_stats(c, lg, idx, blk.ws, counts=counts,
+                                                            f=blk.f, P=blk.P, aux=blk.aux)),
+    ]
+    stages = {n: pct(time_per_call(torch, stream, fn, max(10, steps)), 50)
+              for n, fn in stage_fns}
+    disp()  # counts / offsets of the router's selection again
+    torch.cuda.synchronize()
+    cnt = counts.cpu().numpy()
+    rows = int(offsets[E].item())  # kept pairs (all of them without a capacity)
+    gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt, rows, w4)
+    lflops, lbytes = layer_algorithmic(cfg, cnt, rows, w4)
+    log(f"{cfg.name} gate/up kernel: {gu_ms:.4f} ms/launch, touched experts {touched}/{E}")
+
+    decode = cfg.P <= 4 * cfg.E  # weight-streaming regime: bound by HBM
+    traffic = measured_traffic(cfg.name) if not (cap or w4) else None
+    if decode:
+        achieved = gbytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = gflops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic}
+    if w4:
+        roof["kernel"] = "decode_w4_kernel<true> (gate/up, 4-bit weights, SiLU*mul epilogue)"
+    elif cfg.dtype != "bf16":
+        roof["kernel"] = "gate_up_f32_kernel"
+    elif uses_decode_kernel(cfg):
+        roof["kernel"] = "decode_gemm_bf16_kernel<true> (gate/up, SiLU*mul epilogue)"
+    else:
+        roof["kernel"] = "grouped_gemm_bf16_kernel<true,...> (gate/up, SiLU*mul epilogue)"
+    roof["kernel_ms"] = gu_ms
+    for how, ms in gu_scrubbed.items():  # same algorithmic bytes, 512 MB touched before
+        ach = gbytes / (ms * 1e-3) / 1e9
+        roof[f"after_{how}_512mb"] = {"kernel_ms": ms, "achieved": ach,
+                                      "frac": ach / PEAK_HBM_GBS}
+    roof["algorithmic"] = {"flops": gflops, "bytes": gbytes}
+    roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
+
+    config = {"workload": cfg.name, "T": T, "H": cfg.H, "E": E, "k": k, "I": cfg.I,
+              "norm_topk_prob": cfg.norm, "zipf_s": cfg.zipf_s, "seed": cfg.seed}
+    if cap:
+        config.update({"capacity_factor": cap_factor, "capacity": cap,
+                       "dropped_pairs": int(blk.dropped.item()), "kept_pairs": rows})
+    if router != "plain":
+        config["router"] = router
+    if w4:
+        config["weights"] = "w4 (group 128, bf16 scale/bias)"
+    if dynamic_k_min:
+        kt = blk.k_per_token.cpu().numpy()
+        config.update({"dynamic_k_min": dynamic_k_min, "mean_k": float(kt.mean()),
+                       "routed_pairs": int(kt.sum())})
+    rep = {
+        "ms_per_step": ms_step, "value": T / (ms_step * 1e-3), "config": config,
+        "roofline": roof, "step_ms": dist(step_ms), "stages_ms": stages,
+        "gpu_clock": clk.summary(),
+        "layer": {"tflops": lflops / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "hbm_gbs_min_bytes": lbytes / (ms_step * 1e-3) / 1e9,
+                  "hbm_frac_min_bytes": lbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "min_bytes": lbytes, "touched_experts": touched,
+                  "wall_ms_per_step": wall * 1e3 / steps},
+    }
+    if scrubbed:
+        rep["mall_scrubbed"] = scrubbed
+    del blk, h, y
+    return rep, inp, w4in
+
+
+def decode_summary(rep):
+    """The weight-streaming workload's figures as the "decode" object of the
+    line: ms/step, tokens/s, the layer's fraction of HBM bandwidth (touched
+    expert weights + router matrix + x + out over the step time), the gate/up
+    roofline and the MALL-scrubbed variants."""
+    lay = rep["layer"]
+    return {"workload": rep["config"]["workload"], "config": rep["config"],
+            "ms_per_step": rep["ms_per_step"], "tokens_per_s": rep["value"],
+            "step_ms": rep["step_ms"], "layer_hbm_frac": lay["hbm_frac_min_bytes"],
+            "layer_hbm_gbs": lay["hbm_gbs_min_bytes"], "layer_min_bytes": lay["min_bytes"],
+            "touched_experts": lay["touched_experts"], "roofline": rep["roofline"],
+            "stages_ms": rep["stages_ms"], "mall_scrubbed": rep.get("mall_scrubbed"),
+            "gpu_clock": rep["gpu_clock"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill128_bf16")
+    ap.add_argument("--decode-workload", default="decode128_bf16",
+                    help="weight-streaming workload timed after the main one (the line's "
+                         "\"decode\" object); 'none' to skip")
+    ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,208 +499,39 @@ def main():
 
     from sparse_mixture_experts_40_amd import binding
     from sparse_mixture_experts_40_amd.configs import WORKLOADS
-    from sparse_mixture_experts_40_amd.inputs import (make_inputs, make_router_variant_inputs,
-                                                      make_w4_inputs)
 
-    cfg = WORKLOADS[args.workload]
-    if args.seed != cfg.seed:
-        cfg = type(cfg)(**{**cfg.__dict__, "seed": args.seed})
+    def workload(name):
+        cfg = WORKLOADS[name]
+        if args.seed != cfg.seed:
+            cfg = type(cfg)(**{**cfg.__dict__, "seed": args.seed})
+        return cfg
+
+    cfg = workload(args.workload)
     binding.load()
     torch.cuda.init()
-    log(f"workload {cfg}")
-    t0 = time.perf_counter()
-    inp = make_inputs(cfg, weights=not args.w4)
-    w4 = make_w4_inputs(cfg) if args.w4 else None
-    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
-    cap = binding.capacity(binding.make_config(cfg), args.capacity_factor) \
-        if args.capacity_factor > 0 else 0
-    var = make_router_variant_inputs(cfg) if args.router != "plain" else {}
-    blk = binding.MoEBlock(cfg, inp, capacity=cap,
-                           noise=var.get("noise") if "noise" in args.router else None,
-                           w_noise=var.get("w_noise") if "noise" in args.router else None,
-                           select_bias=var.get("select_bias") if "bias" in args.router else None,
-                           dynamic_k_min=args.dynamic_k_min, w4=w4)
-    x = binding.to_device(inp["x"])
-    torch.cuda.synchronize()
-    log("inputs resident on the GPU")
-
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        blk.forward(x)
-    torch.cuda.synchronize()
-
-    # the K timed steps, one event before each (and one after the last)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    with ClockSampler(clock_files(torch)) as clk:
-        w0 = time.perf_counter()
-        for i in range(args.steps):
-            evs[i].record(stream)
-            blk.forward(x)
-        evs[args.steps].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
-    ms_step = evs[0].elapsed_time(evs[args.steps]) / args.steps
-    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    log(f"layer: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    streaming = uses_decode_kernel(cfg) or args.w4
-    scrub = torch.ones(1 << 27, dtype=torch.float32, device="cuda") if streaming else None
-    scrubs = {"read": lambda i: scrub.sum(), "write": lambda i: scrub.fill_(float(i))}
-
-    def scrubbed_times(fn, how):
-        """Per-call times of fn with 512 MB of other data read or written before
-        each call (outside the events)."""
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            scrubs[how](i)
-            ev[i][0].record(stream)
-            fn()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in ev]
-
-    scrubbed = None
-    if streaming:
-        scrubbed = {"scrub_bytes": 4 << 27}
-        for how in ("read", "write"):
-            sm = scrubbed_times(lambda: blk.forward(x), how)
-            scrubbed[f"after_{how}"] = {**dist(sm), "tokens_per_s": cfg.T / (pct(sm, 50) * 1e-3)}
-
-    # dominant kernel: gate/up grouped GEMM on its own, same inputs, same stream
-    c = blk.c
-    T, E, k = cfg.T, cfg.E, cfg.k
-    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
-    wts = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    h = torch.empty(T * k, cfg.I, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
-    # the same router (variants included) as the timed block
-    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, None, idx, wts, blk.ws)
-    if cap:
-        binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
-    else:
-        binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
-    def gate_up():
-        if args.w4:
-            binding.expert_gate_up_w4(c, x, sp, offsets, blk.w4_struct, h)
-        else:
-            binding.expert_gate_up(c, x, sp, offsets, blk.w_gate, blk.w_up, h)
-
-    for _ in range(2):
-        gate_up()
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        gate_up()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    gu_ms = ev0.elapsed_time(ev1) / args.steps
-    gu_scrubbed = {}
-    if streaming:
-        for how in ("read", "write"):
-            gu_scrubbed[how] = pct(scrubbed_times(gate_up, how), 50)
-    # every stage on its own, same inputs and stream (median of per-call times)
-    y = torch.empty(T * k, cfg.H, dtype=torch.float32, device="cuda")
-    out = torch.empty(T, cfg.H, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
-    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
-    binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, lg, idx, wts, blk.ws)
-    def down():
-        if args.w4:
-            binding.expert_down_w4(c, h, offsets, blk.w4_struct, y)
-        else:
-            binding.expert_down(c, h, offsets, blk.w_down, y)
-    def disp():
-        if cap:
-            binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
-        else:
-            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
-    stage_fns = [
-        ("router", lambda: binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias,
-                                                  None, idx, wts, blk.ws)),
-        ("dispatch", disp),
-        ("gate_up", gate_up),
-        ("down", down),
-        ("combine", lambda: binding.combine(c, y, pp, wts, out)),
-        ("aux_stats_from_logits", lambda: binding.aux_stats(c, lg, idx, blk.ws, counts=counts,
-                                                            f=blk.f, P=blk.P, aux=blk.aux)),
-    ]
-    stages = {n: pct(time_per_call(torch, stream, fn, max(10, args.steps)), 50)
-              for n, fn in stage_fns}
-    disp()  # counts / offsets of the router's selection again
-    torch.cuda.synchronize()
-    cnt = counts.cpu().numpy()
-    rows = int(offsets[E].item())  # kept pairs (all of them without a capacity)
-    gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt, rows, args.w4)
-    lflops, lbytes = layer_algorithmic(cfg, cnt, rows, args.w4)
-    log(f"gate/up kernel: {gu_ms:.4f} ms/launch, touched experts {touched}/{E}")
-
-    decode = cfg.P <= 4 * cfg.E  # weight-streaming regime: bound by HBM
-    traffic = measured_traffic(cfg.name) if not (cap or args.w4) else None
-    if decode:
-        achieved = gbytes / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
-    else:
-        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-        achieved = gflops / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": traffic}
-    if args.w4:
-        roof["kernel"] = "decode_w4_kernel<true> (gate/up, 4-bit weights, SiLU*mul epilogue)"
-    elif cfg.dtype != "bf16":
-        roof["kernel"] = "gate_up_f32_kernel"
-    elif uses_decode_kernel(cfg):
-        roof["kernel"] = "decode_gemm_bf16_kernel<true> (gate/up, SiLU*mul epilogue)"
-    else:
-        roof["kernel"] = "grouped_gemm_bf16_kernel<true,...> (gate/up, SiLU*mul epilogue)"
-    roof["kernel_ms"] = gu_ms
-    for how, ms in gu_scrubbed.items():  # same algorithmic bytes, 512 MB touched before
-        ach = gbytes / (ms * 1e-3) / 1e9
-        roof[f"after_{how}_512mb"] = {"kernel_ms": ms, "achieved": ach,
-                                      "frac": ach / PEAK_HBM_GBS}
-    roof["algorithmic"] = {"flops": gflops, "bytes": gbytes}
-    roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)"
-
-    value = T / (ms_step * 1e-3)
-    if cap:
-        line_cap = {"capacity_factor": args.capacity_factor, "capacity": cap,
-                    "dropped_pairs": int(blk.dropped.item()), "kept_pairs": rows}
+    rep, inp, w4in = measure(torch, binding, cfg, args, args.steps, w4=args.w4,
+                             cap_factor=args.capacity_factor, router=args.router,
+                             dynamic_k_min=args.dynamic_k_min)
     line = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "T": T, "H": cfg.H, "E": E, "k": k, "I": cfg.I,
-                   "norm_topk_prob": cfg.norm, "zipf_s": cfg.zipf_s, "seed": cfg.seed},
-        "roofline": roof,
-        "step_ms": dist(step_ms),
-        "stages_ms": stages,
-        "gpu_clock": clk.summary(),
-        "layer": {"tflops": lflops / (ms_step * 1e-3) / 1e12,
-                  "mfma_frac": lflops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                  "hbm_gbs_min_bytes": lbytes / (ms_step * 1e-3) / 1e9,
-                  "touched_experts": touched, "wall_ms_per_step": wall * 1e3 / args.steps},
+        "metric": METRIC, "value": rep["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rep["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic", "config": rep["config"], "roofline": rep["roofline"],
+        "step_ms": rep["step_ms"], "stages_ms": rep["stages_ms"], "gpu_clock": rep["gpu_clock"],
+        "layer": rep["layer"],
     }
-    if scrubbed:
-        line["mall_scrubbed"] = scrubbed
-    if cap:
-        line["config"].update(line_cap)
-    if args.router != "plain":
-        line["config"]["router"] = args.router
-    if args.w4:
-        line["config"]["weights"] = "w4 (group 128, bf16 scale/bias)"
-    if args.dynamic_k_min:
-        kt = blk.k_per_token.cpu().numpy()
-        line["config"].update({"dynamic_k_min": args.dynamic_k_min,
-                               "mean_k": float(kt.mean()), "routed_pairs": int(kt.sum())})
+    if "mall_scrubbed" in rep:
+        line["mall_scrubbed"] = rep["mall_scrubbed"]
+    plain = not (args.w4 or args.capacity_factor > 0 or args.router != "plain"
+                 or args.dynamic_k_min)
+    if plain and args.decode_workload != "none" and args.decode_workload != cfg.name:
+        torch.cuda.empty_cache()
+        drep, _, _ = measure(torch, binding, workload(args.decode_workload), args,
+                             max(args.steps, args.decode_steps))
+        line["decode"] = decode_summary(drep)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget, w4)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget, w4in)
     print(json.dumps(line), flush=True)
 
 

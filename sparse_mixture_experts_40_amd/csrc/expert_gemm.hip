@@ -26,6 +26,8 @@
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
 #include "moe_internal.h"
 
+#include <atomic>
+
 
 namespace moe {
 
@@ -1442,15 +1444,31 @@ __global__ __launch_bounds__(256) void down_f32_kernel(int E, int H, int I,
   }
 }
 
-// Number of CUs, rounded to a multiple of 8 (the persistent grid is a
-// multiple of it).
+// Number of CUs of the current device, rounded to a multiple of 8 (the
+// persistent grid is a multiple of it). Queried once per device and kept: a
+// decode step launches four GEMMs in about 0.3 ms, and the attribute query
+// costs host time on every launch otherwise. (A value computed twice by two
+// threads is the same value.)
 int persistent_grid() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return (cus + 7) & ~7;
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int g = cached[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    g = (cus + 7) & ~7;
+    cached[dev].store(g, std::memory_order_relaxed);
+  }
+  return g;
 }
 
 }  // namespace
