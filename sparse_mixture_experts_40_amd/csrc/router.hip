@@ -10,15 +10,20 @@
 //     as the A operand and the tokens as B, K staged through swizzled LDS;
 //     fp32: plain FMA dot products. (x == nullptr: the tile is read, or
 //     summed from split-K partials.)
-//  2. each wave takes a quarter of the tokens, up to 4 at a time (their
-//     reductions interleave); lanes hold experts e = lane + 64q. Softmax
-//     max/sum are xor-butterfly reductions (every lane ends with the same
-//     bits). Top-k is k rounds of a wave max over 64-bit keys (order-preserving
-//     fp32 bits, then 0xFFFF - e), so equal logits go to the lower expert
-//     index; -0.0 is folded into +0.0 first.
-//  3. per-block sums of the full softmax over the block's tokens (fixed order)
-//     for the load-balance statistic P_e, and of (ln sum_e exp l)^2 for the
-//     router z-loss.
+//  2. four lanes per token (each wave takes up to 16 tokens): lane part q
+//     holds experts e = 4j + q. Softmax max and sum: over the lane's experts,
+//     then over the four lanes (two DPP exchanges; a + b == b + a, so all four
+//     lanes hold the same bits). Top-k: each lane keeps its k best experts in
+//     registers, sorted, inserting its experts in ascending index order with a
+//     strict greater-than (an equal logit never displaces an earlier, lower
+//     index); then two bitonic merges with the partner lanes (xor 1, xor 2)
+//     under the total order (logit descending, index ascending) leave the
+//     token's k best in every one of its lanes. Plain fp32 compares, so
+//     -0.0 == +0.0. No cross-lane dependency chain runs through the k
+//     selections (the former k rounds of a wave-wide max did).
+//  3. per-block sums of the full softmax over the block's tokens (fixed
+//     token order) for the load-balance statistic P_e, and of
+//     (ln sum_e exp l)^2 for the router z-loss.
 // Variants: noisy logits l + n * softplus(x W_noise) ([MOE-128x8] router
 // pseudocode, [LAB17] noisy top-k gating; the noise logits are a second
 // logits pass, the noise values an input) are formed when the logits are read;
@@ -35,6 +40,11 @@ namespace moe {
 namespace {
 
 constexpr int kTok = 64;       // tokens per block
+
+// Row stride (floats) of the block's logits in LDS: = LPT (mod 64), so the
+// LPT lanes of each of a wave's 64 / LPT tokens (experts LPT j + q of row t)
+// read 64 different banks.
+__host__ __device__ constexpr int router_ls(int E, int lpt) { return ((E + 63) & ~63) + lpt; }
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kBK = 64;        // K step (elements)
 
@@ -233,8 +243,118 @@ __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, 
   }
 }
 
-// NT: tokens a wave reduces together (1 when a wave owns a single token).
-template <bool BF16, int NT>
+// A value of the aligned M-lane group next to this lane's (inside the
+// aligned 2M-lane group): lane ^ 1 and lane ^ 2 by DPP quad permutes; for
+// M = 4 and 8 the mirrored lane inside 8 or 16 lanes (DPP row half mirror,
+// row mirror), which lies in the other group; for 16 and 32 lane ^ M, by the
+// gfx950 permlane swaps (v_permlane16_swap: odd rows receive the even row's
+// values in the first result, even rows the odd row's in the second; likewise
+// for halves with v_permlane32_swap). Used where every lane of each M-lane
+// group holds the same value, so which lane of the other group answers does
+// not matter.
+template <int M>
+__device__ __forceinline__ uint32_t xchg_u32(uint32_t v) {
+  if constexpr (M == 1) return dpp_u32<kDppXor1>(v);
+  else if constexpr (M == 2) return dpp_u32<kDppXor2>(v);
+  else if constexpr (M == 4) return dpp_u32<kDppHalfMirror>(v);
+  else if constexpr (M == 8) return dpp_u32<kDppMirror>(v);
+  else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "group size");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float xchg_f32(float v) {
+  return __uint_as_float(xchg_u32<M>(__float_as_uint(v)));
+}
+
+// Max and sum over the L lanes of a token (aligned groups of L lanes),
+// butterflies over xchg_u32: after each step every lane of the group formed
+// so far holds the same bits (a + b == b + a).
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (L >= 2) v = fmaxf(v, xchg_f32<1>(v));
+  if constexpr (L >= 4) v = fmaxf(v, xchg_f32<2>(v));
+  if constexpr (L >= 8) v = fmaxf(v, xchg_f32<4>(v));
+  if constexpr (L >= 16) v = fmaxf(v, xchg_f32<8>(v));
+  if constexpr (L >= 32) v = fmaxf(v, xchg_f32<16>(v));
+  if constexpr (L >= 64) v = fmaxf(v, xchg_f32<32>(v));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += xchg_f32<1>(v);
+  if constexpr (L >= 4) v += xchg_f32<2>(v);
+  if constexpr (L >= 8) v += xchg_f32<4>(v);
+  if constexpr (L >= 16) v += xchg_f32<8>(v);
+  if constexpr (L >= 32) v += xchg_f32<16>(v);
+  if constexpr (L >= 64) v += xchg_f32<32>(v);
+  return v;
+}
+
+// Total order of the top-k: larger key first, equal keys by lower index.
+__device__ __forceinline__ bool topk_better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bitonic merge of this lane's sorted (descending) list with the one of the
+// neighbouring M-lane group (xchg_u32; the lanes of each group hold the same
+// list): the best KM of both, sorted, in every lane of both groups.
+template <int KM, int M>
+__device__ __forceinline__ void topk_merge(float (&tv)[KM], int (&ti)[KM]) {
+  float bv[KM];
+  int bi[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    bv[s] = xchg_f32<M>(tv[s]);
+    bi[s] = (int)xchg_u32<M>((uint32_t)ti[s]);
+  }
+  // the better of a[s] and b[KM-1-s]: the KM best, as a bitonic sequence
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    const float ob = bv[KM - 1 - s];
+    const int oi = bi[KM - 1 - s];
+    if (!topk_better(tv[s], ti[s], ob, oi)) {
+      tv[s] = ob;
+      ti[s] = oi;
+    }
+  }
+  // bitonic sorter, descending
+#pragma unroll
+  for (int d = KM / 2; d > 0; d >>= 1)
+#pragma unroll
+    for (int s = 0; s < KM; ++s)
+      if ((s & d) == 0) {
+        const int u = s + d;
+        if (topk_better(tv[u], ti[u], tv[s], ti[s])) {
+          const float fv = tv[s];
+          const int fi = ti[s];
+          tv[s] = tv[u];
+          ti[s] = ti[u];
+          tv[u] = fv;
+          ti[u] = fi;
+        }
+      }
+}
+
+// All merges of an L-lane token group.
+template <int KM, int L>
+__device__ __forceinline__ void topk_merge_group(float (&tv)[KM], int (&ti)[KM]) {
+  if constexpr (L >= 2) topk_merge<KM, 1>(tv, ti);
+  if constexpr (L >= 4) topk_merge<KM, 2>(tv, ti);
+  if constexpr (L >= 8) topk_merge<KM, 4>(tv, ti);
+  if constexpr (L >= 16) topk_merge<KM, 8>(tv, ti);
+  if constexpr (L >= 32) topk_merge<KM, 16>(tv, ti);
+  if constexpr (L >= 64) topk_merge<KM, 32>(tv, ti);
+}
+
+// KM: the top-k list length, a power of two >= k (1 <= k <= 16).
+// LPT: lanes per token (4, 16 or 64): 256 / tokens per block.
+template <bool BF16, int KM, int LPT>
 __global__ __launch_bounds__(kThreads) void router_kernel(
     int T, int H, int E, int k, int norm, const void* __restrict__ x, const void* __restrict__ wr,
     const float* __restrict__ bias, const float* __restrict__ logits_in, float* __restrict__ logits_out,
@@ -245,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * tpb;  // tpb = 64 when the logits are computed here
-  const int ls = ((E + 31) & ~31) + 1;
+  const int ls = router_ls(E, LPT);
   float* s_log = reinterpret_cast<float*>(smem);  // [64][ls]
 
   if (part) {  // split-K partial logits: sum in split order, then the bias
@@ -286,10 +406,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
       }
       s_log[t * ls + e] = l;
     }
-  } else if constexpr (BF16) {
+  } else if constexpr (BF16 && LPT == 4) {  // logits computed here: 64-token blocks
     router_logits_mfma(T, H, E, t0, 0, H, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(wr), bias, smem, s_log, ls);
-  } else {
+  } else if constexpr (!BF16 && LPT == 4) {
     const float* xf = static_cast<const float*>(x);
     const float* wf = static_cast<const float*>(wr);
     for (int i = tid; i < kTok * E; i += kThreads) {
@@ -304,159 +424,128 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   }
   __syncthreads();
 
-  const int EQ = (E + 63) >> 6;  // <= 4 experts per lane
-  float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float zacc = 0.0f;  // this wave's sum of (ln sum_e exp l)^2 over its tokens
-  // Each wave owns tpb / 4 tokens, taken NT at a time: their cross-lane
-  // reductions are independent chains, so the shuffle latencies overlap.
-  const int tpw = tpb / 4;
-  for (int tt = 0; tt < tpw; tt += NT) {
-    const int tb0 = wave * tpw + tt;
-    if (t0 + tb0 >= T) break;  // wave-uniform
-    bool ok[NT];
-    float v[NT][4], m[NT], ex[NT][4], ssum[NT], inv[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const int t = tb0 + u, gt = t0 + t;
-      const bool mine = tt + u < tpw;  // a row of this wave (and of this block)
-      ok[u] = mine && gt < T;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        v[u][q] = (q < EQ && e < E) ? (mine ? s_log[t * ls + e] : 0.0f) : -INFINITY;
-        if (logits_out && ok[u] && q < EQ && e < E) logits_out[(size_t)gt * E + e] = v[u][q];
-      }
-      m[u] = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
-    }
-    wave_max_n(m);
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      ssum[u] = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        ex[u][q] = (q < EQ && e < E) ? expf(v[u][q] - m[u]) : 0.0f;
-        ssum[u] += ex[u][q];
-      }
-    }
-    wave_sum_n(ssum);
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      inv[u] = 1.0f / ssum[u];
-      if (ok[u]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pacc[q] += ex[u][q] * inv[u];
-        const float lse = m[u] + logf(ssum[u]);
-        zacc = fmaf(lse, lse, zacc);
-      }
+  // the logits the softmax uses, written out coalesced from LDS
+  if (logits_out)
+    for (int i = tid; i < tpb * E; i += kThreads) {
+      const int t = i / E, e = i - t * E;
+      if (t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = s_log[t * ls + e];
     }
 
-    // entropy-driven number of experts ([QWEN3-ROUTE] §二 dynamic TopK):
-    // k_t = clamp(floor(k_min + (k - k_min) H_t / ln E)), H_t = -sum p ln max(p, 1e-10)
-    int kt[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) kt[u] = k;
-    if (k_min > 0) {
-      float hs[NT];
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        hs[u] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float pe = ex[u][q] * inv[u];
-          if (q < EQ && lane + 64 * q < E) hs[u] = fmaf(pe, logf(fmaxf(pe, 1e-10f)), hs[u]);
-        }
-      }
-      wave_sum_n(hs);
-      const float span = (float)(k - k_min) / logf((float)E);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const int kk = (int)floorf(fmaf(-hs[u], span, (float)k_min));
-        kt[u] = kk < k_min ? k_min : (kk > k ? k : kk);
-        if (kt_out && ok[u] && lane == 0) kt_out[t0 + tb0 + u] = kt[u];
+  // LPT lanes per token: token slot tl of this wave, part q
+  constexpr int TPW = 64 / LPT;                  // token slots per wave
+  const int q = lane & (LPT - 1), tl = lane / LPT;
+  const int tpw = tpb / 4;                       // tokens of this wave (<= TPW)
+  const int tb = wave * tpw + (tl < tpw ? tl : tpw - 1);  // its row in s_log
+  const bool ok = tl < tpw && t0 + tb < T;       // a real token of this lane
+  const float* row = s_log + tb * ls;
+  const int EQ = (E + LPT - 1) / LPT;            // experts per lane (e = LPT j + q)
+  static_assert(TPW * LPT == 64, "lanes per token");
+
+  float m = -INFINITY;
+  for (int j = 0; j < EQ; ++j) {
+    const int e = LPT * j + q;
+    if (e < E) m = fmaxf(m, row[e]);
+  }
+  m = group_max<LPT>(m);
+  float ssum = 0.0f;
+  for (int j = 0; j < EQ; ++j) {
+    const int e = LPT * j + q;
+    if (e < E) ssum += expf(row[e] - m);
+  }
+  ssum = group_sum<LPT>(ssum);
+  const float inv = 1.0f / ssum;
+
+  // entropy-driven number of experts ([QWEN3-ROUTE] §二 dynamic TopK):
+  // k_t = clamp(floor(k_min + (k - k_min) H_t / ln E)), H_t = -sum p ln max(p, 1e-10)
+  int kt = k;
+  if (k_min > 0) {
+    float hs = 0.0f;
+    for (int j = 0; j < EQ; ++j) {
+      const int e = LPT * j + q;
+      if (e < E) {
+        const float pe = expf(row[e] - m) * inv;
+        hs = fmaf(pe, logf(fmaxf(pe, 1e-10f)), hs);
       }
     }
+    hs = group_sum<LPT>(hs);
+    const float span = (float)(k - k_min) / logf((float)E);
+    const int kk = (int)floorf(fmaf(-hs, span, (float)k_min));
+    kt = kk < k_min ? k_min : (kk > k ? k : kk);
+    if (kt_out && ok && q == 0) kt_out[t0 + tb] = kt;
+  }
 
-    if (do_select) {
-      uint32_t key[NT][4];
-      int my_e[NT];
-      float my_p[NT], psum[NT];
+  if (do_select) {
+    float tv[KM];
+    int ti[KM];
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        my_e[u] = 0;
-        my_p[u] = 0.0f;
-        psum[u] = 0.0f;
+    for (int s = 0; s < KM; ++s) {
+      tv[s] = -INFINITY;
+      ti[s] = 0x7FFF;
+    }
+    for (int j = 0; j < EQ; ++j) {
+      const int e = LPT * j + q;
+      if (e >= E) break;
+      const float c = sel_bias ? row[e] + sel_bias[e] : row[e];
+      // sorted insertion, strict: c goes below every entry it does not beat
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = lane + 64 * q;
-          const bool live = q < EQ && e < E;
-          key[u][q] = live ? order_key(sel_bias ? v[u][q] + sel_bias[e] : v[u][q]) : 0u;
-        }
+      for (int s = KM - 1; s >= 0; --s) {
+        const bool gt = c > tv[s];
+        const bool gtp = s > 0 ? c > tv[s > 0 ? s - 1 : 0] : false;
+        const float pv = tv[s > 0 ? s - 1 : 0];
+        const int pi = ti[s > 0 ? s - 1 : 0];
+        tv[s] = gt ? (gtp ? pv : c) : tv[s];
+        ti[s] = gt ? (gtp ? pi : e) : ti[s];
       }
-      for (int j = 0; j < k; ++j) {
-        unsigned long long best[NT];
+    }
+    topk_merge_group<KM, LPT>(tv, ti);
+    // weights from the unbiased logits: p_j = e^(l_j - m) / s, renormalised
+    // over the first k_t slots iff norm; slots past k_t are empty
+    float pj[KM], psum = 0.0f;
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          best[u] = 0ull;
+    for (int s = 0; s < KM; ++s) {
+      const float lj = sel_bias ? row[ti[s] < E ? ti[s] : 0] : tv[s];
+      pj[s] = expf(lj - m) * inv;
+      if (s < kt) psum += pj[s];
+    }
+    if (ok) {
+      const size_t o = (size_t)(t0 + tb) * k;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const unsigned long long cand = (static_cast<unsigned long long>(key[u][q]) << 32) |
-                                            (0xFFFFu - (unsigned)(lane + 64 * q));
-            best[u] = (key[u][q] != 0u && cand > best[u]) ? cand : best[u];
-          }
+      for (int s = 0; s < KM; ++s)
+        if (s < k && (s & (LPT - 1)) == q) {
+          const bool live = s < kt;
+          topk_idx[o + s] = live ? ti[s] : -1;
+          topk_w[o + s] = live ? (norm ? pj[s] / psum : pj[s]) : 0.0f;
         }
-        wave_max_u64_n(best);
-#pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          const int ej = 0xFFFF - static_cast<int>(best[u] & 0xFFFFull);
-          if ((ej & 63) == lane) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (q == (ej >> 6)) key[u][q] = 0u;
-          }
-          // with a selection bias the key is not the logit: read the logit back
-          const float lj = sel_bias ? s_log[(tb0 + u) * ls + ej]
-                                    : key_value(static_cast<uint32_t>(best[u] >> 32));
-          const float pj = expf(lj - m[u]) * inv[u];
-          if (j < kt[u]) psum[u] += pj;
-          if (lane == j) {
-            my_e[u] = ej;
-            my_p[u] = pj;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const int gt = t0 + tb0 + u;
-        if (ok[u] && lane < k) {  // slots past k_t are empty (dynamic k)
-          const bool live = lane < kt[u];
-          topk_idx[(size_t)gt * k + lane] = live ? my_e[u] : -1;
-          topk_w[(size_t)gt * k + lane] = live ? (norm ? my_p[u] / psum[u] : my_p[u]) : 0.0f;
-        }
-      }
     }
   }
 
-  if (zpart) {  // fixed order: waves 0..3, each in its token order
-    __shared__ float s_z[4];
-    __syncthreads();
-    if (lane == 0) s_z[wave] = zacc;
-    __syncthreads();
-    if (tid == 0) zpart[blockIdx.x] = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
+  // statistics: per token (ln s)^2 + m-shifted, and the full softmax written
+  // back over the block's logits; then fixed-order sums over the tokens
+  __shared__ float s_z[kTok];
+  if (zpart && q == 0 && tl < tpw) {
+    const float lse = m + logf(ssum);
+    s_z[tb] = ok ? lse * lse : 0.0f;
   }
   if (partials) {
-    __syncthreads();  // every wave is done with s_log
-    float* s_part = reinterpret_cast<float*>(smem);  // [4][256]
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (e < 256) s_part[wave * 256 + e] = pacc[q];
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads)
-      partials[(size_t)blockIdx.x * E + e] =
-          ((s_part[e] + s_part[256 + e]) + s_part[512 + e]) + s_part[768 + e];
+    __syncthreads();  // every lane's top-k reads of its row are done
+    if (tl < tpw)
+      for (int j = 0; j < EQ; ++j) {
+        const int e = LPT * j + q;
+        if (e < E) s_log[tb * ls + e] = ok ? expf(row[e] - m) * inv : 0.0f;
+      }
   }
+  if (zpart || partials) __syncthreads();
+  if (zpart && tid == 0) {
+    float z = 0.0f;
+    for (int t = 0; t < tpb; ++t) z += s_z[t];  // token order
+    zpart[blockIdx.x] = z;
+  }
+  if (partials)
+    for (int e = tid; e < E; e += kThreads) {
+      float a = 0.0f;
+      for (int t = 0; t < tpb; ++t) a += s_log[t * ls + e];  // token order
+      partials[(size_t)blockIdx.x * E + e] = a;
+    }
 }
 
 // Split-K router logits for small token counts (a single 64-token block
@@ -507,8 +596,9 @@ __global__ __launch_bounds__(kThreads) void router_reduce_kernel(int T, int E, i
 }  // namespace
 
 // Tokens per router block: 64 when the block computes its logits (one MFMA
-// tile); fewer when it starts from logits and T is small, so that more waves
-// share the top-k work (its cost is the serial reduction chain of each wave).
+// tile); fewer when it starts from logits and T is small, so that the tokens
+// spread over more waves (each wave's top-k time is one pass over its
+// lanes' experts, whatever the number of its tokens).
 int router_tpb(const moe_config& c, bool from_logits) {
   if (!from_logits) return kTok;
   return c.num_tokens <= 256 ? 4 : c.num_tokens <= 4096 ? 16 : kTok;
@@ -576,7 +666,7 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
                          const RouterExtras& ex) {
   const int E = c.num_experts;
   const int EP = (E + 31) & ~31;
-  size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
+  size_t lds = (size_t)kTok * router_ls(E, 64) * sizeof(float);
   if (x && c.dtype == MOE_DTYPE_BF16) {
     const size_t tiles = (size_t)(kTok + EP) * kBK * sizeof(uint16_t);
     if (tiles > lds) lds = tiles;
@@ -588,23 +678,34 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   const float* lin = x ? nullptr : logits;
   float* lout = x ? (logits_out ? logits : nullptr) : ex.logits_final;
   const float* noise = x ? nullptr : ex.noise;
-#define MOE_ROUTER_LAUNCH(BF, NT_)                                                            \
-  router_kernel<BF, NT_><<<grid, block, lds, s>>>(                                              \
+#define MOE_ROUTER_LAUNCH(BF, KM_, LPT_)                                                      \
+  router_kernel<BF, KM_, LPT_><<<grid, block, lds, s>>>(                                        \
       c.num_tokens, c.hidden, E, c.top_k, c.norm_topk_prob, x, w_router, bias, lin, lout,       \
       topk_idx, topk_w, prob_partials, do_select, tpb, noise, ex.nlogits, ex.sel_bias, ex.zpart, \
       ex.k_min, ex.kt_out, ex.part, ex.nsplit)
-  const bool one = tpb / 4 == 1;  // one token per wave
-  if (c.dtype == MOE_DTYPE_BF16) {
-    // With the logits computed here (64 tokens per block, one block per 64
-    // tokens) a wave's 16 tokens go through the top-k as one interleaved
-    // group: 16 independent reduction chains hide each other's latency at one
-    // wave per SIMD (router 116 -> 105 us at 16K tokens x 128 experts).
-    if (one) MOE_ROUTER_LAUNCH(true, 1);
-    else if (x) MOE_ROUTER_LAUNCH(true, 16);
-    else MOE_ROUTER_LAUNCH(true, 4);
-  } else {
-    if (one) MOE_ROUTER_LAUNCH(false, 1); else MOE_ROUTER_LAUNCH(false, 4);
-  }
+#define MOE_ROUTER_KM(BF, LPT_)                             \
+  do {                                                      \
+    const int k = c.top_k;                                  \
+    if (k <= 1) MOE_ROUTER_LAUNCH(BF, 1, LPT_);             \
+    else if (k <= 2) MOE_ROUTER_LAUNCH(BF, 2, LPT_);        \
+    else if (k <= 4) MOE_ROUTER_LAUNCH(BF, 4, LPT_);        \
+    else if (k <= 8) MOE_ROUTER_LAUNCH(BF, 8, LPT_);        \
+    else MOE_ROUTER_LAUNCH(BF, 16, LPT_);                   \
+  } while (0)
+#define MOE_ROUTER_LPT(BF)                                  \
+  do {                                                      \
+    if (tpb == kTok) MOE_ROUTER_KM(BF, 4);                  \
+    else if (tpb == 16) MOE_ROUTER_KM(BF, 16);              \
+    else MOE_ROUTER_KM(BF, 64);                             \
+  } while (0)
+  // the top-k list length: the power of two at or above k; lanes per token:
+  // 256 / tokens per block (64-token blocks, which compute logits, use 4)
+  if (c.dtype == MOE_DTYPE_BF16)
+    MOE_ROUTER_LPT(true);
+  else
+    MOE_ROUTER_LPT(false);
+#undef MOE_ROUTER_LPT
+#undef MOE_ROUTER_KM
 #undef MOE_ROUTER_LAUNCH
   return hipGetLastError();
 }
