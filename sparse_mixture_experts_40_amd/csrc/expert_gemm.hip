@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
-    int n_tiles_n) {
+    int n_tiles_n, int8_t* __restrict__ y_exp) {
   constexpr int BN = 256;
   constexpr int WN = NW / 2;                  // waves along the weight rows
   constexpr int MB = BM / 64;                 // token blocks of 32 rows per wave
@@ -482,15 +482,41 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       // c ^ (s & 15): conflict-free for the column writes (16 rows, one chunk)
       // and the row reads (one row, 16 chunks).
       static_assert(BN * 64 * 4 <= STAGE * 2, "slab must fit in one stage");
+      static_assert(NB * 32 == kYChunk, "one scaled-fp16 chunk per wave and row");
       float* slab = reinterpret_cast<float*>(smem + ((g0 + nk - 1) % NST) * STAGE);
       const int srow_w = wm * 32 + (lane & 31);
-      // one store per slab row of this wave inside the tile
+      // one store per slab row of this wave inside the tile (the exponent
+      // stores below are not counted: fewer counted than issued only makes
+      // the next tile's first wait stricter)
       st_after = 0;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         st_after += min(max(row_end - (row0 + mb * 64 + wave * (64 / NW)), 0), 64 / NW);
+      // this wave's kYChunk columns lie wholly inside N or wholly past it
+      const int ycol0 = n0 + wn * NB * 32;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        if (y_exp) {
+          // scaled fp16: lane l holds 32 of row srow_w's kYChunk columns here,
+          // lane l ^ 32 the other 32; the chunk exponent comes from their
+          // largest |v| (fmaxf skips NaN), and the values are scaled before
+          // they reach the slab
+          float mx = 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[nb][mb][r]));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const int e = yh_exponent(__float_as_uint(mx));
+          const float sc = pow2i(-e);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][mb][r] *= sc;
+          const int grow = row0 + mb * 64 + srow_w;
+          if (lane < 32 && grow < row_end && ycol0 < N_out)
+            y_exp[(size_t)grow * (N_out / kYChunk) + ycol0 / kYChunk] = (int8_t)e;
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -509,11 +535,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
               *reinterpret_cast<const float4*>(slab + sr * BN + ((lane ^ (sr & 15)) << 2));
           const int col = n0 + lane * 4;
           // y_sorted is read once, by the combine: non-temporal stores keep it
-          // from displacing the operands in L2 (-2.5% down at 16K tokens)
-          if (row < row_end && col < N_out)
+          // from displacing the operands in L2 (-2.5% down at 16K tokens).
+          if (y_exp) {
+            if (row < row_end && col < N_out)  // already scaled: fp16 conversion only
+              __builtin_nontemporal_store(
+                  u32x2_t{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)},
+                  reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + (size_t)row * N_out +
+                                             col));
+          } else if (row < row_end && col < N_out) {
             __builtin_nontemporal_store(
                 f32x4_t{v.x, v.y, v.z, v.w},
                 reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)row * N_out + col));
+          }
         }
         lds_barrier();
       }
@@ -1497,12 +1530,14 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
       <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
       c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
       sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
-      static_cast<const uint16_t*>(w_up), h, ntn);
+      static_cast<const uint16_t*>(w_up), h, ntn, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offsets,
-                       const void* w_down, void* y, hipStream_t s) {
+                       const void* w_down, void* y, hipStream_t s, int8_t* y_exp,
+                       bool* y_half) {
+  if (y_half) *y_half = false;
   const int P = c.num_tokens * c.top_k;
   if (c.dtype == MOE_DTYPE_F32) {
     down_f32_kernel<<<P, 256, c.intermediate * sizeof(float), s>>>(
@@ -1521,7 +1556,8 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
   grouped_gemm_bf16_kernel<false, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
       <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
       c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h), nullptr,
-      offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn);
+      offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn, y_exp);
+  if (y_exp && y_half) *y_half = true;
   return hipGetLastError();
 }
 

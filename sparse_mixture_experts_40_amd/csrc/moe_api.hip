@@ -134,7 +134,9 @@ Layout carve(const moe_config& c, void* ws) {
   L.sorted_pair = cv.take<int32_t>(P);
   L.pair_pos = cv.take<int32_t>(P);
   L.h = cv.take<char>(P * c.intermediate * elem_bytes(c));
-  L.y = cv.take<float>(P * c.hidden);  // y_sorted is fp32
+  // y_sorted: fp32 rows, or (bf16 layers) scaled fp16 rows in the first half
+  // and their int8 chunk exponents after them
+  L.y = cv.take<float>(P * c.hidden);
   L.layer_end = cv.off;
   return L;
 }
@@ -225,6 +227,13 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
                                   L.base, true, o.capacity, o.dropped, stream));
   }
   if (st != MOE_OK) return st;
+  // bf16 layers keep y_sorted in scaled fp16 where the tiled down kernel
+  // writes it (half the bytes between the down GEMM and the combine): the
+  // rows in the first half of L.y, their chunk exponents after them
+  int8_t* y_exp = nullptr;
+  bool y_half = false;
+  if (c.dtype == MOE_DTYPE_BF16 && !w4 && combine_half_fits(c))
+    y_exp = reinterpret_cast<int8_t*>(L.y) + (size_t)c.num_tokens * c.top_k * c.hidden * 2;
   if (w4) {
     st = launched(launch_gate_up_w4(c, x, L.sorted_pair, L.offsets, *w4, L.h, stream));
     if (st != MOE_OK) return st;
@@ -232,10 +241,10 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   } else {
     st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
     if (st != MOE_OK) return st;
-    st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream));
+    st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream, y_exp, &y_half));
   }
   if (st != MOE_OK) return st;
-  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream));
+  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream, y_half ? y_exp : nullptr));
   if (st != MOE_OK) return st;
   if ((want_aux || ao.z_loss) && !aux_done)
     st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, ao, stream, ex.zpart,

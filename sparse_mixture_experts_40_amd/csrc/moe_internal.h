@@ -13,6 +13,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 is carried as its 16-bit pattern.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -28,6 +29,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Scaled fp16 rows of y_sorted (inside the bf16 layer forward): each chunk of
+// kYChunk columns of a row holds fp16(v * 2^-e), with one exponent e (int8)
+// per row and chunk, chosen from the chunk's largest |v| so that it scales to
+// below 2^15: fp16's 11-bit significand (rounding error 2^-11 relative, an
+// eighth of bf16's) over fp32's whole exponent range, in bf16's 2 bytes.
+// H is a multiple of kYChunk.
+constexpr int kYChunk = 64;
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// e for a chunk whose largest |v| has bit pattern max_abs_bits (sign clear):
+// floor(log2 max) - 14, at least -126 (2^-e stays a normal fp32); inf / NaN
+// (biased exponent 255) give 114 and pass through the fp16 conversion as such.
+__device__ __forceinline__ int yh_exponent(uint32_t max_abs_bits) {
+  return max((int)(max_abs_bits >> 23) - 141, -126);
+}
+
+// 2^e as an fp32 for e in [-126, 127]
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// fp32 -> fp16 (round to nearest even), two to a word
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+}
+
+__device__ __forceinline__ float2 unpack_f16x2(uint32_t u) {
+  const f16x2_t h = __builtin_bit_cast(f16x2_t, u);
+  return make_float2((float)h.x, (float)h.y);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -231,8 +261,12 @@ hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t
 hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,
                           const int32_t* offsets, const void* w_gate, const void* w_up, void* h,
                           hipStream_t s);
+// y rows are fp32, or, where y_exp is given (bf16 layers) and the tiled
+// kernel runs, scaled fp16 with their exponents in y_exp [rows][H / kYChunk];
+// *y_half (nullable) says which was written.
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offsets,
-                       const void* w_down, void* y, hipStream_t s);
+                       const void* w_down, void* y, hipStream_t s, int8_t* y_exp = nullptr,
+                       bool* y_half = nullptr);
 // 4-bit weights (weight-streaming kernels): bf16 activations, H and I
 // multiples of 512.
 bool w4_supported(const moe_config& c);
@@ -253,8 +287,12 @@ struct AuxOut {
 };
 
 // Combine and statistics.
+// y_exp (nullable): y rows are scaled fp16 with these exponents (bf16 layers,
+// combine_half_fits), else fp32; the sum is fp32 either way.
+bool combine_half_fits(const moe_config& c);
 hipError_t launch_combine(const moe_config& c, const void* y, const int32_t* pair_pos,
-                          const float* topk_w, void* out, hipStream_t s);
+                          const float* topk_w, void* out, hipStream_t s,
+                          const int8_t* y_exp = nullptr);
 // fp_scratch: E doubles of workspace (per-expert f_e * P_e).
 // zpart [n_zpart] (nullable): per router block sums of (ln sum_e exp l)^2 for
 // out.z_loss.

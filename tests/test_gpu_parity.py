@@ -354,6 +354,41 @@ def test_all_tokens_to_one_expert(orc):
     assert check_block(orc, cfg, inp, blk, np.arange(cfg.T, dtype=np.int32)) == 0
 
 
+def test_layer_forward_y_chunk_exponents(orc):
+    """Inside a bf16 layer forward the tiled down GEMM hands y_sorted to the
+    combine as fp16 scaled by 2^-e, one exponent e per row and 64-column chunk.
+    Scaling the W_down rows of output column group g by 2^s_g scales y and the
+    output of that group by exactly 2^s_g (the router is untouched), so the
+    GPU output unscaled per group meets the oracle on the unscaled weights,
+    and equals the unscaled run's bit for bit where no product of the down
+    GEMM turns subnormal (s_g > -60). The shifts put y far outside fp16's
+    range both ways (2^100, 2^-100) and give every chunk its own exponent;
+    H = 320 leaves the last column tile with one chunk inside N. (The
+    exponent's lower clamp, for chunks whose largest |y| is below 2^-112, is
+    not reached: weights that small would be subnormal bf16.)"""
+    cfg = MoEConfig("y_range", T=600, H=320, E=16, k=4, I=128, norm=True, dtype="bf16")
+    inp = make_inputs(cfg, seed=11)
+    base = _run_block(cfg, inp)
+    base_out, base_idx = host(base.out), host(base.topk_idx)
+    shifts = np.array([-100, 100, -17, 0, 60])
+    col_shift = np.repeat(shifts, 64)
+    wd = (inp["w_down"].astype(np.uint32) << 16).view(np.float32)
+    wd = wd * np.ldexp(1.0, col_shift).astype(np.float32)[None, :, None]
+    scaled = dict(inp)
+    scaled["w_down"] = (wd.view(np.uint32) >> 16).astype(np.uint16)
+    assert ((wd.view(np.uint32) & 0xFFFF) == 0).all()  # the scaling is exact in bf16
+    blk = _run_block(cfg, scaled)
+    gi, gw = host(blk.topk_idx), host(blk.topk_w)
+    assert (gi == base_idx).all()
+    got = host(blk.out).astype(np.float64) * np.ldexp(1.0, -col_shift)[None, :]
+    normal = col_shift > -60
+    assert np.array_equal(got[:, normal], base_out[:, normal].astype(np.float64))
+    tokens = np.arange(cfg.T, dtype=np.int32)
+    r, _ = compare_selection(orc, cfg, inp, tokens, gi[tokens], gw[tokens])
+    mx, rm = check_output(got, r["out"], cfg.dtype)
+    print(f"y_range: max|d|/RMS {mx:.4f}  RMS(d)/RMS {rm:.5f}", flush=True)
+
+
 def test_decode_path_hot_expert_multi_pass(orc):
     """Weight-streaming kernels with one expert holding more than 64 rows
     (several token passes) and a ragged last pass."""
