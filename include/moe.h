@@ -44,7 +44,7 @@
  *    synchronisation.
  *  - Supported sizes (MOE_ERR_UNSUPPORTED otherwise): 1 <= E <= 256,
  *    1 <= k <= min(E, 16), H and I multiples of 64, T >= 1, T*k < 2^31,
- *    T*k*max(H,I) < 2^31 elements, H*I < 2^31, E*H*I < 2^40.
+ *    T*k*max(H,I) < 2^31 elements, H*I < 2^31, E*H < 2^31, E*H*I < 2^40.
  *  - Non-finite values in x or the weights are outside the contract.
  *  - Results are deterministic: the same inputs give bitwise-identical
  *    outputs on every call (fixed reduction orders, no float atomics).

@@ -74,8 +74,10 @@ moe_status check_config(const moe_config* cfg) {
   const long long wide = c.hidden > c.intermediate ? c.hidden : c.intermediate;
   if (P >= (1LL << 31) || P * wide >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long long)c.num_experts * c.intermediate * c.hidden >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
-  // one expert's matrix is addressed with 32-bit byte offsets
+  // one expert's matrix, and the router matrix, are addressed with 32-bit
+  // byte offsets
   if ((long long)c.intermediate * c.hidden >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)c.num_experts * c.hidden >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -135,93 +135,129 @@ __device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[N]) {
 // swizzled [rows][64] bf16 tile: 16-byte chunk c of row r lives at chunk c ^ (r & 7)
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
 
-// Logits tile by bf16 MFMA into s_log[t * ls + e] (+ bias).
+// Router rows of one K stage in LDS: the power of two (times 32) at or above
+// E rounded to 32, so that each of the 4 waves issues the same number of
+// 8-row LDS-DMA loads.
+__host__ __device__ constexpr int router_wrows(int E) {
+  return (E + 31) / 32 <= 1 ? 32 : (E + 31) / 32 <= 2 ? 64 : (E + 31) / 32 <= 4 ? 128 : 256;
+}
+constexpr int kStages = 3;  // LDS stages of the logits pipeline
+// LDS bytes of the logits pipeline: kStages x ([64] token rows + router rows) x 64
+__host__ __device__ constexpr size_t router_tile_lds(int E) {
+  return (size_t)kStages * (kTok + router_wrows(E)) * kBK * sizeof(uint16_t);
+}
+
+// One K step of the logits tile: issue the LDS-DMA loads of a later stage
+// into dst (if issue), then the MFMAs of the stage in src. dst and src are
+// distinct __restrict__ pointers, so the compiler gives the DMA writes and
+// the fragment reads disjoint alias scopes and does not drain the loads in
+// flight before every fragment read; wait_vmcnt + lds_barrier order them.
+// Each DMA instruction fills 8 consecutive tile rows (lane l: row l / 8,
+// slot l % 8); the lane's source chunk is (l % 8) ^ (l / 8), which is the
+// swz layout. Waves own x row groups 2w, 2w + 1 and router row groups
+// NW w .. NW w + NW - 1.
+template <int NQ, int NW>
+__device__ __forceinline__ void router_step(uint16_t* __restrict__ dst,
+                                            const uint16_t* __restrict__ src, bool issue,
+                                            __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw,
+                                            const uint32_t (&xo)[2], const uint32_t (&wo)[NW],
+                                            uint32_t kb, f32x16_t (&acc)[NQ > 0 ? NQ : 1],
+                                            int wave, int lane) {
+  if (issue) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + (2 * wave + i) * 8 * kBK),
+                                               16, xo[i], kb, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_void_t*)(dst + (kTok + (NW * wave + i) * 8) * kBK), 16, wo[i], kb, 0, 0);
+  }
+  const uint16_t* s_w = src + kTok * kBK;
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int tile = q * 4 + wave;
+      const int eb = tile >> 1, tb = tile & 1;
+      const int er = eb * 32 + (lane & 31), tr = tb * 32 + (lane & 31);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(src + swz(tr, ch));
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
+    }
+  }
+}
+
+// Logits tile by bf16 MFMA into s_log[t * ls + e] (+ bias): tokens t0 ..
+// t0 + 63 over K range [kbeg, kend), through a kStages LDS ring filled by
+// LDS-DMA (no register staging, no LDS store instructions), one wait and one
+// barrier per K step. A stage buffer is refilled two steps after it was read,
+// and every wave has passed the barrier between. Rows past T and past E are
+// clamped to valid rows on load and never stored. Needs T H and E H below
+// 2^31 elements (32-bit buffer offsets).
 __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, int kbeg, int kend,
                                    const uint16_t* __restrict__ x,
                                    const uint16_t* __restrict__ wr, const float* __restrict__ bias,
                                    char* smem, float* s_log, int ls) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int EP = (E + 31) & ~31;
-  uint16_t* s_x = reinterpret_cast<uint16_t*>(smem);  // [64][64]
-  uint16_t* s_w = s_x + kTok * kBK;                     // [EP][64]
+  uint16_t* s_ring = reinterpret_cast<uint16_t*>(smem);
   const int ntiles = (EP / 32) * 2;                     // (expert block, token block)
 
   // tiles of this wave: (expert block, token block) q * 4 + wave for q < nq
   const int nq = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0,
+                                        (int)((uint32_t)T * (uint32_t)H * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wr), (short)0,
+                                        (int)((uint32_t)E * (uint32_t)H * 2u), 0x00020000);
+  const int r_in = lane >> 3, chunk = (lane & 7) ^ r_in;
 
-  // Two register sets: the loads of steps kt + 1 and kt + 2 are in flight
-  // while step kt is multiplied. The loads are unconditional (rows clamped)
-  // and the tile count is a compile-time constant of the loop, so the
-  // compiler's load counting stays exact and each set is waited for only
-  // where it is stored. Barriers order LDS only.
-  typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 16 bytes in registers
-  auto gload = [&](int k0, v4u (&rx)[2], v4u (&rw)[8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      const int gt = t0 + row < T ? t0 + row : T - 1;  // rows past T are never stored
-      rx[i] = *reinterpret_cast<const v4u*>(x + (size_t)gt * H + k0 + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      const int gr = row < E ? row : E - 1;  // slots past E re-read row E-1 (one line)
-      rw[i] = *reinterpret_cast<const v4u*>(wr + (size_t)gr * H + k0 + ch * 8);
-    }
-  };
-  auto sstore = [&](const v4u (&rx)[2], const v4u (&rw)[8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      *reinterpret_cast<v4u*>(s_x + swz(row, ch)) = rx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i, row = c >> 3, ch = c & 7;
-      if (32 * i < EP) *reinterpret_cast<v4u*>(s_w + swz(row, ch)) = rw[i];
-    }
-  };
-  auto kloop = [&](auto nq_c) __attribute__((always_inline)) {
+  auto kloop = [&](auto nq_c, auto nw_c) __attribute__((always_inline)) {
     constexpr int NQ = decltype(nq_c)::value;
+    constexpr int NW = decltype(nw_c)::value;
+    constexpr int NL = 2 + NW;  // DMA loads per wave and stage
+    const int stage_elems = (kTok + 32 * NW) * kBK;
+    uint32_t xo[2], wo[NW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = t0 + (2 * wave + i) * 8 + r_in;
+      xo[i] = (uint32_t)(r < T ? r : T - 1) * (uint32_t)H * 2u + chunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int r = (NW * wave + i) * 8 + r_in;
+      wo[i] = (uint32_t)(r < E ? r : E - 1) * (uint32_t)H * 2u + chunk * 16;
+    }
     f32x16_t acc[NQ > 0 ? NQ : 1];
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
-    auto compute = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int tile = q * 4 + wave;
-          const int eb = tile >> 1, tb = tile & 1;
-          const int er = eb * 32 + (lane & 31), tr = tb * 32 + (lane & 31);
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
-          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(s_x + swz(tr, ch));
-          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
-        }
-      }
-    };
     const int nk = (kend - kbeg) / kBK;
-    v4u rxa[2], rwa[8], rxb[2], rwb[8];  // the two load sets
-    gload(kbeg, rxa, rwa);
-    if (nk > 1) gload(kbeg + kBK, rxb, rwb);
-    for (int kt = 0; kt < nk; kt += 2) {
-      lds_barrier();  // previous compute done with the tile
-      sstore(rxa, rwa);
+    // prologue: stages 0 and 1 in flight (no MFMAs)
+    f32x16_t none[1];
+    router_step<0, NW>(s_ring, s_ring, nk > 0, rx, rw, xo, wo, (uint32_t)kbeg * 2u, none, wave,
+                       lane);
+    router_step<0, NW>(s_ring + stage_elems, s_ring, nk > 1, rx, rw, xo, wo,
+                       (uint32_t)(kbeg + kBK) * 2u, none, wave, lane);
+    int cur = 0;  // ring buffer of stage kt
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk)
+        wait_vmcnt(NL);  // stage kt landed; stage kt + 1 may still be in flight
+      else
+        wait_vmcnt(0);
       lds_barrier();
-      if (kt + 2 < nk) gload(kbeg + (kt + 2) * kBK, rxa, rwa);
-      compute();
-      if (kt + 1 < nk) {
-        lds_barrier();
-        sstore(rxb, rwb);
-        lds_barrier();
-        if (kt + 3 < nk) gload(kbeg + (kt + 3) * kBK, rxb, rwb);
-        compute();
-      }
+      const int nxt = cur == 0 ? 2 : cur - 1;  // (kt + 2) mod kStages
+      router_step<NQ, NW>(s_ring + nxt * stage_elems, s_ring + cur * stage_elems, kt + 2 < nk,
+                          rx, rw, xo, wo, (uint32_t)(kbeg + (kt + 2) * kBK) * 2u, acc, wave,
+                          lane);
+      cur = cur == 2 ? 0 : cur + 1;
     }
-    __syncthreads();  // tiles dead; s_log aliases them
+    __syncthreads();  // ring dead; s_log aliases it
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int tile = q * 4 + wave;
@@ -234,12 +270,20 @@ __device__ __forceinline__ void router_logits_mfma(int T, int H, int E, int t0, 
       }
     }
   };
-  switch (nq) {  // wave-uniform
-    case 0: kloop(std::integral_constant<int, 0>{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    default: kloop(std::integral_constant<int, 4>{}); break;
+  auto by_nq = [&](auto nw_c) __attribute__((always_inline)) {
+    switch (nq) {  // wave-uniform
+      case 0: kloop(std::integral_constant<int, 0>{}, nw_c); break;
+      case 1: kloop(std::integral_constant<int, 1>{}, nw_c); break;
+      case 2: kloop(std::integral_constant<int, 2>{}, nw_c); break;
+      case 3: kloop(std::integral_constant<int, 3>{}, nw_c); break;
+      default: kloop(std::integral_constant<int, 4>{}, nw_c); break;
+    }
+  };
+  switch (router_wrows(E)) {
+    case 32: by_nq(std::integral_constant<int, 1>{}); break;
+    case 64: by_nq(std::integral_constant<int, 2>{}); break;
+    case 128: by_nq(std::integral_constant<int, 4>{}); break;
+    default: by_nq(std::integral_constant<int, 8>{}); break;
   }
 }
 
@@ -627,7 +671,7 @@ void launch_partial(const moe_config& c, const void* x, const void* w, float* pa
   const int ks = router_k_splits(c), E = c.num_experts;
   const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * (EP + 1) * sizeof(float);
-  const size_t tiles = (size_t)(kTok + EP) * kBK * sizeof(uint16_t);
+  const size_t tiles = router_tile_lds(E);
   if (tiles > lds) lds = tiles;
   router_partial_kernel<<<dim3(router_num_blocks(c, false), ks), kThreads, lds, s>>>(
       c.num_tokens, c.hidden, E, c.hidden / ks, static_cast<const uint16_t*>(x),
@@ -668,7 +712,7 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
   const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * router_ls(E, 64) * sizeof(float);
   if (x && c.dtype == MOE_DTYPE_BF16) {
-    const size_t tiles = (size_t)(kTok + EP) * kBK * sizeof(uint16_t);
+    const size_t tiles = router_tile_lds(E);
     if (tiles > lds) lds = tiles;
   }
   if (lds < 4 * 256 * sizeof(float)) lds = 4 * 256 * sizeof(float);
