@@ -173,19 +173,30 @@ __device__ __forceinline__ void router_step(uint16_t* __restrict__ dst,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (lds_void_t*)(dst + (kTok + (NW * wave + i) * 8) * kBK), 16, wo[i], kb, 0, 0);
   }
-  const uint16_t* s_w = src + kTok * kBK;
+  // all fragments of the stage first (the token block, wave & 1, is the same
+  // for every tile of the wave), then the MFMAs: the reads' latency overlaps
+  // the MFMA pipe instead of stalling each MFMA on its own reads
+  if constexpr (NQ > 0) {
+    constexpr int KK = kBK / 16;
+    const uint16_t* s_w = src + kTok * kBK;
+    const int tr = (wave & 1) * 32 + (lane & 31);
+    bf16x8_t fb[KK], fa[KK][NQ];
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int ch = kk * 2 + (lane >> 5);
+      fb[kk] = *reinterpret_cast<const bf16x8_t*>(src + swz(tr, ch));
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int tile = q * 4 + wave;
-      const int eb = tile >> 1, tb = tile & 1;
-      const int er = eb * 32 + (lane & 31), tr = tb * 32 + (lane & 31);
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(src + swz(tr, ch));
-      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
+      for (int q = 0; q < NQ; ++q) {
+        const int er = (q * 2 + (wave >> 1)) * 32 + (lane & 31);  // expert block (q 4 + wave) / 2
+        fa[kk][q] = *reinterpret_cast<const bf16x8_t*>(s_w + swz(er, ch));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][q], fb[kk], acc[q], 0, 0, 0);
   }
 }
 
