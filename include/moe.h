@@ -156,8 +156,8 @@ typedef struct {
  * A tile's codes for one 64-element chunk are one contiguous 1 KB, and a
  * group's (scale, bias) for 32 rows one 128-byte line, so the kernels load
  * them with fully used cache lines; one byte permute forms two bf16 operands
- * from a word. (MLX's row-major packing, element i of a word at bits 4i,
- * converts to this layout once, on the host.)
+ * from a word. Weights in MLX's row-major packing convert to this layout once,
+ * on the host, with moe_w4_from_mlx below.
  * Device pointers, 16-byte aligned. Used by the *_w4 entry points, which need
  * dtype bf16 and H, I multiples of 512 (MOE_ERR_UNSUPPORTED otherwise). */
 typedef struct {
@@ -168,6 +168,23 @@ typedef struct {
   const void* up_sb;
   const void* down_sb;
 } moe_w4_weights;
+
+/* Host-only conversion of one 4-bit matrix [E, N, K] from MLX's row-major
+ * packing to the tiled layout of moe_w4_weights (the format of the page's
+ * 4-bit model, [MOE-128x8] 参数量化与存储优化: group_size 128, a scale and a
+ * bias per group, w = scale * q + bias).
+ *   mlx_w      [E, N, K/8] uint32: code q of element k of row n in bits
+ *              4*(k%8) .. 4*(k%8)+3 of word [e, n, k/8];
+ *   mlx_scales, mlx_biases [E, N, K/128] bf16 (16-bit patterns);
+ *   codes      out, [E, N/32, K/64, 32, 32] uint8 (layout above);
+ *   sb         out, [E, N/32, K/128, 32, 2] bf16 (scale, bias) pairs.
+ * All HOST pointers, caller-owned, not overlapping; nothing is enqueued.
+ * Returns MOE_ERR_INVALID_ARGUMENT for a NULL pointer or a size < 1, and
+ * MOE_ERR_UNSUPPORTED unless N % 32 == 0 and K % 128 == 0 (then nothing is
+ * written). The conversion only moves bits: the dequantised values are equal. */
+moe_status moe_w4_from_mlx(int E, int N, int K, const uint32_t* mlx_w,
+                           const uint16_t* mlx_scales, const uint16_t* mlx_biases,
+                           uint8_t* codes, uint16_t* sb);
 
 /* Bytes of workspace every entry point below needs for `cfg` (the maximum
  * over all of them). Host-only and pure; returns 0 if `cfg` is invalid. */

@@ -10,6 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 from .configs import MoEConfig
@@ -26,7 +28,7 @@ EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_ro
            "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_z_loss", "moe_layer_forward",
            "moe_layer_forward_ex", "moe_expert_gate_up_w4", "moe_expert_down_w4",
-           "moe_layer_forward_w4", "moe_layer_forward_noalloc")
+           "moe_layer_forward_w4", "moe_layer_forward_noalloc", "moe_w4_from_mlx")
 
 # bytes of the library-owned scratch of moe_layer_forward_noalloc (moe.h)
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -94,6 +96,7 @@ def load(path: str = LIB_PATH):
         "moe_layer_forward_w4": [C, ctypes.POINTER(moe_options), V, V, V,
                                  ctypes.POINTER(moe_w4_weights), V, V, V, V, moe_aux_out, V, S,
                                  V],
+        "moe_w4_from_mlx": [st, st, st, V, V, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -246,6 +249,24 @@ def layer_forward_noalloc(c: moe_config, x, w_router, logit_bias, w_gate, w_up, 
                                             _ptr(topk_idx), _ptr(topk_w), _aux(counts, f, P, aux),
                                             _stream()),
            "moe_layer_forward_noalloc")
+
+
+def w4_from_mlx(mlx_w, mlx_scales, mlx_biases) -> tuple:
+    """moe_w4_from_mlx on host arrays: mlx_w uint32 [E,N,K/8], scales and
+    biases uint16 (bf16 bits) [E,N,K/128] -> (codes uint8 [E,N/32,K/64,32,32],
+    sb uint16 [E,N/32,K/128,32,2])."""
+    w = np.ascontiguousarray(mlx_w, dtype=np.uint32)
+    sc = np.ascontiguousarray(mlx_scales, dtype=np.uint16)
+    bi = np.ascontiguousarray(mlx_biases, dtype=np.uint16)
+    E, N, K8 = w.shape
+    K = 8 * K8
+    if sc.shape != (E, N, K // 128) or bi.shape != sc.shape:
+        raise ValueError(f"scales/biases must be [E, N, K/128] = {(E, N, K // 128)}")
+    codes = np.empty((E, N // 32, K // 64, 32, 32), np.uint8)
+    sb = np.empty((E, N // 32, K // 128, 32, 2), np.uint16)
+    _check(load().moe_w4_from_mlx(E, N, K, w.ctypes.data, sc.ctypes.data, bi.ctypes.data,
+                                  codes.ctypes.data, sb.ctypes.data), "moe_w4_from_mlx")
+    return codes, sb
 
 
 def _with_z_loss(opts: moe_options | None, z_loss) -> moe_options | None:

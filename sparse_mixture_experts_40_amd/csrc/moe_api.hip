@@ -502,6 +502,34 @@ moe_status moe_expert_down_w4(const moe_config* cfg, const void* h,
   return launched(launch_down_w4(*cfg, h, expert_offsets, *w, y_sorted, stream));
 }
 
+moe_status moe_w4_from_mlx(int E, int N, int K, const uint32_t* mlx_w,
+                           const uint16_t* mlx_scales, const uint16_t* mlx_biases,
+                           uint8_t* codes, uint16_t* sb) {
+  if (!mlx_w || !mlx_scales || !mlx_biases || !codes || !sb || E < 1 || N < 1 || K < 1)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (N % 32 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const size_t NB = (size_t)N / 32, KC = (size_t)K / 64, KG = (size_t)K / 128;
+  for (size_t e = 0; e < (size_t)E; ++e)
+    for (size_t n = 0; n < (size_t)N; ++n) {
+      const size_t row = e * N + n, b = e * NB + n / 32, r = n % 32;
+      // codes: MLX word w holds elements 8w .. 8w + 7 at nibbles 0..7; the
+      // tiled word of those 8 elements holds element j (j < 4) in the low and
+      // element j + 4 in the high nibble of byte j
+      for (size_t w = 0; w < (size_t)K / 8; ++w) {
+        const uint32_t u = mlx_w[row * (K / 8) + w];
+        uint8_t* dst = codes + (b * KC + w / 8) * 1024 + r * 32 + 4 * (w % 8);
+        for (int j = 0; j < 4; ++j)
+          dst[j] = (uint8_t)(((u >> (4 * j)) & 15u) | (((u >> (16 + 4 * j)) & 15u) << 4));
+      }
+      for (size_t g = 0; g < KG; ++g) {
+        uint16_t* d = sb + ((b * KG + g) * 32 + r) * 2;
+        d[0] = mlx_scales[row * KG + g];
+        d[1] = mlx_biases[row * KG + g];
+      }
+    }
+  return MOE_OK;
+}
+
 moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
                                      const float* logit_bias, const void* w_gate,
                                      const void* w_up, const void* w_down, void* out,
