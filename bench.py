@@ -282,6 +282,9 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
     ms_step = evs[0].elapsed_time(evs[steps]) / steps
     step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     log(f"{cfg.name}: {ms_step:.4f} ms/step (events), wall {wall * 1e3 / steps:.4f} ms/step")
+    if args.layer_only:  # profiling: nothing but the warm-up and the timed steps
+        return {"ms_per_step": ms_step, "value": cfg.T / (ms_step * 1e-3),
+                "step_ms": dist(step_ms)}, inp, w4in
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     streaming = uses_decode_kernel(cfg) or w4
@@ -475,6 +478,9 @@ def main():
                     help="> 0: entropy-driven number of experts per token in [KMIN, k]")
     ap.add_argument("--w4", action="store_true",
                     help="4-bit group-quantised expert weights (codes + per-128 scale/bias)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="profiling: run only the warm-up and the timed layer steps, print "
+                         "their time and exit (no kernel legs, stages or CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times: the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -512,6 +518,11 @@ def main():
     rep, inp, w4in = measure(torch, binding, cfg, args, args.steps, w4=args.w4,
                              cap_factor=args.capacity_factor, router=args.router,
                              dynamic_k_min=args.dynamic_k_min)
+    if args.layer_only:
+        print(json.dumps({"layer_only": True, "workload": cfg.name, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": rep["ms_per_step"],
+                          "tokens_per_s": rep["value"], "step_ms": rep["step_ms"]}), flush=True)
+        return
     line = {
         "metric": METRIC, "value": rep["value"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": rep["ms_per_step"],
