@@ -50,21 +50,25 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 # HBM traffic of the gate/up kernel per launch, from rocprofv3 --pmc FETCH_SIZE
-# and WRITE_SIZE passes over this script (KiB per dispatch, averaged), scaled by
-# what the same counters read for a plain 1 GiB device copy (bench.py
-# --copy-calibration): FETCH_SIZE reported 524303 KiB for 1 GiB read (x2.0),
-# WRITE_SIZE 1048576 KiB for 1 GiB written (x1.0). Valid only for the kernel
-# sources they were taken on (sha256 below); otherwise traffic is null.
+# and WRITE_SIZE passes over the layer's own steps (bench.py --layer-only, 3
+# timed steps after 1 warm-up; KiB per dispatch, averaged over the timed ones),
+# scaled by what the same counters read for a plain 1 GiB device copy (bench.py
+# --copy-calibration): FETCH_SIZE reported 524304.8 KiB for 1 GiB read (x2.0),
+# WRITE_SIZE 1048576 KiB for 1 GiB written (x1.0). Valid only for the sources
+# they were taken on (sha256 below: the kernel, its dispatch input order and
+# the build flags); otherwise traffic is null.
 TRAFFIC_SOURCES = ("sparse_mixture_experts_40_amd/csrc/expert_gemm.hip",
-                   "sparse_mixture_experts_40_amd/csrc/moe_internal.h")
-FETCH_SCALE = 1048576.0 / 524302.4
+                   "sparse_mixture_experts_40_amd/csrc/moe_internal.h",
+                   "sparse_mixture_experts_40_amd/csrc/dispatch.hip",
+                   "sparse_mixture_experts_40_amd/build.py")
+FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("f569da93d9a4ba92e69975a45e9acfe54e18d7da914d8fe90a12ae8c27feacb0",
-                        3798049.5, 394143.9),
-    "decode128_bf16": ("f569da93d9a4ba92e69975a45e9acfe54e18d7da914d8fe90a12ae8c27feacb0",
-                       542903.0, 1561.8),
+    "prefill128_bf16": ("7838da92ed070d4c3d84d3a174c126b05b57fb0751235e538485b40f16777d84",
+                        3940136.3, 394065.1),
+    "decode128_bf16": ("7838da92ed070d4c3d84d3a174c126b05b57fb0751235e538485b40f16777d84",
+                       542887.6, 1556.5),
 }
 
 
