@@ -62,7 +62,7 @@ __device__ __forceinline__ int swz_f(int r) {
 // only for the fragments it needs.
 // Loads [i0, i1) of the wave's LA + LB (A first, then B); the whole stage by
 // default.
-template <int BK, int BM, int NW>
+template <int BK, int BM, int NW, bool WNT>
 __device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* __restrict__ dB,
                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t* a_off, const uint32_t* b_off, uint32_t kb,
@@ -78,7 +78,7 @@ __device__ __forceinline__ void dma_stage(uint16_t* __restrict__ dA, uint16_t* _
   for (int i = 0; i < LB; ++i)
     if (LA + i >= i0 && LA + i < i1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dB + (wave * LB + i) * RPI * BK),
-                                               16, b_off[i], kb, 0, 0);
+                                               16, b_off[i], kb, 0, WNT ? 2 : 0);
 }
 
 // Fragments of k step kk of a stage: NB weight blocks (A operand) and the MBV
@@ -112,7 +112,7 @@ __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ sA,
 // The distinct __restrict__ pointers give the LDS accesses disjoint alias
 // scopes, so the compiler does not drain the in-flight LDS-DMA loads before
 // every fragment read; the explicit wait_vmcnt + lds_barrier order them.
-template <int BK, int BM, int NW, int MB, int NB, int MBV>
+template <int BK, int BM, int NW, int MB, int NB, int MBV, bool WNT>
 __device__ __forceinline__ void gemm_step(
     uint16_t* __restrict__ dA, uint16_t* __restrict__ dB, bool issue_next,
     __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase, const uint32_t* a_off,
@@ -134,7 +134,7 @@ __device__ __forceinline__ void gemm_step(
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (kk < KD && issue_next)
-      dma_stage<BK, BM, NW>(dA, dB, abase, bbase, a_off, b_off, kb, wave, NL * kk / KD,
+      dma_stage<BK, BM, NW, WNT>(dA, dB, abase, bbase, a_off, b_off, kb, wave, NL * kk / KD,
                             NL * (kk + 1) / KD);
     if (kk + 1 < KK)
       stage_frag<BK, MB, NB, MBV>(cA, cB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wrow,
@@ -187,7 +187,7 @@ __device__ __forceinline__ void gemm_step(
 // the number of store instructions that epilogue issued: the counter
 // completes in order, so the stage has landed once no more than those stores
 // remain. The count must never exceed the stores actually issued.
-template <int BK, int BM, int NST, int NW, int MB, int NB, int MBV>
+template <int BK, int BM, int NST, int NW, int MB, int NB, int MBV, bool WNT>
 __device__ __forceinline__ void tile_k(uint16_t* smem, int nk, int g0, bool pf, int st_allow,
                                        __amdgpu_buffer_rsrc_t abase, __amdgpu_buffer_rsrc_t bbase,
                                        __amdgpu_buffer_rsrc_t bbase_n, const uint32_t* a_off,
@@ -218,7 +218,7 @@ __device__ __forceinline__ void tile_k(uint16_t* smem, int nk, int g0, bool pf, 
     uint16_t* dA = smem + ((g + NST - 1) % NST) * STAGE;
     const uint16_t* cA = smem + (g % NST) * STAGE;
     const uint16_t* nA = smem + ((g + 1) % NST) * STAGE;
-    gemm_step<BK, BM, NW, MB, NB, MBV>(
+    gemm_step<BK, BM, NW, MB, NB, MBV, WNT>(
         dA, dA + BM * BK, in_cur || pf, abase, in_cur ? bbase : bbase_n, ao, bo,
         (uint32_t)((in_cur ? is : is - nk) * BK) * 2u, cA, cA + BM * BK, nA, nA + BM * BK, vm,
         acc, fa, fb, wrow, trow0, lane, sw, wave);
@@ -291,7 +291,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 //         row tile minor, so concurrent blocks share weight tiles in L2.
 // Rows past an expert's end and columns past N are clamped to valid memory on
 // load and never stored.
-template <bool GATEUP, int BM, int BK, int NST, int NW, int OCC>
+template <bool GATEUP, int BM, int BK, int NST, int NW, int OCC, bool WNT>
 __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     if (!staged) {
       for (int st = 0; st < npro; ++st) {
         uint16_t* d = smem + ((g0 + st) % NST) * STAGE;
-        dma_stage<BK, BM, NW>(d, d + BM * BK, abase, bbase, a_off, b_off,
+        dma_stage<BK, BM, NW, WNT>(d, d + BM * BK, abase, bbase, a_off, b_off,
                               (uint32_t)(st * BK) * 2u, wave);
       }
       wait_vmcnt((LA + LB) * (npro - 1));
@@ -396,22 +396,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
     const int live = min(BM, cur.row_end - cur.row0) - wm * 32;
     const int mbv = live <= 0 ? 0 : min(MB, (live + 63) / 64);
     if (mbv >= MB)
-      tile_k<BK, BM, NST, NW, MB, NB, MB>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n,
+      tile_k<BK, BM, NST, NW, MB, NB, MB, WNT>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n,
                                           a_off, b_off, a_offn, b_offn, acc, wrow, trow0, lane,
                                           sw, wave);
     else if (mbv == 3)
-      tile_k<BK, BM, NST, NW, MB, NB, (MB > 3 ? 3 : MB)>(smem, nk, g0, prefetch, st_allow, abase, bbase,
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 3 ? 3 : MB), WNT>(smem, nk, g0, prefetch, st_allow, abase, bbase,
                                                          bbase_n, a_off, b_off, a_offn, b_offn,
                                                          acc, wrow, trow0, lane, sw, wave);
     else if (mbv == 2)
-      tile_k<BK, BM, NST, NW, MB, NB, (MB > 2 ? 2 : MB)>(smem, nk, g0, prefetch, st_allow, abase, bbase,
+      tile_k<BK, BM, NST, NW, MB, NB, (MB > 2 ? 2 : MB), WNT>(smem, nk, g0, prefetch, st_allow, abase, bbase,
                                                          bbase_n, a_off, b_off, a_offn, b_offn,
                                                          acc, wrow, trow0, lane, sw, wave);
     else if (mbv == 1)
-      tile_k<BK, BM, NST, NW, MB, NB, 1>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
+      tile_k<BK, BM, NST, NW, MB, NB, 1, WNT>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
                                          a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
     else
-      tile_k<BK, BM, NST, NW, MB, NB, 0>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
+      tile_k<BK, BM, NST, NW, MB, NB, 0, WNT>(smem, nk, g0, prefetch, st_allow, abase, bbase, bbase_n, a_off, b_off,
                                          a_offn, b_offn, acc, wrow, trow0, lane, sw, wave);
     // No barrier here: the only LDS the epilogue touches is the stage computed
     // last (its reads finished before the last stage barrier), and the next
@@ -475,8 +475,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
       }
     }
     } else {
-      static_assert(NB * 32 == kYChunk, "one scaled-fp16 chunk per wave and row");
-      // this wave's kYChunk columns lie wholly inside N or wholly past it
+      constexpr int NG = NB * 32 / kYChunk;  // scaled-fp16 chunks per wave and row
+      static_assert(NG * kYChunk == NB * 32 && kYChunk == 64, "whole chunks of two blocks");
+      // each kYChunk columns of this wave lie wholly inside N or wholly past it
       const int ycol0 = n0 + wn * NB * 32;
       if (y_exp) {
         // scaled fp16 straight from the accumulators, no LDS: lane l holds 4
@@ -497,12 +498,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
         st_after = 0;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          st_after += (ycol0 < N_out && row0 + mb * 64 + wm * 32 < row_end) ? 2 * NB : 0;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+          for (int g = 0; g < NG; ++g)
+            st_after +=
+                (ycol0 + g * kYChunk < N_out && row0 + mb * 64 + wm * 32 < row_end) ? 4 : 0;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
           float mx = 0.0f;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 2 * g; nb < 2 * g + 2; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc[nb][mb][r]));
           {
@@ -512,12 +518,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void grouped_gemm_bf16_kernel(
           }
           const int e = yh_exponent(__float_as_uint(mx));
           const float sc = pow2i(-e);
+          const int gcol0 = ycol0 + g * kYChunk;
           const int grow = row0 + mb * 64 + wm * 32 + (lane & 31);
-          const bool live = grow < row_end && ycol0 < N_out;
+          const bool live = grow < row_end && gcol0 < N_out;
           if (h == 0 && live)
-            y_exp[(size_t)grow * (N_out / kYChunk) + ycol0 / kYChunk] = (int8_t)e;
+            y_exp[(size_t)grow * (N_out / kYChunk) + gcol0 / kYChunk] = (int8_t)e;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
+          for (int nb = 2 * g; nb < 2 * g + 2; ++nb) {
             uint32_t pk[4][2];  // column group q as 4 fp16 in 2 words
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1546,6 +1553,14 @@ int persistent_grid() {
 
 }  // namespace
 
+// Weight loads of the tiled GEMMs with the non-temporal hint when one
+// expert's matrix is large (64 MB or more, e.g. 8 experts x 14336 x 4096): its
+// stream would otherwise push the token rows, which every column tile reads
+// again, out of the MALL (-3.6% layer time at that shape). With small experts
+// the hint costs the L2 reuse of weight tiles across row tiles (+4.8% at 128
+// experts of 1536 x 4096), so it is off there.
+static bool gemm_weights_streamed(size_t expert_bytes) { return expert_bytes >= ((size_t)64 << 20); }
+
 hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,
                           const int32_t* offsets, const void* w_gate, const void* w_up, void* h,
                           hipStream_t s) {
@@ -1566,11 +1581,18 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
     return hipGetLastError();
   }
   const int ntn = (c.intermediate + 127) / 128;
-  grouped_gemm_bf16_kernel<true, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
-      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
-      c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
-      sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
-      static_cast<const uint16_t*>(w_up), h, ntn, nullptr);
+  const size_t wexp = (size_t)2 * c.intermediate * c.hidden * 2;  // gate + up bytes per expert
+#define MOE_GATE_UP(WNT)                                                                  \
+  grouped_gemm_bf16_kernel<true, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc, WNT> \
+      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(                          \
+          c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x), \
+          sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),                    \
+          static_cast<const uint16_t*>(w_up), h, ntn, nullptr)
+  if (gemm_weights_streamed(wexp))
+    MOE_GATE_UP(true);
+  else
+    MOE_GATE_UP(false);
+#undef MOE_GATE_UP
   return hipGetLastError();
 }
 
@@ -1593,10 +1615,17 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
     return hipGetLastError();
   }
   const int ntn = (c.hidden + 255) / 256;
-  grouped_gemm_bf16_kernel<false, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc>
-      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(
-      c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h), nullptr,
-      offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn, y_exp);
+  const size_t wexp = (size_t)c.hidden * c.intermediate * 2;  // down bytes per expert
+#define MOE_DOWN(WNT)                                                                      \
+  grouped_gemm_bf16_kernel<false, kGemmBM, kGemmBK, kGemmStages, kGemmWaves, kGemmOcc, WNT> \
+      <<<persistent_grid() * kGemmOcc, 64 * kGemmWaves, 0, s>>>(                           \
+          c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),  \
+          nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, ntn, y_exp)
+  if (gemm_weights_streamed(wexp))
+    MOE_DOWN(true);
+  else
+    MOE_DOWN(false);
+#undef MOE_DOWN
   if (y_exp && y_half) *y_half = true;
   return hipGetLastError();
 }
