@@ -15,8 +15,9 @@
 //             bit of the expert id), wave counts go through LDS, so pairs of an
 //             expert land in ascending pair order (a stable sort).
 // With a single chunk (P <= kChunk, the decode case) the three steps run in
-// one block and one launch, followed (do_aux) by the load-balance statistics
-// from these counts, which then need no launch of their own.
+// one block and one launch; a second block of the same launch (do_aux) makes
+// the same histogram and from it the load-balance statistics, while the
+// first one sorts, so they need no launch of their own.
 // Capacity ([MOE-128x8] 容量因子设计; [QWEN3-ROUTE] §四, tokens taken in order,
 // an expert accepts while below its capacity): the pair of rank r inside its
 // expert is kept iff r < capacity, i.e. each expert keeps its first
@@ -187,6 +188,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
   hist_chunk(P, E, idx, 0, s_h);
   __syncthreads();
   const int tot = e < E ? s_h[e] : 0;
+  if (blockIdx.x == 1) {  // the statistics, next to block 0's sort
+    if (do_aux) aux_small_body(aux, e < E ? tot : 0);  // block-uniform
+    return;
+  }
   const int kept = (cap > 0 && tot > cap) ? cap : tot;
   s_c[e] = kept;
   __syncthreads();
@@ -204,8 +209,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
     if (offsets && e == E - 1) offsets[E] = s_c[e];
   }
   if (dropped && e == 0) *dropped = s_drop;
-  if (do_aux) aux_small_body(aux, e < E ? tot : 0);  // block-uniform
-  if (!scatter) return;                              // block-uniform
+  if (!scatter) return;  // block-uniform
   s_off[e] = excl;
   s_h[e] = 0;  // becomes the running rank of each expert
   __syncthreads();
@@ -248,7 +252,8 @@ hipError_t launch_dispatch_aux(const moe_config& c, const int32_t* topk_idx, int
   if (!*fused)
     return launch_dispatch(c, topk_idx, counts, offsets, sorted_pair, pair_pos, hist, rank0, true,
                            capacity, dropped, s);
-  dispatch_single_kernel<<<1, kThreads, 0, s>>>(c.num_tokens * c.top_k, c.num_experts, capacity,
+  // block 1 computes the statistics while block 0 sorts
+  dispatch_single_kernel<<<2, kThreads, 0, s>>>(c.num_tokens * c.top_k, c.num_experts, capacity,
                                                 topk_idx, counts, offsets, dropped, 1,
                                                 sorted_pair, pair_pos, 1, aux);
   return hipGetLastError();
