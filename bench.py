@@ -65,10 +65,10 @@ FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("7838da92ed070d4c3d84d3a174c126b05b57fb0751235e538485b40f16777d84",
-                        3940136.3, 394065.1),
-    "decode128_bf16": ("7838da92ed070d4c3d84d3a174c126b05b57fb0751235e538485b40f16777d84",
-                       542887.6, 1556.5),
+    "prefill128_bf16": ("6bd464ef2c4eec35f81c75ca4d9e538ae32d940dc7f3583de3db370746fccee9",
+                        3959927.0, 393960.9),
+    "decode128_bf16": ("6bd464ef2c4eec35f81c75ca4d9e538ae32d940dc7f3583de3db370746fccee9",
+                       542859.2, 1550.3),
 }
 
 
