@@ -19,8 +19,10 @@
 //         the W_up rows of the same columns, so each lane holds matching g and
 //         u; the epilogue writes h = silu(g) * u (fp32 math, one bf16
 //         rounding). The token rows are gathered through sorted_pair / k;
-//   down: y_sorted = h W_down^T over contiguous h rows, stored in fp32 (the
-//         combine adds the k rows of a token in fp32 and rounds once).
+//   down: y_sorted = h W_down^T over contiguous h rows, stored in fp32, or
+//         inside the bf16 layer forward as fp16 scaled by 2^-e per row and 64
+//         columns (the combine folds 2^e into the routing weight, adds the k
+//         rows of a token in fp32 and rounds once).
 // Decode-sized batches (few rows per expert) take the weight-streaming
 // kernels further down instead.
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
