@@ -65,9 +65,9 @@ FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("6bd464ef2c4eec35f81c75ca4d9e538ae32d940dc7f3583de3db370746fccee9",
+    "prefill128_bf16": ("71793fbe95c36eb3431797b799752da2d3aa49795ded86c2f31a444f12d70d83",
                         3959927.0, 393960.9),
-    "decode128_bf16": ("6bd464ef2c4eec35f81c75ca4d9e538ae32d940dc7f3583de3db370746fccee9",
+    "decode128_bf16": ("71793fbe95c36eb3431797b799752da2d3aa49795ded86c2f31a444f12d70d83",
                        542859.2, 1550.3),
 }
 
