@@ -26,6 +26,13 @@ main one, and reports it as the line's "decode" object (ms/step, tokens/s, the
 layer's fraction of HBM bandwidth, the gate/up roofline, stages, and the
 MALL-scrubbed variants); `value` and the rest of the line stay the main
 workload's.
+
+The CPU-oracle leg also compares, outside its timed calls, the oracle's
+outputs on its sample tokens with the timed block's output and selection
+(plain routing, bf16 or 4-bit weights): the line's "parity" object holds the
+number of tokens whose selection differs (recomputed by the oracle with the
+GPU's selection), the largest |d| over RMS(ref), and the largest share of the
+element tolerance used.
 """
 from __future__ import annotations
 
@@ -127,24 +134,27 @@ def layer_algorithmic(cfg, counts: np.ndarray, rows: int, w4: bool = False):
     return flops, bytes_
 
 
-def cpu_baseline(cfg, inp, budget_s: float, w4=None):
+def cpu_baseline(cfg, inp, budget_s: float, w4=None, gpu=None):
     """The oracle as it stands on a bounded sample of tokens of the same
-    workload (4-bit weights: its 4-bit forward); returns tokens/s, cores used
-    and the sample description."""
+    workload (4-bit weights: its 4-bit forward); returns (tokens/s, cores used
+    and the sample description; parity of the GPU's block output on the
+    sample, or None). `gpu` holds the timed block's output [T,H] and
+    selection [T,k] on the host (None: no parity figures). The comparison
+    runs after the timed oracle calls, outside their time."""
     from oracle import oracle
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     cores = int(os.environ["OMP_NUM_THREADS"])
 
-    def forward(tokens):
+    def forward(tokens, forced_idx=None):
         if w4 is None:
-            oracle.forward_tokens(inp, cfg, tokens=tokens)
-        else:
-            oracle.forward_w4(inp, w4, cfg, tokens=tokens)
+            return oracle.forward_tokens(inp, cfg, tokens=tokens, forced_idx=forced_idx)
+        return oracle.forward_w4(inp, w4, cfg, tokens=tokens, forced_idx=forced_idx)
 
     n = 8
+    tok = np.arange(n, dtype=np.int32)
     t0 = time.perf_counter()
-    forward(np.arange(n, dtype=np.int32))
+    ref = forward(tok)
     dt = time.perf_counter() - t0
     # scale the sample to about `budget_s` seconds
     want = int(max(n, n * budget_s / max(dt, 1e-3)))
@@ -155,14 +165,56 @@ def cpu_baseline(cfg, inp, budget_s: float, w4=None):
         tok = np.linspace(0, cfg.T - 1, n2).astype(np.int32)
         t0 = time.perf_counter()
         for _ in range(passes):
-            forward(tok)
+            ref = forward(tok)
         dt = time.perf_counter() - t0
         n = n2 * passes
+    else:
+        n2 = n
     what = (f"{n2} of {cfg.T} tokens" if passes == 1 else
             f"all {cfg.T} tokens x {passes} passes")
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    base = {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{what} of {cfg.name} (full block forward per token, "
                       f"fp64 scalar loops), {dt:.1f} s"}
+    return base, (sample_parity(cfg, tok, ref, gpu, forward) if gpu is not None else None)
+
+
+def sample_parity(cfg, tok, ref, gpu, forward):
+    """The GPU block's output and selection on the oracle's sample tokens.
+
+    A token whose selection (experts or their slot order) differs from the
+    oracle's is counted, its k-th/(k+1)-th logit gap recorded, and its oracle
+    output recomputed with the GPU's selection (forced routing) before the
+    outputs are compared. Tolerance: bf16, |d| <= 2e-2 * RMS(ref) + 2^-8 |ref|
+    per element (the second term is the rounding of a bf16 output); fp32,
+    |d| <= 1e-4. `allowance_used` is the largest |d| over its allowance."""
+    gidx = np.asarray(gpu["idx"])[tok]
+    mism = np.flatnonzero((gidx != ref["idx"]).any(1))
+    sets = sum(set(gidx[i].tolist()) != set(ref["idx"][i].tolist()) for i in mism)
+    gaps = []
+    for i in mism:
+        s_ = np.sort(ref["logits"][i].astype(np.float64))[::-1]
+        gaps.append(float(s_[cfg.k - 1] - s_[cfg.k]) if cfg.k < cfg.E else float("inf"))
+    out = np.array(ref["out"], dtype=np.float64)
+    if len(mism):
+        out[mism] = forward(tok[mism], forced_idx=np.ascontiguousarray(gidx[mism]))["out"]
+    got = np.asarray(gpu["out"])[tok].astype(np.float64)
+    d = np.abs(got - out)
+    rms = float(np.sqrt((out ** 2).mean()))
+    if cfg.dtype == "bf16":
+        allow = 2e-2 * rms + 2.0 ** -8 * np.abs(out)
+        tol = "|d| <= 2e-2*RMS(ref) + 2^-8*|ref| per element"
+    else:
+        allow = np.full_like(out, 1e-4)
+        tol = "|d| <= 1e-4 per element"
+    used = float((d / np.maximum(allow, 1e-300)).max())
+    return {"sample_tokens": int(len(tok)), "index_mismatch_tokens": int(len(mism)),
+            "expert_set_mismatch_tokens": int(sets),
+            "max_kth_gap_of_mismatches": max(gaps) if gaps else None,
+            "max_d_over_rms": float(d.max() / rms), "rms_d_over_rms":
+            float(np.sqrt((d ** 2).mean()) / rms),
+            "max_ref_over_rms": float(np.abs(out).max() / rms), "allowance_used": used,
+            "within_tolerance": bool(used <= 1.0), "tolerance": tol,
+            "reference": "oracle (fp64), mismatched selections recomputed with the GPU's"}
 
 
 def pct(v, q):
@@ -442,6 +494,14 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
     }
     if scrubbed:
         rep["mall_scrubbed"] = scrubbed
+    # the timed block's last output and selection, for the parity figures
+    plain = not (cap or router != "plain" or dynamic_k_min)
+    gpu = None
+    if plain:
+        blk.forward(x)
+        torch.cuda.synchronize()
+        gpu = {"out": blk.out.float().cpu().numpy(), "idx": blk.topk_idx.cpu().numpy()}
+    rep["_gpu"] = gpu
     del blk, h, y
     return rep, inp, w4in
 
@@ -546,7 +606,10 @@ def main():
         line["decode"] = decode_summary(drep)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget, w4in)
+        line["cpu_baseline"], par = cpu_baseline(cfg, inp, args.cpu_budget, w4in,
+                                                 gpu=rep.get("_gpu"))
+        if par is not None:
+            line["parity"] = par
     print(json.dumps(line), flush=True)
 
 

@@ -57,3 +57,69 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+def _small_bf16():
+    from sparse_mixture_experts_40_amd.configs import MoEConfig
+    return MoEConfig(name="small_bf16", T=48, H=128, E=16, k=4, I=64, norm=True, dtype="bf16",
+                     zipf_s=0.0, seed=5)
+
+
+def test_parity_leg_counts_mismatches_and_recomputes_them():
+    """The bench's parity figures on planted GPU results: a reordered slot and
+    a different expert set are counted, the latter compared against the
+    oracle's forced-routing output; an output error over the tolerance is
+    reported as such."""
+    import torch
+
+    from oracle import oracle
+    from sparse_mixture_experts_40_amd.inputs import make_inputs
+    cfg = _small_bf16()
+    inp = make_inputs(cfg)
+
+    def fwd(tokens, forced_idx=None):
+        return oracle.forward_tokens(inp, cfg, tokens=tokens, forced_idx=forced_idx)
+
+    tok = np.arange(cfg.T, dtype=np.int32)
+    ref = fwd(tok)
+    as_bf16 = torch.from_numpy(ref["out"]).to(torch.bfloat16).float().numpy()
+    gpu = {"out": as_bf16.copy(), "idx": ref["idx"].copy()}
+    p = bench.sample_parity(cfg, tok, ref, gpu, fwd)
+    assert p["index_mismatch_tokens"] == 0 and p["within_tolerance"]
+    assert p["max_d_over_rms"] < 2e-2
+    # slot order of token 3 reversed; token 7 routed to another expert set,
+    # with the output the oracle gives for that set
+    gpu["idx"][3] = gpu["idx"][3][::-1]
+    other = [e for e in range(cfg.E) if e not in ref["idx"][7]][0]
+    gpu["idx"][7, -1] = other
+    forced = fwd(np.array([7], np.int32), forced_idx=gpu["idx"][7:8].copy())["out"][0]
+    assert np.abs(forced - ref["out"][7]).max() > 0
+    gpu["out"][7] = torch.from_numpy(forced).to(torch.bfloat16).float().numpy()
+    p = bench.sample_parity(cfg, tok, ref, gpu, fwd)
+    assert p["index_mismatch_tokens"] == 2 and p["expert_set_mismatch_tokens"] == 1
+    assert p["within_tolerance"], p
+    # the same set change without the matching output is caught
+    gpu["out"][7] = as_bf16[7]
+    assert not bench.sample_parity(cfg, tok, ref, gpu, fwd)["within_tolerance"]
+    gpu["out"][7] = torch.from_numpy(forced).to(torch.bfloat16).float().numpy()
+    # one element 5% of RMS off
+    rms = float(np.sqrt((ref["out"] ** 2).mean()))
+    gpu["out"][11, 5] += 0.05 * rms
+    p = bench.sample_parity(cfg, tok, ref, gpu, fwd)
+    assert not p["within_tolerance"] and p["max_d_over_rms"] >= 0.049
+
+
+def test_cpu_baseline_returns_baseline_and_parity():
+    import torch
+
+    from oracle import oracle
+    from sparse_mixture_experts_40_amd.inputs import make_inputs
+    cfg = _small_bf16()
+    inp = make_inputs(cfg)
+    ref = oracle.forward_tokens(inp, cfg)
+    gpu = {"out": torch.from_numpy(ref["out"]).to(torch.bfloat16).float().numpy(),
+           "idx": ref["idx"]}
+    base, par = bench.cpu_baseline(cfg, inp, 0.05, gpu=gpu)
+    assert base["kind"] == "oracle" and base["value"] > 0
+    assert par["sample_tokens"] >= 8 and par["within_tolerance"]
+    assert bench.cpu_baseline(cfg, inp, 0.05)[1] is None
