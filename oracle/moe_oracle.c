@@ -341,6 +341,82 @@ int orc_dispatch_capacity(int T, int E, int k, int capacity, const int32_t* idx,
   return 0;
 }
 
+/* Capacity-limited routing with the least-loaded fallback, [QWEN3-ROUTE] §四
+ * (inference routing with expert capacities). The tokens are taken in order.
+ * Each of a token's experts, in slot order, accepts it while the number of
+ * tokens that expert has accepted is below `capacity`, and its count then
+ * grows by one. A token left with fewer than `fallback_min` accepted experts
+ * gets the least-loaded experts added: ascending accepted count at that
+ * moment (the token's own acceptances included), ties to the lower id, as
+ * many as it lacks. Those additions are not counted as acceptances.
+ * Slot form of the result (readings: the page keeps token lists per expert
+ * and does not weight them): a kept slot keeps its expert and weight; the
+ * added experts, in the order taken, go to the token's dropped slots in slot
+ * order, each with that slot's weight, and no more are added than the token
+ * has dropped slots; dropped slots left over and empty slots (id -1) get id -1
+ * and weight 0. *dropped counts the dropped slots left over. fallback_min = 0
+ * leaves every dropped slot empty (the plain capacity limit). */
+int orc_capacity_fallback(int T, int E, int k, int capacity, int fallback_min,
+                          const int32_t* idx, const float* w, int32_t* idx_out, float* w_out,
+                          int32_t* dropped) {
+  if (T < 0 || E < 1 || k < 1 || capacity < 1 || fallback_min < 0 || fallback_min > k || !idx ||
+      !w || !idx_out || !w_out || !dropped)
+    return -1;
+  int32_t* accepted = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  char* taken = (char*)malloc((size_t)E);
+  if (!accepted || !taken) {
+    free(accepted);
+    free(taken);
+    return -1;
+  }
+  *dropped = 0;
+  for (int t = 0; t < T; ++t) {
+    const long p0 = (long)t * k;
+    int kept = 0, ndrop = 0;
+    for (int j = 0; j < k; ++j) { /* the token's experts, in slot order */
+      const int e = idx[p0 + j];
+      idx_out[p0 + j] = -1;
+      w_out[p0 + j] = 0.0f;
+      if (e == -1) continue; /* empty slot */
+      if (e < 0 || e >= E) {
+        free(accepted);
+        free(taken);
+        return -1;
+      }
+      if (accepted[e] < capacity) {
+        accepted[e] += 1;
+        idx_out[p0 + j] = e;
+        w_out[p0 + j] = w[p0 + j];
+        kept += 1;
+      } else {
+        ndrop += 1;
+      }
+    }
+    int need = fallback_min - kept;
+    if (need > ndrop) need = ndrop;
+    if (need < 0) need = 0;
+    /* the least-loaded experts, one at a time: the smallest (accepted, id)
+     * not taken yet, i.e. the first `need` of the experts sorted by load */
+    for (int e = 0; e < E; ++e) taken[e] = 0;
+    int slot = 0;
+    for (int r = 0; r < need; ++r) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || accepted[e] < accepted[best])) best = e;
+      taken[best] = 1;
+      /* the next dropped slot of the token */
+      while (!(idx[p0 + slot] >= 0 && idx_out[p0 + slot] == -1)) ++slot;
+      idx_out[p0 + slot] = best;
+      w_out[p0 + slot] = w[p0 + slot];
+      ++slot;
+    }
+    *dropped += ndrop - need;
+  }
+  free(accepted);
+  free(taken);
+  return 0;
+}
+
 /* One expert MLP per requested row, [MOE-128x8] gate_proj / up_proj / down_proj
  * with the SwiGLU form down(silu(gate x) * up x), no biases:
  *   g_i = sum_h Wg[e,i,h] x[t,h],  u_i = sum_h Wu[e,i,h] x[t,h]

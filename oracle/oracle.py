@@ -58,6 +58,7 @@ def _load():
         lib.orc_capacity.argtypes = [i, i, i, ctypes.c_double]
         lib.orc_dispatch_capacity.argtypes = [i, i, i, i, P, P, P, P, P, P]
         lib.orc_aux.argtypes = [i, i, i, P, P, P, P, P]
+        lib.orc_capacity_fallback.argtypes = [i, i, i, i, i, P, P, P, P, P]
         lib.orc_forward_tokens.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P, P, i,
                                            P, P, P, P]
         for f in (lib.orc_logits, lib.orc_route, lib.orc_dispatch, lib.orc_expert_rows,
@@ -65,7 +66,7 @@ def _load():
                   lib.orc_dispatch_capacity, lib.orc_aux, lib.orc_forward_tokens,
                   lib.orc_route_sel, lib.orc_noisy_logits, lib.orc_z_loss,
                   lib.orc_route_dynamic, lib.orc_dequant_w4, lib.orc_expert_rows_w4,
-                  lib.orc_expert_rows_f64w):
+                  lib.orc_expert_rows_f64w, lib.orc_capacity_fallback):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -192,6 +193,42 @@ def dispatch_capacity(idx: np.ndarray, E: int, cap: int):
     _check(_load().orc_dispatch_capacity(T, E, k, int(cap), _p(idx), _p(counts), _p(offsets),
                                          _p(sp), _p(pp), _p(dropped)), "dispatch_capacity")
     return counts, offsets, sp, pp, int(dropped[0])
+
+
+def capacity_fallback(idx: np.ndarray, w: np.ndarray, E: int, cap: int, fallback_min: int):
+    """Capacity-limited routing with the least-loaded fallback ([T,k] idx with
+    -1 for empty slots, [T,k] float32 weights). Returns (idx_out [T,k] int32,
+    -1 where no expert; w_out [T,k] float32; dropped slots left over)."""
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    io = np.empty((T, k), np.int32)
+    wo = np.empty((T, k), np.float32)
+    dropped = np.zeros(1, np.int32)
+    _check(_load().orc_capacity_fallback(T, E, k, int(cap), int(fallback_min), _p(idx), _p(w),
+                                         _p(io), _p(wo), _p(dropped)), "capacity_fallback")
+    return io, wo, int(dropped[0])
+
+
+def forward_routed(inp: dict, cfg, idx: np.ndarray, w: np.ndarray, tokens=None,
+                   round_h: bool = False) -> np.ndarray:
+    """Block output of the listed tokens for a given routing: idx [n,k]
+    (-1 = no expert in that slot) and weights w [n,k]: out[t] = sum over the
+    slots with an expert of w * MLP_e(x_t). Returns float64 [n,H]."""
+    x = _c(inp["x"])
+    T = x.shape[0]
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    tokens = _c(tokens, np.int32)
+    idx = _c(idx, np.int32)
+    n, k = idx.shape
+    live = idx >= 0
+    tok = np.repeat(tokens, k).reshape(n, k)[live]
+    y = np.zeros((n * k, x.shape[1]), np.float64)
+    if live.any():
+        y[live.ravel()] = expert_rows(x, inp["w_gate"], inp["w_up"], inp["w_down"], tok,
+                                      idx[live], round_h=round_h)
+    return combine(np.asarray(w, np.float64), y, keep=live.astype(np.int8))
 
 
 def expert_rows(x, w_gate, w_up, w_down, tok, ex, round_h: bool = False) -> np.ndarray:

@@ -29,6 +29,9 @@ int orc_capacity(int T, int E, int k, double cf);
 int orc_dispatch_capacity(int T, int E, int k, int capacity, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* dropped);
+int orc_capacity_fallback(int T, int E, int k, int capacity, int fallback_min,
+                          const int32_t* idx, const float* w, int32_t* idx_out, float* w_out,
+                          int32_t* dropped);
 int orc_expert_rows(int H, int I, int dtype, const void* x, const void* wg, const void* wu,
                     const void* wd, int n, const int32_t* tok, const int32_t* ex, int round_h,
                     double* y);
@@ -146,6 +149,27 @@ static void run_block(int dtype, int T, int H, int E, int k, int I) {
   expect(orc_dispatch_capacity(T, E, k, cap, idx, counts, offsets, sorted_pair, pair_pos,
                                &dropped),
          0, "dispatch_capacity");
+  {
+    /* fallback routing, exact-size buffers (with one empty slot) */
+    int32_t* fi = malloc(sizeof(int32_t) * P);
+    int32_t* fo = malloc(sizeof(int32_t) * P);
+    float* fw = malloc(sizeof(float) * P);
+    float* fwo = malloc(sizeof(float) * P);
+    for (size_t i = 0; i < P; ++i) {
+      fi[i] = idx[i];
+      fw[i] = (float)w[i];
+    }
+    fi[P - 1] = -1;
+    int32_t fdrop = 0;
+    expect(orc_capacity_fallback(T, E, k, cap, k, fi, fw, fo, fwo, &fdrop), 0,
+           "capacity_fallback");
+    expect(orc_capacity_fallback(T, E, k, cap, k + 1, fi, fw, fo, fwo, &fdrop), -1,
+           "capacity_fallback fallback_min > k");
+    free(fi);
+    free(fo);
+    free(fw);
+    free(fwo);
+  }
   for (size_t i = 0; i < P; ++i) {
     tok[i] = (int32_t)(i / k);
     ex[i] = idx[i];

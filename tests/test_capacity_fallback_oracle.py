@@ -1,0 +1,135 @@
+"""Pins of the oracle's capacity-limited routing with the least-loaded fallback
+(Qwen3 细粒度专家路由策略全解析, §四: inference routing with expert capacities).
+The oracle walks the tokens in order as the page's loop does; these tests
+check it against worked examples done by hand, against the plain capacity
+dispatch (fallback off), and against a brute-force restatement of the loads
+each token sees (accepted pairs of every expert among the tokens up to it)."""
+import numpy as np
+import pytest
+
+from oracle import oracle
+from sparse_mixture_experts_40_amd.configs import MoEConfig
+from sparse_mixture_experts_40_amd.inputs import make_inputs
+
+
+def test_worked_example_fallback_not_counted():
+    # E = 4, k = 2, capacity 2, fallback to 2 experts per token. By hand:
+    #  t0 [0,1]: both accepted            loads (1,1,0,0)
+    #  t1 [0,1]: both accepted            loads (2,2,0,0)
+    #  t2 [0,2]: 0 full, 2 accepted       loads (2,2,1,0); one short: least
+    #            loaded is 3 (load 0) -> slot 0 gets expert 3, not counted
+    #  t3 [3,0]: 3 accepted (its load is still 0), 0 full; loads (2,2,1,1);
+    #            one short: 2 and 3 tie at 1 -> the lower id, 2, into slot 1
+    #  t4 [1,2]: 1 full, 2 accepted       loads (2,2,2,1); one short: 3
+    idx = np.array([[0, 1], [0, 1], [0, 2], [3, 0], [1, 2]], np.int32)
+    w = np.array([[.6, .4], [.7, .3], [.8, .2], [.55, .45], [.9, .1]], np.float32)
+    io, wo, dropped = oracle.capacity_fallback(idx, w, 4, 2, 2)
+    np.testing.assert_array_equal(io, [[0, 1], [0, 1], [3, 2], [3, 2], [3, 2]])
+    np.testing.assert_array_equal(wo, w)  # every slot keeps its weight
+    assert dropped == 0
+    # fallback to 1 expert: no token is short, the three full slots stay empty
+    io, wo, dropped = oracle.capacity_fallback(idx, w, 4, 2, 1)
+    np.testing.assert_array_equal(io, [[0, 1], [0, 1], [-1, 2], [3, -1], [-1, 2]])
+    np.testing.assert_array_equal(wo, np.where(io >= 0, w, 0))
+    assert dropped == 3
+
+
+def test_worked_example_empty_slots_and_too_few_dropped():
+    # E = 3, k = 3, capacity 1, fallback to 3: t0 takes all three experts;
+    # t1 has an empty slot and two full experts: it lacks 3 but has only 2
+    # dropped slots, which get the least-loaded experts 0 and 1 (all loads
+    # 1, ties by id: the added experts may be the ones that were full)
+    idx = np.array([[0, 1, 2], [1, 0, -1]], np.int32)
+    w = np.array([[.5, .3, .2], [.6, .4, 0]], np.float32)
+    io, wo, dropped = oracle.capacity_fallback(idx, w, 3, 1, 3)
+    np.testing.assert_array_equal(io, [[0, 1, 2], [0, 1, -1]])
+    np.testing.assert_array_equal(wo, w)
+    assert dropped == 0
+
+
+def _random_routing(T, E, k, seed, empty=0.0, skew=1.2):
+    rng = np.random.default_rng(seed)
+    p = np.arange(1, E + 1, dtype=np.float64) ** -skew
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    if empty:
+        idx[rng.random((T, k)) < empty] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    return idx, w
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fallback_off_is_the_plain_capacity_limit(seed):
+    T, E, k, cap = 300, 16, 4, 60
+    idx, w = _random_routing(T, E, k, seed)
+    io, wo, dropped = oracle.capacity_fallback(idx, w, E, cap, 0)
+    _, _, _, pp, d2 = oracle.dispatch_capacity(idx, E, cap)
+    kept = (pp >= 0).reshape(T, k)
+    np.testing.assert_array_equal(io, np.where(kept, idx, -1))
+    np.testing.assert_array_equal(wo, np.where(kept, w, 0))
+    assert dropped == d2 > 0
+
+
+def test_no_drops_is_the_identity():
+    T, E, k = 200, 8, 3
+    idx, w = _random_routing(T, E, k, 7)
+    io, wo, dropped = oracle.capacity_fallback(idx, w, E, T, k)
+    np.testing.assert_array_equal(io, idx)
+    np.testing.assert_array_equal(wo, w)
+    assert dropped == 0
+
+
+@pytest.mark.parametrize("T,E,k,cap,fmin,empty", [
+    (400, 16, 4, 50, 4, 0.0), (400, 16, 4, 50, 2, 0.1), (300, 64, 8, 20, 4, 0.0),
+    (250, 8, 2, 40, 1, 0.0), (500, 32, 6, 30, 6, 0.2)])
+def test_invariants_against_brute_force_loads(T, E, k, cap, fmin, empty):
+    """Kept slots are untouched; a short token gets exactly min(fmin - kept,
+    dropped slots) experts, in its dropped slots in slot order with their
+    weights; they are the smallest (load, id) where the load of e is
+    min(cap, pairs of e among tokens <= t) recounted here from idx alone."""
+    idx, w = _random_routing(T, E, k, T + E + k, empty=empty)
+    io, wo, dropped = oracle.capacity_fallback(idx, w, E, cap, fmin)
+    total_left = 0
+    seen = np.zeros(E, np.int64)  # pairs of each expert among tokens < t
+    refilled_tokens = 0
+    for t in range(T):
+        kept_mask = np.zeros(k, bool)
+        for j in range(k):
+            e = idx[t, j]
+            if e >= 0:
+                kept_mask[j] = seen[e] < cap  # rank in pair order below capacity
+                seen[e] += 1
+        dropped_slots = [j for j in range(k) if idx[t, j] >= 0 and not kept_mask[j]]
+        need = max(0, min(fmin - int(kept_mask.sum()), len(dropped_slots)))
+        for j in range(k):
+            if kept_mask[j]:
+                assert io[t, j] == idx[t, j] and wo[t, j] == w[t, j]
+        load = np.minimum(seen, cap)  # includes token t's own pairs
+        order = sorted(range(E), key=lambda e: (load[e], e))[:need]
+        for r, j in enumerate(dropped_slots):
+            if r < need:
+                assert io[t, j] == order[r] and wo[t, j] == w[t, j], (t, j)
+            else:
+                assert io[t, j] == -1 and wo[t, j] == 0
+        for j in range(k):
+            if idx[t, j] < 0:
+                assert io[t, j] == -1 and wo[t, j] == 0
+        refilled_tokens += need > 0
+        total_left += len(dropped_slots) - need
+    assert dropped == total_left
+    assert refilled_tokens > 0  # the case exercises the fallback
+
+
+def test_forward_routed_equals_forward_tokens_on_the_router_choice():
+    cfg = MoEConfig(name="fb_small", T=24, H=64, E=8, k=2, I=64, norm=True, dtype="f32",
+                    zipf_s=0.0, seed=3)
+    inp = make_inputs(cfg)
+    ref = oracle.forward_tokens(inp, cfg)
+    out = oracle.forward_routed(inp, cfg, ref["idx"], ref["w"])
+    np.testing.assert_allclose(out, ref["out"], rtol=1e-12, atol=1e-12)
+    # a slot with no expert adds nothing: drop slot 1 of every token
+    idx1 = ref["idx"].copy()
+    idx1[:, 1] = -1
+    out1 = oracle.forward_routed(inp, cfg, idx1, ref["w"])
+    only0 = oracle.forward_routed(inp, cfg, ref["idx"][:, :1].copy(), ref["w"][:, :1].copy())
+    np.testing.assert_allclose(out1, only0, rtol=1e-12, atol=1e-12)
