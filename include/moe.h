@@ -137,6 +137,14 @@ typedef struct {
    * (challenge 3: a router z-loss for training stability) names the
    * statistic without a formula; this is the form taken (see moe_z_loss). */
   float* z_loss;
+  /* Least-loaded fallback of the capacity limit, [QWEN3-ROUTE] §四 (at
+   * inference a token left with fewer than 4 accepted experts gets the
+   * least-loaded experts added). 0 = off: dropped slots stay empty. In
+   * [1, top_k], with capacity > 0 (else MOE_ERR_INVALID_ARGUMENT): the routing
+   * is that of moe_capacity_fallback with this minimum, and `dropped` counts
+   * the dropped slots it does not refill. topk_idx / topk_w (outputs of the
+   * layer) stay the router's choice; the statistics count the router's pairs. */
+  int32_t capacity_fallback_min;
 } moe_options;
 
 /* 4-bit group-quantised expert weights, [MOE-128x8] 参数量化与存储优化 (4-bit
@@ -276,6 +284,38 @@ moe_status moe_dispatch_capacity(const moe_config* cfg, const int32_t* topk_idx,
                                  int32_t* expert_offsets, int32_t* sorted_pair,
                                  int32_t* pair_pos, int32_t* dropped, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Capacity limit with the least-loaded fallback, in slot form. [QWEN3-ROUTE]
+ * §四 (inference routing with expert capacities): the tokens are taken in
+ * order; an expert accepts a token while it has accepted fewer than
+ * `capacity` (pair p = t*k + j is kept iff fewer than `capacity` pairs of its
+ * expert have a smaller pair id); a token left with fewer than fallback_min
+ * kept slots gets the least-loaded experts added, and those are not counted as
+ * accepted. The load of expert e for token t is the number of pairs e has
+ * accepted among the tokens 0..t: min(capacity, pairs of e with id < (t+1)*k).
+ * The added experts are those with the smallest (load, id), taken in that
+ * order into the token's dropped slots in slot order; each takes the weight
+ * of its slot. No more are added than the token has dropped slots. An added
+ * expert may already be one of the token's, or full (the page's code excludes
+ * neither); fallback_min = 0 adds none (the plain capacity limit).
+ *   topk_idx [T,k] int32 (-1 = empty slot), topk_w [T,k] fp32: the routing.
+ *   expert_offsets [E+1], sorted_pair [T*k], pair_pos [T*k]: the outputs of
+ *                  moe_dispatch on the same topk_idx (no capacity).
+ *   capacity >= 1; fallback_min in [0, top_k].
+ *   topk_idx_out [T,k] int32 out: the expert of every slot after the limit and
+ *                  the fallback, -1 for a slot with none (dropped and not
+ *                  refilled, or empty); topk_w_out [T,k] fp32 out: its weight
+ *                  (0 where -1). Separate from the inputs.
+ *   dropped        [1] int32 out or NULL: dropped slots not refilled.
+ * Feed topk_idx_out to moe_dispatch (a negative id is an empty slot) and
+ * topk_w_out to moe_combine. Returns MOE_ERR_INVALID_ARGUMENT for a null
+ * pointer (other than dropped), capacity < 1 or fallback_min out of range;
+ * nothing is launched then. No workspace. */
+moe_status moe_capacity_fallback(const moe_config* cfg, const int32_t* topk_idx,
+                                 const float* topk_w, int32_t capacity, int32_t fallback_min,
+                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                 const int32_t* pair_pos, int32_t* topk_idx_out,
+                                 float* topk_w_out, int32_t* dropped, hipStream_t stream);
 
 /* Experts, first half: for every sorted row i of expert e (offsets[e] <= i <
  * offsets[e+1]) with token t = sorted_pair[i] / k:

@@ -25,7 +25,8 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 # public entry points of include/moe.h
 EXPORTS = ("moe_workspace_size", "moe_status_string", "moe_router_topk", "moe_router_topk_ex",
            "moe_dispatch",
-           "moe_capacity", "moe_dispatch_capacity", "moe_expert_gate_up", "moe_expert_down",
+           "moe_capacity", "moe_dispatch_capacity", "moe_capacity_fallback",
+           "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_swiglu", "moe_combine", "moe_aux_stats", "moe_z_loss", "moe_layer_forward",
            "moe_layer_forward_ex", "moe_expert_gate_up_w4", "moe_expert_down_w4",
            "moe_layer_forward_w4", "moe_layer_forward_noalloc", "moe_w4_from_mlx")
@@ -45,7 +46,8 @@ class moe_options(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("dropped", ctypes.c_void_p),
                 ("noise", ctypes.c_void_p), ("w_noise", ctypes.c_void_p),
                 ("select_bias", ctypes.c_void_p), ("dynamic_k_min", ctypes.c_int32),
-                ("k_per_token", ctypes.c_void_p), ("z_loss", ctypes.c_void_p)]
+                ("k_per_token", ctypes.c_void_p), ("z_loss", ctypes.c_void_p),
+                ("capacity_fallback_min", ctypes.c_int32)]
 
 
 class moe_w4_weights(ctypes.Structure):
@@ -81,6 +83,7 @@ def load(path: str = LIB_PATH):
         "moe_router_topk_ex": [C, ctypes.POINTER(moe_options), V, V, V, V, V, V, V, S, V],
         "moe_dispatch": [C, V, V, V, V, V, V, S, V],
         "moe_dispatch_capacity": [C, V, ctypes.c_int32, V, V, V, V, V, V, S, V],
+        "moe_capacity_fallback": [C, V, V, ctypes.c_int32, ctypes.c_int32, V, V, V, V, V, V, V],
         "moe_expert_gate_up": [C, V, V, V, V, V, V, V, S, V],
         "moe_expert_down": [C, V, V, V, V, V, S, V],
         "moe_expert_swiglu": [C, V, V, V, V, V, V, V, V, S, V],
@@ -150,10 +153,12 @@ def router_topk(c: moe_config, x, w_router, logit_bias, logits, topk_idx, topk_w
 
 
 def options(capacity: int = 0, dropped=None, noise=None, w_noise=None, select_bias=None,
-            dynamic_k_min: int = 0, k_per_token=None, z_loss=None) -> moe_options:
+            dynamic_k_min: int = 0, k_per_token=None, z_loss=None,
+            fallback_min: int = 0) -> moe_options:
     """moe_options from tensors (the tensors must outlive the calls)."""
     return moe_options(int(capacity), _ptr(dropped), _ptr(noise), _ptr(w_noise),
-                       _ptr(select_bias), int(dynamic_k_min), _ptr(k_per_token), _ptr(z_loss))
+                       _ptr(select_bias), int(dynamic_k_min), _ptr(k_per_token), _ptr(z_loss),
+                       int(fallback_min))
 
 
 def router_topk_ex(c: moe_config, opts: moe_options | None, x, w_router, logit_bias, logits,
@@ -184,6 +189,15 @@ def dispatch_capacity(c: moe_config, topk_idx, cap: int, counts, offsets, sorted
                                         _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                                         _ptr(dropped), _ptr(ws), ws.numel(), _stream()),
            "moe_dispatch_capacity")
+
+
+def capacity_fallback(c: moe_config, topk_idx, topk_w, cap: int, fallback_min: int, offsets,
+                      sorted_pair, pair_pos, idx_out, w_out, dropped=None):
+    _check(load().moe_capacity_fallback(ctypes.byref(c), _ptr(topk_idx), _ptr(topk_w), int(cap),
+                                        int(fallback_min), _ptr(offsets), _ptr(sorted_pair),
+                                        _ptr(pair_pos), _ptr(idx_out), _ptr(w_out), _ptr(dropped),
+                                        _stream()),
+           "moe_capacity_fallback")
 
 
 def expert_gate_up(c: moe_config, x, sorted_pair, offsets, w_gate, w_up, h, ws=None):
@@ -357,8 +371,10 @@ class MoEBlock:
     whole forward with one library call per step."""
 
     def __init__(self, cfg: MoEConfig, inputs: dict, device="cuda", capacity: int = 0,
-                 noise=None, w_noise=None, select_bias=None, dynamic_k_min: int = 0, w4=None):
-        """capacity > 0: capacity-limited dispatch (see moe_capacity); noise
+                 noise=None, w_noise=None, select_bias=None, dynamic_k_min: int = 0, w4=None,
+                 fallback_min: int = 0):
+        """capacity > 0: capacity-limited dispatch (see moe_capacity), with
+        fallback_min > 0 the least-loaded fallback (moe_capacity_fallback); noise
         [T,E] fp32 + w_noise [E,H]: noisy top-k; select_bias [E] fp32:
         selection-only bias (numpy arrays or tensors); dynamic_k_min > 0:
         entropy-driven k in [dynamic_k_min, k]; w4: 4-bit expert weights
@@ -372,7 +388,8 @@ class MoEBlock:
         self.k_per_token = torch.empty(cfg.T, dtype=torch.int32, device=device)
         variant = capacity or noise is not None or select_bias is not None or dynamic_k_min
         self.opts = options(capacity, self.dropped, self.noise, self.w_noise, self.select_bias,
-                            dynamic_k_min, self.k_per_token) if variant else None
+                            dynamic_k_min, self.k_per_token,
+                            fallback_min=fallback_min) if variant else None
         self.w_router = to_device(inputs["w_router"], device)
         self.w4 = w4_to_device(w4, device) if w4 is not None else None
         self.w4_struct = w4_weights(self.w4) if w4 is not None else None

@@ -216,6 +216,93 @@ __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
   scatter_chunk(P, E, cap, idx, 0, s_h, s_off, s_wc, sorted_pair, pair_pos);
 }
 
+// Least-loaded fallback of a capacity limit ([QWEN3-ROUTE] §四: a token left
+// with fewer than fallback_min accepted experts gets the least-loaded ones
+// added, and those are not counted as accepted). Input: the dropless
+// dispatch of the same routing. Pair p of expert e has rank
+// pair_pos[p] - offsets[e] in its expert and is kept iff that rank is below
+// the capacity. The load of e that token t sees (its accepted pairs among
+// tokens <= t) is min(capacity, pairs of e with an id below (t + 1) k),
+// found by binary search in e's segment of sorted_pair (ascending pair ids),
+// so tokens do not depend on each other. A short token takes the experts with
+// the smallest (load, id), one wave minimum per expert, into its dropped
+// slots in slot order, each with that slot's weight; the other dropped slots
+// and the empty ones get id -1 and weight 0. One wave per token; E <= 256.
+__global__ __launch_bounds__(kThreads) void capacity_fallback_kernel(
+    int T, int E, int k, int cap, int fmin, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ dropped) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform
+  const size_t p = (size_t)t * k + lane;
+  int e = -1;
+  float wv = 0.0f;
+  bool kept = false, drop = false;
+  if (lane < k) {
+    e = idx[p];
+    wv = w[p];
+    if (e >= 0) {  // a pair (a negative id is an empty slot)
+      kept = pair_pos[p] - offsets[clamp_expert(e, E)] < cap;
+      drop = !kept;
+    }
+  }
+  const unsigned long long dm = __ballot(drop);
+  const int nkept = __popcll(__ballot(kept)), ndrop = __popcll(dm);
+  int need = fmin - nkept;
+  need = need > ndrop ? ndrop : (need < 0 ? 0 : need);
+  int out_e = kept ? e : -1;
+  float out_w = kept ? wv : 0.0f;
+  if (need > 0) {  // wave-uniform
+    const int lim = (t + 1) * k;  // pair ids of the tokens up to t
+    unsigned long long key[4];    // (load, expert) of experts lane + 64 i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane + 64 * i;
+      key[i] = ~0ull;
+      if (ee < E) {
+        const int base = offsets[ee];
+        int lo = base, hi = offsets[ee + 1];
+        while (lo < hi) {  // first entry with a pair id >= lim
+          const int mid = (lo + hi) >> 1;
+          if (sorted_pair[mid] < lim) lo = mid + 1; else hi = mid;
+        }
+        const int load = lo - base < cap ? lo - base : cap;
+        key[i] = ((unsigned long long)(unsigned)load << 32) | (unsigned)ee;
+      }
+    }
+    // pick r goes to the dropped slot of rank r (slot order)
+    const int rank = __popcll(dm & ((1ull << lane) - 1ull));
+    for (int r = 0; r < need; ++r) {
+      unsigned long long m = key[0] < key[1] ? key[0] : key[1];
+      const unsigned long long m2 = key[2] < key[3] ? key[2] : key[3];
+      m = m2 < m ? m2 : m;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(m, off);
+        m = o < m ? o : m;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key[i] == m) key[i] = ~0ull;
+      if (drop && rank == r) {
+        out_e = (int)(unsigned)(m & 0xFFFFFFFFull);
+        out_w = wv;
+      }
+    }
+  }
+  if (lane < k) {
+    idx_out[p] = out_e;
+    w_out[p] = out_w;
+  }
+  if (dropped && lane == 0 && ndrop > need) atomicAdd(dropped, ndrop - need);  // exact
+}
+
+__global__ void zero_count_kernel(int32_t* __restrict__ n) {
+  if (threadIdx.x == 0) n[0] = 0;
+}
+
 }  // namespace
 
 int dispatch_num_chunks(const moe_config& c) {
@@ -256,6 +343,19 @@ hipError_t launch_dispatch_aux(const moe_config& c, const int32_t* topk_idx, int
   dispatch_single_kernel<<<2, kThreads, 0, s>>>(c.num_tokens * c.top_k, c.num_experts, capacity,
                                                 topk_idx, counts, offsets, dropped, 1,
                                                 sorted_pair, pair_pos, 1, aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_capacity_fallback(const moe_config& c, const int32_t* topk_idx,
+                                    const float* topk_w, int capacity, int fallback_min,
+                                    const int32_t* offsets, const int32_t* sorted_pair,
+                                    const int32_t* pair_pos, int32_t* idx_out, float* w_out,
+                                    int32_t* dropped, hipStream_t s) {
+  if (dropped) zero_count_kernel<<<1, 64, 0, s>>>(dropped);
+  const int T = c.num_tokens, per = kThreads / 64;
+  capacity_fallback_kernel<<<(T + per - 1) / per, kThreads, 0, s>>>(
+      T, c.num_experts, c.top_k, capacity, fallback_min, topk_idx, topk_w, offsets, sorted_pair,
+      pair_pos, idx_out, w_out, dropped);
   return hipGetLastError();
 }
 

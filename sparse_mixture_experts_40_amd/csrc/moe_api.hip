@@ -110,6 +110,9 @@ struct Layout {
   float* zpart;   // per router block z-loss sums
   void* h;
   void* y;
+  int32_t* fb_idx;    // routing after the least-loaded fallback [T, k]
+  float* fb_w;        // its weights [T, k]
+  int32_t* fb_counts; // rows per expert of that routing [E]
   size_t dispatch_end, aux_end, router_end, layer_end;
 };
 
@@ -139,6 +142,9 @@ Layout carve(const moe_config& c, void* ws) {
   // y_sorted: fp32 rows, or (bf16 layers) scaled fp16 rows in the first half
   // and their int8 chunk exponents after them
   L.y = cv.take<float>(P * c.hidden);
+  L.fb_idx = cv.take<int32_t>(P);
+  L.fb_w = cv.take<float>(P);
+  L.fb_counts = cv.take<int32_t>(E);
   L.layer_end = cv.off;
   return L;
 }
@@ -178,6 +184,9 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   const moe_options none{};
   const moe_options& o = opt ? *opt : none;
   if (o.capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (o.capacity_fallback_min < 0 || o.capacity_fallback_min > cfg->top_k ||
+      (o.capacity_fallback_min > 0 && o.capacity == 0))
+    return MOE_ERR_INVALID_ARGUMENT;
   st = check_router_options(*cfg, o);
   if (st != MOE_OK) return st;
   const Layout L = carve(*cfg, workspace);
@@ -216,19 +225,36 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
     router_blocks = router_num_blocks(c, false);
   }
   if (st != MOE_OK) return st;
+  // with the least-loaded fallback the first dispatch is dropless (it gives
+  // the ranks and loads the fallback reads); the routing it makes is then
+  // dispatched again
+  const bool fallback = o.capacity_fallback_min > 0;
+  const int cap1 = fallback ? 0 : o.capacity;
+  int32_t* drop1 = fallback ? nullptr : o.dropped;
   // with few router blocks and one dispatch chunk (decode batches) the
   // statistics come out of the dispatch block itself
   bool aux_done = false;
   if ((want_aux || ao.z_loss) && aux_small_fits(c, router_blocks)) {
     st = launched(launch_dispatch_aux(
-        c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist, L.base, o.capacity,
-        o.dropped, aux_small_args(c, L.partials, router_blocks, ao, ex.zpart, router_blocks),
-        &aux_done, stream));
+        c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist, L.base, cap1, drop1,
+        aux_small_args(c, L.partials, router_blocks, ao, ex.zpart, router_blocks), &aux_done,
+        stream));
   } else {
     st = launched(launch_dispatch(c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist,
-                                  L.base, true, o.capacity, o.dropped, stream));
+                                  L.base, true, cap1, drop1, stream));
   }
   if (st != MOE_OK) return st;
+  const float* wc = w;  // weights of the combine
+  if (fallback) {
+    st = launched(launch_capacity_fallback(c, idx, w, o.capacity, o.capacity_fallback_min,
+                                           L.offsets, L.sorted_pair, L.pair_pos, L.fb_idx,
+                                           L.fb_w, o.dropped, stream));
+    if (st != MOE_OK) return st;
+    st = launched(launch_dispatch(c, L.fb_idx, L.fb_counts, L.offsets, L.sorted_pair, L.pair_pos,
+                                  L.hist, L.base, true, 0, nullptr, stream));
+    if (st != MOE_OK) return st;
+    wc = L.fb_w;
+  }
   // bf16 layers keep y_sorted in scaled fp16 where the tiled down kernel
   // writes it (half the bytes between the down GEMM and the combine): the
   // rows in the first half of L.y, their chunk exponents after them
@@ -246,7 +272,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
     st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream, y_exp, &y_half));
   }
   if (st != MOE_OK) return st;
-  st = launched(launch_combine(c, L.y, L.pair_pos, w, out, stream, y_half ? y_exp : nullptr));
+  st = launched(launch_combine(c, L.y, L.pair_pos, wc, out, stream, y_half ? y_exp : nullptr));
   if (st != MOE_OK) return st;
   if ((want_aux || ao.z_loss) && !aux_done)
     st = launched(launch_aux(c, L.counts, L.partials, router_blocks, L.fp, ao, stream, ex.zpart,
@@ -360,6 +386,21 @@ moe_status moe_dispatch_capacity(const moe_config* cfg, const int32_t* topk_idx,
   if (!workspace || workspace_bytes < L.dispatch_end) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return launched(launch_dispatch(*cfg, topk_idx, expert_counts, expert_offsets, sorted_pair,
                                   pair_pos, L.hist, L.base, true, capacity, dropped, stream));
+}
+
+moe_status moe_capacity_fallback(const moe_config* cfg, const int32_t* topk_idx,
+                                 const float* topk_w, int32_t capacity, int32_t fallback_min,
+                                 const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                 const int32_t* pair_pos, int32_t* topk_idx_out,
+                                 float* topk_w_out, int32_t* dropped, hipStream_t stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !topk_w || !expert_offsets || !sorted_pair || !pair_pos || !topk_idx_out ||
+      !topk_w_out || capacity < 1 || fallback_min < 0 || fallback_min > cfg->top_k)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return launched(launch_capacity_fallback(*cfg, topk_idx, topk_w, capacity, fallback_min,
+                                           expert_offsets, sorted_pair, pair_pos, topk_idx_out,
+                                           topk_w_out, dropped, stream));
 }
 
 moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_t* sorted_pair,

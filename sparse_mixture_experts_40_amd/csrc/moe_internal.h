@@ -258,6 +258,16 @@ hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t
                            int32_t* hist, int32_t* rank0, bool scatter, int capacity,
                            int32_t* dropped, hipStream_t s);
 
+// Least-loaded fallback of a capacity limit, from the dropless dispatch
+// (offsets, sorted_pair, pair_pos) of topk_idx: the routing in slot form
+// (idx_out -1 where no expert) and the dropped slots left over in *dropped
+// (zeroed here first when non-null).
+hipError_t launch_capacity_fallback(const moe_config& c, const int32_t* topk_idx,
+                                    const float* topk_w, int capacity, int fallback_min,
+                                    const int32_t* offsets, const int32_t* sorted_pair,
+                                    const int32_t* pair_pos, int32_t* idx_out, float* w_out,
+                                    int32_t* dropped, hipStream_t s);
+
 // Expert GEMMs.
 hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,
                           const int32_t* offsets, const void* w_gate, const void* w_up, void* h,

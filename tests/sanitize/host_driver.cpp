@@ -82,6 +82,23 @@ void entry_point_checks(const moe_config& c) {
   expect(moe_layer_forward_ex(&c, &o, d, d, nullptr, d, d, d, d, nullptr, nullptr, nullptr,
                               no_aux, d, ws, nullptr),
          1, "layer_ex negative capacity");
+  std::memset(&o, 0, sizeof o);
+  o.capacity_fallback_min = 1;  // fallback without a capacity
+  expect(moe_layer_forward_ex(&c, &o, d, d, nullptr, d, d, d, d, nullptr, nullptr, nullptr,
+                              no_aux, d, ws, nullptr),
+         1, "layer_ex fallback without capacity");
+  o.capacity = 4;
+  o.capacity_fallback_min = c.top_k + 1;
+  expect(moe_layer_forward_ex(&c, &o, d, d, nullptr, d, d, d, d, nullptr, nullptr, nullptr,
+                              no_aux, d, ws, nullptr),
+         1, "layer_ex fallback_min > k");
+  expect(moe_capacity_fallback(&c, di, df, 0, 1, di, di, di, dio, dfo, nullptr, nullptr), 1,
+         "capacity_fallback capacity 0");
+  expect(moe_capacity_fallback(&c, di, df, 4, c.top_k + 1, di, di, di, dio, dfo, nullptr,
+                               nullptr),
+         1, "capacity_fallback fallback_min > k");
+  expect(moe_capacity_fallback(&c, di, df, 4, 1, di, nullptr, di, dio, dfo, nullptr, nullptr), 1,
+         "capacity_fallback NULL sorted_pair");
 
   expect(moe_dispatch(&c, nullptr, dio, dio, dio, dio, d, ws, nullptr), 1, "dispatch NULL idx");
   expect(moe_dispatch(&c, di, dio, dio, dio, dio, d, 1, nullptr), 3, "dispatch small ws");

@@ -111,6 +111,32 @@ def test_capacity_helper_and_validation(lib, orc):
     assert r == 1
 
 
+def test_capacity_fallback_validation(lib):
+    """moe_capacity_fallback and the fallback option reject bad arguments
+    with MOE_ERR_INVALID_ARGUMENT before any launch."""
+    c = binding.make_config(WORKLOADS["tiny_f32"])  # k = 2
+    d = ctypes.c_void_p(16)
+    cf = lib.moe_capacity_fallback
+    assert cf(ctypes.byref(c), d, d, 0, 1, d, d, d, d, d, None, None) == 1     # capacity < 1
+    assert cf(ctypes.byref(c), d, d, 4, -1, d, d, d, d, d, None, None) == 1    # fallback_min < 0
+    assert cf(ctypes.byref(c), d, d, 4, 3, d, d, d, d, d, None, None) == 1     # > top_k
+    for i in range(7):  # every array but `dropped` is required
+        args = [d] * 7
+        args[i] = None
+        a_idx, a_w, a_off, a_sp, a_pp, a_io, a_wo = args
+        assert cf(ctypes.byref(c), a_idx, a_w, 4, 1, a_off, a_sp, a_pp, a_io, a_wo, None,
+                  None) == 1
+    bad = binding.moe_config(0, 128, 8, 2, 256, 1, 0)
+    assert cf(ctypes.byref(bad), d, d, 4, 1, d, d, d, d, d, None, None) == 1
+    ws = ctypes.c_void_p(256)
+    big = 1 << 30
+    for cap, fmin in ((0, 1), (4, -1), (4, 3)):  # no capacity, out of [0, top_k]
+        opt = binding.options(cap, fallback_min=fmin)
+        r = lib.moe_layer_forward_ex(ctypes.byref(c), ctypes.byref(opt), d, d, None, d, d, d, d,
+                                     None, None, None, binding.moe_aux_out(), ws, big, None)
+        assert r == 1, (cap, fmin)
+
+
 def test_w4_validation(lib):
     d = ctypes.c_void_p(16)
     w4 = binding.moe_w4_weights(16, 16, 16, 16, 16, 16)
