@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--decode-workload NAME|none] [--decode-steps N]
                     [--capacity-factor CF]   # capacity-limited dispatch, C = ceil(T*k*CF/E)
+                    [--capacity-fallback-min M]  # with CF: least-loaded fallback to M slots
                     [--router noise|bias|noise+bias]   # router variants (seeded inputs)
                     [--dynamic-k-min KMIN]   # entropy-driven k in [KMIN, k]
                     [--w4]                   # 4-bit group-quantised expert weights
@@ -296,7 +297,7 @@ def time_per_call(torch, stream, fn, reps):
 
 
 def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="plain",
-            dynamic_k_min=0):
+            dynamic_k_min=0, fallback_min=0):
     """Everything the JSON line reports about one workload, except the CPU
     baseline: the timed steps, the dominant kernel's roofline, the stages,
     the clock, and for weight-streaming workloads the MALL-scrubbed variants.
@@ -314,7 +315,7 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
                            noise=var.get("noise") if "noise" in router else None,
                            w_noise=var.get("w_noise") if "noise" in router else None,
                            select_bias=var.get("select_bias") if "bias" in router else None,
-                           dynamic_k_min=dynamic_k_min, w4=w4in)
+                           dynamic_k_min=dynamic_k_min, w4=w4in, fallback_min=fallback_min)
     x = binding.to_device(inp["x"])
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
@@ -379,11 +380,23 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
     pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     h = torch.empty(T * k, cfg.I, dtype=binding.TORCH_DTYPE[cfg.dtype], device="cuda")
     # the same router (variants included) as the timed block
+    # the routing after a capacity limit with the least-loaded fallback
+    idx2 = torch.empty(T, k, dtype=torch.int32, device="cuda") if fallback_min else None
+    w2 = torch.empty(T, k, dtype=torch.float32, device="cuda") if fallback_min else None
+    counts2 = torch.empty(E, dtype=torch.int32, device="cuda")
     binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias, None, idx, wts, blk.ws)
-    if cap:
-        binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
-    else:
-        binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+
+    def disp():
+        if cap and fallback_min:  # dropless dispatch, the fallback routing, its dispatch
+            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+            binding.capacity_fallback(c, idx, wts, cap, fallback_min, offsets, sp, pp, idx2, w2)
+            binding.dispatch(c, idx2, counts2, offsets, sp, pp, blk.ws)
+        elif cap:
+            binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
+        else:
+            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+
+    disp()
 
     def gate_up():
         if w4:
@@ -416,18 +429,14 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
         else:
             binding.expert_down(c, h, offsets, blk.w_down, y)
 
-    def disp():
-        if cap:
-            binding.dispatch_capacity(c, idx, cap, counts, offsets, sp, pp, blk.ws)
-        else:
-            binding.dispatch(c, idx, counts, offsets, sp, pp, blk.ws)
+    wc = w2 if fallback_min else wts  # the combine's weights
     stage_fns = [
         ("router", lambda: binding.router_topk_ex(c, blk.opts, x, blk.w_router, blk.logit_bias,
                                                   None, idx, wts, blk.ws)),
         ("dispatch", disp),
         ("gate_up", gate_up),
         ("down", down),
-        ("combine", lambda: binding.combine(c, y, pp, wts, out)),
+        ("combine", lambda: binding.combine(c, y, pp, wc, out)),
         ("aux_stats_from_logits", lambda: binding.aux_stats(c, lg, idx, blk.ws, counts=counts,
                                                             f=blk.f, P=blk.P, aux=blk.aux)),
     ]
@@ -435,7 +444,8 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
               for n, fn in stage_fns}
     disp()  # counts / offsets of the router's selection again
     torch.cuda.synchronize()
-    cnt = counts.cpu().numpy()
+    # rows per expert of the routing the experts ran (with the fallback, its own)
+    cnt = (counts2 if cap and fallback_min else counts).cpu().numpy()
     rows = int(offsets[E].item())  # kept pairs (all of them without a capacity)
     gflops, gbytes, touched = gate_up_algorithmic(cfg, cnt, rows, w4)
     lflops, lbytes = layer_algorithmic(cfg, cnt, rows, w4)
@@ -473,6 +483,8 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
     if cap:
         config.update({"capacity_factor": cap_factor, "capacity": cap,
                        "dropped_pairs": int(blk.dropped.item()), "kept_pairs": rows})
+        if fallback_min:
+            config["capacity_fallback_min"] = fallback_min
     if router != "plain":
         config["router"] = router
     if w4:
@@ -536,6 +548,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="> 0: capacity-limited dispatch with C = ceil(T*k*CF/E)")
+    ap.add_argument("--capacity-fallback-min", type=int, default=0,
+                    help="with --capacity-factor: a token keeping fewer than this many of its "
+                         "slots gets the least-loaded experts in its dropped slots")
     ap.add_argument("--router", default="plain", choices=["plain", "noise", "bias", "noise+bias"],
                     help="router variant: noisy top-k and/or selection-only bias")
     ap.add_argument("--dynamic-k-min", type=int, default=0,
@@ -581,6 +596,7 @@ def main():
     torch.cuda.init()
     rep, inp, w4in = measure(torch, binding, cfg, args, args.steps, w4=args.w4,
                              cap_factor=args.capacity_factor, router=args.router,
+                             fallback_min=args.capacity_fallback_min,
                              dynamic_k_min=args.dynamic_k_min)
     if args.layer_only:
         print(json.dumps({"layer_only": True, "workload": cfg.name, "steps": args.steps,
