@@ -73,10 +73,10 @@ FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("71793fbe95c36eb3431797b799752da2d3aa49795ded86c2f31a444f12d70d83",
-                        3959927.0, 393960.9),
-    "decode128_bf16": ("71793fbe95c36eb3431797b799752da2d3aa49795ded86c2f31a444f12d70d83",
-                       542859.2, 1550.3),
+    "prefill128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
+                        4195094.7, 394202.4),
+    "decode128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
+                       542847.9, 1537.1),
 }
 
 
