@@ -211,10 +211,11 @@ def capacity_fallback(idx: np.ndarray, w: np.ndarray, E: int, cap: int, fallback
 
 
 def forward_routed(inp: dict, cfg, idx: np.ndarray, w: np.ndarray, tokens=None,
-                   round_h: bool = False) -> np.ndarray:
+                   round_h: bool = False, w4: dict | None = None) -> np.ndarray:
     """Block output of the listed tokens for a given routing: idx [n,k]
     (-1 = no expert in that slot) and weights w [n,k]: out[t] = sum over the
-    slots with an expert of w * MLP_e(x_t). Returns float64 [n,H]."""
+    slots with an expert of w * MLP_e(x_t), with the 4-bit experts when w4 is
+    given (dequantised element by element). Returns float64 [n,H]."""
     x = _c(inp["x"])
     T = x.shape[0]
     if tokens is None:
@@ -225,7 +226,9 @@ def forward_routed(inp: dict, cfg, idx: np.ndarray, w: np.ndarray, tokens=None,
     live = idx >= 0
     tok = np.repeat(tokens, k).reshape(n, k)[live]
     y = np.zeros((n * k, x.shape[1]), np.float64)
-    if live.any():
+    if live.any() and w4 is not None:
+        y[live.ravel()] = expert_rows_w4(x, w4, tok, idx[live], round_h=round_h)
+    elif live.any():
         y[live.ravel()] = expert_rows(x, inp["w_gate"], inp["w_up"], inp["w_down"], tok,
                                       idx[live], round_h=round_h)
     return combine(np.asarray(w, np.float64), y, keep=live.astype(np.int8))

@@ -69,10 +69,10 @@ def test_capacity_fallback_bitexact(orc, T, E, k, cf, fmin, empty):
         assert total_refilled > 0  # the case exercises the fallback
 
 
-def check_fallback_block(orc, cfg, inp, cf, fmin, tokens, dynamic_k_min=0):
+def check_fallback_block(orc, cfg, inp, cf, fmin, tokens, dynamic_k_min=0, w4=None):
     cap = orc.capacity(cfg.T, cfg.E, cfg.k, cf)
     blk = binding.MoEBlock(cfg, inp, capacity=cap, fallback_min=fmin,
-                           dynamic_k_min=dynamic_k_min)
+                           dynamic_k_min=dynamic_k_min, w4=w4)
     blk.forward(dev(inp["x"]))
     torch.cuda.synchronize()
     g_idx, g_w = host(blk.topk_idx), host(blk.topk_w)
@@ -82,7 +82,10 @@ def check_fallback_block(orc, cfg, inp, cf, fmin, tokens, dynamic_k_min=0):
         o_idx, _, _ = orc.route(lg, cfg.k, cfg.norm)
         for t in np.flatnonzero((g_idx != o_idx).any(1)):
             check_selection_row(lg[t], g_idx[t], o_idx[t], cfg.k, t)
-        r = orc.forward_tokens(inp, cfg, tokens=tokens, forced_idx=g_idx[tokens])
+        if w4 is None:
+            r = orc.forward_tokens(inp, cfg, tokens=tokens, forced_idx=g_idx[tokens])
+        else:
+            r = orc.forward_w4(inp, w4, cfg, tokens=tokens, forced_idx=g_idx[tokens])
         np.testing.assert_allclose(g_w[tokens], r["w"], rtol=0, atol=1e-5)
     # the routing the block must have used: the oracle's fallback applied to
     # the GPU's router choice (so that a near tie cannot move later loads)
@@ -92,7 +95,7 @@ def check_fallback_block(orc, cfg, inp, cf, fmin, tokens, dynamic_k_min=0):
     # statistics count the router's pairs, before the limit
     live = g_idx[g_idx >= 0]
     assert (host(blk.counts) == np.bincount(live, minlength=cfg.E)).all()
-    ref = orc.forward_routed(inp, cfg, io[tokens], wo[tokens], tokens=tokens)
+    ref = orc.forward_routed(inp, cfg, io[tokens], wo[tokens], tokens=tokens, w4=w4)
     mx, _ = check_output(host(blk.out)[tokens], ref, cfg.dtype)
     _, _, _, _, plain_drop = orc.dispatch_capacity(g_idx, cfg.E, cap)
     print(f"{cfg.name} cf={cf} cap={cap} fallback_min={fmin}: dropped by the limit "
@@ -128,6 +131,17 @@ def test_fallback_with_dynamic_k(orc):
     inp = make_inputs(cfg, seed=5)
     plain_drop, left = check_fallback_block(orc, cfg, inp, 0.5, 4,
                                             np.arange(cfg.T, dtype=np.int32), dynamic_k_min=4)
+    assert plain_drop > left
+
+
+def test_fallback_with_w4_experts(orc):
+    from sparse_mixture_experts_40_amd.inputs import make_w4_inputs
+    cfg = MoEConfig("w4_fb", T=64, H=512, E=128, k=8, I=512, norm=True, dtype="bf16",
+                    zipf_s=1.2)
+    inp = make_inputs(cfg, seed=0, weights=False)
+    w4 = make_w4_inputs(cfg, seed=0)
+    plain_drop, left = check_fallback_block(orc, cfg, inp, 1.0, 4,
+                                            np.arange(cfg.T, dtype=np.int32), w4=w4)
     assert plain_drop > left
 
 
