@@ -8,6 +8,8 @@
                     [--dynamic-k-min KMIN]   # entropy-driven k in [KMIN, k]
                     [--w4]                   # 4-bit group-quantised expert weights
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
+    python bench.py ... --rocprof stats|traffic|mops [--rocprof-dir D]
+                                           # the same command under rocprofv3, + summary.md
 
 A step is one moe_layer_forward (router, dispatch, gate/up GEMM, down GEMM,
 combine, load-balance statistics) over one batch of seeded synthetic input that
@@ -58,13 +60,13 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 # HBM traffic of the gate/up kernel per launch, from rocprofv3 --pmc FETCH_SIZE
-# and WRITE_SIZE passes over the layer's own steps (bench.py --layer-only, 3
-# timed steps after 1 warm-up; KiB per dispatch, averaged over the timed ones),
-# scaled by what the same counters read for a plain 1 GiB device copy (bench.py
-# --copy-calibration): FETCH_SIZE reported 524304.8 KiB for 1 GiB read (x2.0),
-# WRITE_SIZE 1048576 KiB for 1 GiB written (x1.0). Valid only for the sources
-# they were taken on (sha256 below: the kernel, its dispatch input order and
-# the build flags); otherwise traffic is null.
+# and WRITE_SIZE passes over the layer's own steps (bench.py --workload W
+# --steps 3 --warmup 1 --rocprof traffic; KiB per dispatch, averaged over the
+# timed steps), scaled by what the same counters read for a plain 1 GiB device
+# copy (bench.py --copy-calibration): FETCH_SIZE reported 524304.8 KiB for
+# 1 GiB read (x2.0), WRITE_SIZE 1048576 KiB for 1 GiB written (x1.0). Valid only
+# for the sources they were taken on (sha256 below: the kernel, its dispatch
+# input order and the build flags); otherwise traffic is null.
 TRAFFIC_SOURCES = ("sparse_mixture_experts_40_amd/csrc/expert_gemm.hip",
                    "sparse_mixture_experts_40_amd/csrc/moe_internal.h",
                    "sparse_mixture_experts_40_amd/csrc/dispatch.hip",
@@ -74,9 +76,9 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
     "prefill128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
-                        4195094.7, 394202.4),
+                        4666597.3, 394304.4),
     "decode128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
-                       542847.9, 1537.1),
+                       542848.0, 1537.8),
 }
 
 
@@ -533,6 +535,172 @@ def decode_summary(rep):
             "gpu_clock": rep["gpu_clock"]}
 
 
+# ---- --rocprof: this command under rocprofv3, with a summary --------------
+#
+# The profiler runs bench.py again as a child process (the parent touches no
+# GPU), and the summary tables are written from its CSV output, so every
+# profile summary comes from committed code and names the commands behind it.
+
+ROCPROF_PMC = {  # counter passes of each mode (one pass per inner list)
+    "traffic": [["FETCH_SIZE"], ["WRITE_SIZE"]],
+    "mops": [["SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE"]],
+}
+
+
+def rocprof_child_args(argv):
+    """argv without the --rocprof and --rocprof-dir options."""
+    out, skip = [], False
+    for a in argv:
+        if skip:
+            skip = False
+        elif a in ("--rocprof", "--rocprof-dir"):
+            skip = True
+        elif not a.startswith(("--rocprof=", "--rocprof-dir=")):
+            out.append(a)
+    return out
+
+
+def short_kernel_name(name: str) -> str:
+    """Kernel name without the namespace and the argument list."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("moe::(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def stats_table(path: str):
+    """Markdown rows of a rocprofv3 kernel_stats.csv (durations in us)."""
+    import csv
+    out = ["| kernel | calls | average us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(path)):
+        out.append(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return out
+
+
+def counter_per_kernel(path: str, counter: str, skip_first: bool):
+    """Values of one counter per kernel, in dispatch order; with skip_first the
+    first dispatch of each kernel (the warm-up step) is left out when there
+    are more."""
+    import csv
+    acc = {}
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            acc.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(
+                float(r["Counter_Value"]))
+    if skip_first:
+        acc = {k: (v[1:] if len(v) > 1 else v) for k, v in acc.items()}
+    return acc
+
+
+def rocprof(mode: str, child: list, outdir: str, timeout_s: int = 240) -> int:
+    """Runs `bench.py <child>` under rocprofv3 (mode stats: kernel trace and
+    statistics; traffic: FETCH_SIZE and WRITE_SIZE passes over --layer-only
+    steps plus the same counters on the 1 GiB copy calibration; mops: the
+    bf16 MFMA ops counter over --layer-only steps) and writes
+    <outdir>/summary.md. Returns 0, or the failing pass's status."""
+    import subprocess
+    os.makedirs(outdir, exist_ok=True)
+    env = {**os.environ, "TMPDIR": os.environ.get("TMPDIR", "/tmp")}
+    py = [sys.executable, os.path.join(ROOT, "bench.py")]
+    layer = child + ([] if "--layer-only" in child else ["--layer-only"])
+    passes = []  # (directory name, command, csv file)
+    if mode == "stats":
+        passes.append(("stats", ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv",
+                                 "-d", f"{outdir}/stats", "-o", "run", "--", *py, *child],
+                       "run_kernel_stats.csv"))
+    else:
+        runs = [(cs, layer, cs[0]) for cs in ROCPROF_PMC[mode]]
+        if mode == "traffic":
+            runs += [([c], ["--copy-calibration"], f"copy-{c}") for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        for cs, args_, name in runs:
+            passes.append((name, ["timeout", "-s", "KILL", str(timeout_s), "rocprofv3", "--pmc", *cs,
+                                  "--output-format", "csv", "-d", f"{outdir}/{name}", "-o", "run",
+                                  "--", *py, *args_], "run_counter_collection.csv"))
+    for name, cmd, csvname in passes:
+        log(f"rocprof pass {name}: {' '.join(cmd)}")
+        r = subprocess.run(cmd, cwd=ROOT, env=env)
+        # rocprofv3 itself may exit non-zero after a complete run: the CSV decides
+        if not os.path.exists(os.path.join(outdir, name, csvname)):
+            log(f"rocprof pass {name} left no {csvname} (status {r.returncode})")
+            return r.returncode or 1
+    path = rocprof_summary(mode, child, outdir, [cmd for _, cmd, _ in passes])
+    print(json.dumps({"rocprof": mode, "summary": path}), flush=True)
+    return 0
+
+
+def rocprof_summary(mode: str, child: list, outdir: str, commands: list) -> str:
+    """Writes <outdir>/summary.md from the CSV output of the passes of
+    rocprof() (`commands`: their command lines) and returns its path."""
+    layer = child + ([] if "--layer-only" in child else ["--layer-only"])
+
+    def shown(cmd):
+        return " ".join("python3" if c == sys.executable else
+                        (os.path.relpath(c, ROOT) if c.startswith(ROOT) else c) for c in cmd)
+
+    head = ["Command (repo root, one MI355X):", "",
+            f"    python3 bench.py {' '.join(child)} --rocprof {mode} --rocprof-dir {outdir}", "",
+            "which runs:", ""] + [f"    {shown(cmd)}" for cmd in commands] + [""]
+    if mode == "stats":
+        lines = [f"# rocprofv3 kernel statistics: bench.py {' '.join(child)}", "", *head,
+                 "Durations in microseconds; the grouped GEMM template arguments are <GATEUP, BM, "
+                 "BK, stages, waves, blocks per CU, non-temporal weights>.", "",
+                 *stats_table(f"{outdir}/stats/run_kernel_stats.csv")]
+    elif mode == "traffic":
+        fe = counter_per_kernel(f"{outdir}/FETCH_SIZE/run_counter_collection.csv", "FETCH_SIZE", True)
+        wr = counter_per_kernel(f"{outdir}/WRITE_SIZE/run_counter_collection.csv", "WRITE_SIZE", True)
+        cf = counter_per_kernel(f"{outdir}/copy-FETCH_SIZE/run_counter_collection.csv", "FETCH_SIZE",
+                                False)
+        cw = counter_per_kernel(f"{outdir}/copy-WRITE_SIZE/run_counter_collection.csv", "WRITE_SIZE",
+                                False)
+        ck = [k for k in cf if "copyBuffer" in k][0]
+        cfa, cwa = float(np.mean(cf[ck])), float(np.mean(cw[ck]))
+        fs, ws = 1048576.0 / cfa, 1048576.0 / cwa
+        lines = [f"# HBM traffic per kernel launch: bench.py {' '.join(layer)}", "", *head,
+                 "One counter per pass, over the layer's own steps (`--layer-only`); values per "
+                 "launch are the mean over the timed steps (the warm-up step's dispatches are left "
+                 "out), scaled by what the same counters read for a plain copy of 1 GiB:", "",
+                 "| copy kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|",
+                 f"| `{ck}` (1 GiB read, 1 GiB written) | {cfa:.1f} | {cwa:.1f} |", "",
+                 f"Scale factors: read bytes = FETCH_SIZE x {fs:.4f}; written bytes = "
+                 f"WRITE_SIZE x {ws:.4f}.", "",
+                 "| kernel | launches averaged | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB "
+                 "(scaled) | HBM written MB (scaled) |", "|---|---|---|---|---|---|"]
+        for k, v in fe.items():
+            if "at::native" in k or "rocclr" in k:
+                continue
+            f, w = float(np.mean(v)), float(np.mean(wr.get(k, [0.0])))
+            lines.append(f"| `{k}` | {len(v)} | {f:.1f} | {w:.1f} | {f * 1024 * fs / 1e6:.1f} | "
+                         f"{w * 1024 * ws / 1e6:.1f} |")
+        lines += ["", f"Sources sha256 (the stamp of measured traffic): {kernel_sources_sha256()}"]
+    else:
+        mo = counter_per_kernel(f"{outdir}/{ROCPROF_PMC['mops'][0][0]}/run_counter_collection.csv",
+                                "SQ_INSTS_VALU_MFMA_MOPS_BF16", True)
+        lines = [f"# bf16 MFMA work per kernel launch: bench.py {' '.join(layer)}", "", *head,
+                 "Executed FLOP per launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (mean over the "
+                 "timed steps; the warm-up step's dispatches are left out).", "",
+                 "| kernel | launches averaged | MOPS per launch | executed TFLOP per launch |",
+                 "|---|---|---|---|"]
+        for k, v in mo.items():
+            m = float(np.mean(v))
+            if m > 0:
+                lines.append(f"| `{k}` | {len(v)} | {m:.6g} | {m * 512 / 1e12:.4f} |")
+    path = os.path.join(outdir, "summary.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,6 +728,12 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="profiling: run only the warm-up and the timed layer steps, print "
                          "their time and exit (no kernel legs, stages or CPU baseline)")
+    ap.add_argument("--rocprof", choices=["stats", "traffic", "mops"],
+                    help="run this same command under rocprofv3 (child processes) and write "
+                         "a summary: kernel statistics, HBM traffic per launch (with the copy "
+                         "calibration) or bf16 MFMA work per launch")
+    ap.add_argument("--rocprof-dir", default="gpurun_out/rocprof",
+                    help="where --rocprof puts the profiler output and summary.md")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times: the "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -569,6 +743,9 @@ def main():
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(no sharding, no collectives); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.rocprof:  # before anything touches the GPU
+        sys.exit(rocprof(args.rocprof, rocprof_child_args(sys.argv[1:]), args.rocprof_dir))
 
     import torch
 

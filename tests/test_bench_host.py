@@ -123,3 +123,47 @@ def test_cpu_baseline_returns_baseline_and_parity():
     assert base["kind"] == "oracle" and base["value"] > 0
     assert par["sample_tokens"] >= 8 and par["within_tolerance"]
     assert bench.cpu_baseline(cfg, inp, 0.05)[1] is None
+
+
+def _write_counter_csv(path, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_rocprof_summaries_from_csv(tmp_path):
+    """The --rocprof summaries from synthetic rocprofv3 CSV output: kernel
+    statistics, and traffic per launch with the warm-up dispatch left out and
+    the copy calibration's scale applied."""
+    import csv
+    out = str(tmp_path)
+    os.makedirs(f"{out}/stats")
+    with open(f"{out}/stats/run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        w.writerow(["void moe::(anonymous namespace)::combine_kernel<true, 8, true>(int, float)",
+                    12, 2400000, 200000.0, 3.9, 199000, 213000, 1.0])
+    text = open(bench.rocprof_summary("stats", ["--steps", "3"], out, [["rocprofv3", "x"]])).read()
+    assert "| `combine_kernel<true, 8, true>` | 12 | 200.0 | 199.0 | 213.0 | 3.9 |" in text
+    assert "python3 bench.py --steps 3 --rocprof stats" in text
+    k = "void moe::(anonymous namespace)::grouped_gemm_bf16_kernel<true, 256>(int)"
+    # two launches: the first (warm-up) is left out
+    _write_counter_csv(f"{out}/FETCH_SIZE/run_counter_collection.csv",
+                       [(1, k, "FETCH_SIZE", 999.0), (5, k, "FETCH_SIZE", 1000.0)])
+    _write_counter_csv(f"{out}/WRITE_SIZE/run_counter_collection.csv",
+                       [(1, k, "WRITE_SIZE", 7.0), (5, k, "WRITE_SIZE", 500.0)])
+    cp = "__amd_rocclr_copyBuffer"
+    _write_counter_csv(f"{out}/copy-FETCH_SIZE/run_counter_collection.csv",
+                       [(1, cp, "FETCH_SIZE", 524288.0)])
+    _write_counter_csv(f"{out}/copy-WRITE_SIZE/run_counter_collection.csv",
+                       [(1, cp, "WRITE_SIZE", 1048576.0)])
+    text = open(bench.rocprof_summary("traffic", ["--workload", "w"], out, [["a"], ["b"]])).read()
+    # 1000 KiB x 2.0 (copy: 524288 KiB for 1 GiB read) = 2.048 MB; 500 KiB x 1.0
+    assert "| `grouped_gemm_bf16_kernel<true, 256>` | 1 | 1000.0 | 500.0 | 2.0 | 0.5 |" in text
+    assert "read bytes = FETCH_SIZE x 2.0000" in text
+    assert "--layer-only" in text
