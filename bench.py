@@ -24,6 +24,8 @@ touched between them, outside the timed events: read (no weight byte can then
 come from the 256 MB MALL) and, separately, written (the MALL is then full of
 dirty lines that the next kernel's reads evict with write-backs).
 
+Each workload is also timed as one step captured in a HIP graph and replayed
+(`graph_replay`, launch overhead removed; `value` stays the eager step's).
 The default run also times the 64-token, 128-expert decode workload after the
 main one, and reports it as the line's "decode" object (ms/step, tokens/s, the
 layer's fraction of HBM bandwidth, the gate/up roofline, stages, and the
@@ -298,6 +300,33 @@ def time_per_call(torch, stream, fn, reps):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
 
 
+def graph_replay_ms(torch, fn, steps):
+    """The step fn captured once in a HIP graph (torch.cuda.CUDAGraph, after
+    one eager call on a side stream) and replayed `steps` times back to back:
+    ms per replay from HIP events around the replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
+
+
 def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="plain",
             dynamic_k_min=0, fallback_min=0):
     """Everything the JSON line reports about one workload, except the CPU
@@ -344,6 +373,9 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
     if args.layer_only:  # profiling: nothing but the warm-up and the timed steps
         return {"ms_per_step": ms_step, "value": cfg.T / (ms_step * 1e-3),
                 "step_ms": dist(step_ms)}, inp, w4in
+    g_ms = graph_replay_ms(torch, lambda: blk.forward(x), steps)
+    graph = {"ms_per_step": g_ms, "tokens_per_s": cfg.T / (g_ms * 1e-3), "replays": steps}
+    log(f"{cfg.name}: {g_ms:.4f} ms/step replayed from a HIP graph")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     streaming = uses_decode_kernel(cfg) or w4
@@ -497,6 +529,7 @@ def measure(torch, binding, cfg, args, steps, w4=False, cap_factor=0.0, router="
                        "routed_pairs": int(kt.sum())})
     rep = {
         "ms_per_step": ms_step, "value": T / (ms_step * 1e-3), "config": config,
+        "graph_replay": graph,
         "roofline": roof, "step_ms": dist(step_ms), "stages_ms": stages,
         "gpu_clock": clk.summary(),
         "layer": {"tflops": lflops / (ms_step * 1e-3) / 1e12,
@@ -531,6 +564,7 @@ def decode_summary(rep):
             "step_ms": rep["step_ms"], "layer_hbm_frac": lay["hbm_frac_min_bytes"],
             "layer_hbm_gbs": lay["hbm_gbs_min_bytes"], "layer_min_bytes": lay["min_bytes"],
             "touched_experts": lay["touched_experts"], "roofline": rep["roofline"],
+            "graph_replay": rep.get("graph_replay"),
             "stages_ms": rep["stages_ms"], "mall_scrubbed": rep.get("mall_scrubbed"),
             "gpu_clock": rep["gpu_clock"]}
 
@@ -786,7 +820,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic", "config": rep["config"], "roofline": rep["roofline"],
         "step_ms": rep["step_ms"], "stages_ms": rep["stages_ms"], "gpu_clock": rep["gpu_clock"],
-        "layer": rep["layer"],
+        "layer": rep["layer"], "graph_replay": rep.get("graph_replay"),
     }
     if "mall_scrubbed" in rep:
         line["mall_scrubbed"] = rep["mall_scrubbed"]
