@@ -350,8 +350,8 @@ hipError_t launch_capacity_fallback(const moe_config& c, const int32_t* topk_idx
                                     const float* topk_w, int capacity, int fallback_min,
                                     const int32_t* offsets, const int32_t* sorted_pair,
                                     const int32_t* pair_pos, int32_t* idx_out, float* w_out,
-                                    int32_t* dropped, hipStream_t s) {
-  if (dropped) zero_count_kernel<<<1, 64, 0, s>>>(dropped);
+                                    int32_t* dropped, bool dropped_zeroed, hipStream_t s) {
+  if (dropped && !dropped_zeroed) zero_count_kernel<<<1, 64, 0, s>>>(dropped);
   const int T = c.num_tokens, per = kThreads / 64;
   capacity_fallback_kernel<<<(T + per - 1) / per, kThreads, 0, s>>>(
       T, c.num_experts, c.top_k, capacity, fallback_min, topk_idx, topk_w, offsets, sorted_pair,

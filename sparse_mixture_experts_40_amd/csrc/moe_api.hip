@@ -230,7 +230,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   // dispatched again
   const bool fallback = o.capacity_fallback_min > 0;
   const int cap1 = fallback ? 0 : o.capacity;
-  int32_t* drop1 = fallback ? nullptr : o.dropped;
+  int32_t* drop1 = o.dropped;  // with the fallback: 0 (no limit), the count starts there
   // with few router blocks and one dispatch chunk (decode batches) the
   // statistics come out of the dispatch block itself
   bool aux_done = false;
@@ -248,7 +248,7 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   if (fallback) {
     st = launched(launch_capacity_fallback(c, idx, w, o.capacity, o.capacity_fallback_min,
                                            L.offsets, L.sorted_pair, L.pair_pos, L.fb_idx,
-                                           L.fb_w, o.dropped, stream));
+                                           L.fb_w, o.dropped, true, stream));
     if (st != MOE_OK) return st;
     st = launched(launch_dispatch(c, L.fb_idx, L.fb_counts, L.offsets, L.sorted_pair, L.pair_pos,
                                   L.hist, L.base, true, 0, nullptr, stream));
@@ -400,7 +400,7 @@ moe_status moe_capacity_fallback(const moe_config* cfg, const int32_t* topk_idx,
     return MOE_ERR_INVALID_ARGUMENT;
   return launched(launch_capacity_fallback(*cfg, topk_idx, topk_w, capacity, fallback_min,
                                            expert_offsets, sorted_pair, pair_pos, topk_idx_out,
-                                           topk_w_out, dropped, stream));
+                                           topk_w_out, dropped, false, stream));
 }
 
 moe_status moe_expert_gate_up(const moe_config* cfg, const void* x, const int32_t* sorted_pair,

@@ -260,13 +260,14 @@ hipError_t launch_dispatch(const moe_config& c, const int32_t* topk_idx, int32_t
 
 // Least-loaded fallback of a capacity limit, from the dropless dispatch
 // (offsets, sorted_pair, pair_pos) of topk_idx: the routing in slot form
-// (idx_out -1 where no expert) and the dropped slots left over in *dropped
-// (zeroed here first when non-null).
+// (idx_out -1 where no expert) and the dropped slots left over added to
+// *dropped, which is zeroed here first unless dropped_zeroed (an earlier
+// launch on the stream wrote 0 there).
 hipError_t launch_capacity_fallback(const moe_config& c, const int32_t* topk_idx,
                                     const float* topk_w, int capacity, int fallback_min,
                                     const int32_t* offsets, const int32_t* sorted_pair,
                                     const int32_t* pair_pos, int32_t* idx_out, float* w_out,
-                                    int32_t* dropped, hipStream_t s);
+                                    int32_t* dropped, bool dropped_zeroed, hipStream_t s);
 
 // Expert GEMMs.
 hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sorted_pair,
