@@ -77,10 +77,10 @@ FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
-                        4666597.3, 394304.4),
-    "decode128_bf16": ("b61756b782fa4a823847f2415e89ba2f8d0fa826601eb97f9b969d5e2f8afaa2",
-                       542848.0, 1537.8),
+    "prefill128_bf16": ("068f6fbdb519562eb8580a6fbcceaabff02a8b7f131b4a4d00722bba08f0565f",
+                        4050803.9, 393975.5),
+    "decode128_bf16": ("068f6fbdb519562eb8580a6fbcceaabff02a8b7f131b4a4d00722bba08f0565f",
+                       542847.1, 1537.4),
 }
 
 
