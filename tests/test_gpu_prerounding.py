@@ -1,0 +1,76 @@
+"""The block's bf16 arithmetic before the final rounding of the output, held to
+the bare bound max|d| <= 2e-2 * RMS(oracle output) with no allowance for that
+rounding. Through the C ABI: the router, the dispatch and the expert stage of
+the bf16 configuration (its fp32 y_sorted rows; h stays bf16 as in the
+layer), then moe_combine under the same shapes with the fp32 element type,
+which sums the rows into an fp32 output. Compared with the oracle run with the
+GPU's selection (near ties aside, the oracle's own)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_mixture_experts_40_amd import binding
+from sparse_mixture_experts_40_amd.configs import MoEConfig, WORKLOADS
+from sparse_mixture_experts_40_amd.inputs import make_inputs
+
+from gpu_common import check_output, check_selection_row, dev, host, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (MoEConfig("e128_like", T=2500, H=512, E=128, k=8, I=192, norm=True, dtype="bf16"), None),
+    (MoEConfig("mixtral_like", T=700, H=512, E=8, k=2, I=1024, norm=False, dtype="bf16"), None),
+    (MoEConfig("decode_like", T=64, H=512, E=128, k=8, I=256, norm=True, dtype="bf16",
+               zipf_s=1.2), None),
+    (MoEConfig("finegrained_like", T=1000, H=256, E=64, k=8, I=128, norm=True, dtype="bf16"),
+     None),
+    (WORKLOADS["prefill128_bf16"], 48),
+    (WORKLOADS["mixtral_bf16"], 48),
+    (WORKLOADS["finegrained_bf16"], 48),
+    (WORKLOADS["decode128_bf16"], 64),
+]
+
+
+def fp32_output(cfg, inp):
+    """Router, dispatch and experts of cfg, then the combine with fp32 rows and
+    output. Returns (out fp32 [T,H], topk_idx, topk_w, logits) on the host."""
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    x = dev(inp["x"])
+    wr, wg, wu, wd = (dev(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
+    bias = dev(inp["logit_bias"]) if inp.get("logit_bias") is not None else None
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    y = torch.empty(T * k, H, dtype=torch.float32, device="cuda")
+    binding.router_topk(c, x, wr, bias, logits, idx, w)
+    binding.dispatch(c, idx, counts, offsets, sp, pp, ws)
+    binding.expert_swiglu(c, x, sp, offsets, wg, wu, wd, y, ws)
+    c32 = binding.moe_config(T, H, E, k, cfg.I, int(cfg.norm), binding.MOE_DTYPE["f32"])
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    binding.combine(c32, y, pp, w, out)
+    torch.cuda.synchronize()
+    return host(out), host(idx), host(w), host(logits)
+
+
+@pytest.mark.parametrize("cfg,n", CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_output_before_rounding_meets_bare_bound(orc, cfg, n):
+    print(f"[{cfg.name}] generating inputs", flush=True)
+    inp = make_inputs(cfg, seed=0)
+    out, idx, w, lg = fp32_output(cfg, inp)
+    tokens = (np.arange(cfg.T, dtype=np.int32) if n is None else
+              sample_tokens(cfg.T, n, seed=7))
+    ref = orc.forward_tokens(inp, cfg, tokens=tokens)
+    for i in np.flatnonzero((idx[tokens] != ref["idx"]).any(1)):  # near ties only
+        check_selection_row(ref["logits"][i], idx[tokens][i], ref["idx"][i], cfg.k, tokens[i])
+    ref = orc.forward_tokens(inp, cfg, tokens=tokens, forced_idx=idx[tokens])
+    np.testing.assert_allclose(w[tokens], ref["w"], rtol=0, atol=1e-5)
+    mx, rm = check_output(out[tokens], ref["out"], "bf16", "out_before_rounding",
+                          bf16_rounded=False)
+    print(f"{cfg.name}: {len(tokens)} tokens, before the output rounding max|d|/RMS "
+          f"{mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
