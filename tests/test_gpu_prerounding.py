@@ -74,3 +74,80 @@ def test_output_before_rounding_meets_bare_bound(orc, cfg, n):
                           bf16_rounded=False)
     print(f"{cfg.name}: {len(tokens)} tokens, before the output rounding max|d|/RMS "
           f"{mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
+
+
+def _fp32_chain(cfg, inp, idx, w, cap=0, w4=None):
+    """Given a routing (idx [T,k] with -1 for empty slots, w [T,k]): dispatch
+    (with a capacity when cap > 0), the expert stage (bf16, or 4-bit with
+    w4), and the combine with fp32 rows and output. Returns (out, keep mask)."""
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    c = binding.make_config(cfg)
+    ws = binding.alloc_workspace(c)
+    x = dev(inp["x"])
+    gi, gw = dev(np.ascontiguousarray(idx, np.int32)), dev(np.ascontiguousarray(w, np.float32))
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    y = torch.empty(T * k, H, dtype=torch.float32, device="cuda")
+    if cap:
+        binding.dispatch_capacity(c, gi, cap, counts, offsets, sp, pp, ws)
+    else:
+        binding.dispatch(c, gi, counts, offsets, sp, pp, ws)
+    if w4 is None:
+        binding.expert_swiglu(c, x, sp, offsets, *(dev(inp[n]) for n in
+                                                  ("w_gate", "w_up", "w_down")), y, ws)
+    else:
+        gw4 = binding.w4_to_device(w4)
+        s4 = binding.w4_weights(gw4)
+        h = torch.empty(T * k, cfg.I, dtype=torch.bfloat16, device="cuda")
+        binding.expert_gate_up_w4(c, x, sp, offsets, s4, h)
+        binding.expert_down_w4(c, h, offsets, s4, y)
+    c32 = binding.moe_config(T, H, E, k, cfg.I, int(cfg.norm), binding.MOE_DTYPE["f32"])
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    binding.combine(c32, y, pp, gw, out)
+    torch.cuda.synchronize()
+    return host(out), (host(pp) >= 0).reshape(T, k)
+
+
+OPTION_CASES = {
+    "capacity": (MoEConfig("e128_like", T=2500, H=512, E=128, k=8, I=192, norm=True,
+                           dtype="bf16"), {"cf": 1.0}),
+    "noise+bias": (MoEConfig("mixtral_like", T=700, H=512, E=8, k=2, I=1024, norm=False,
+                             dtype="bf16"), {"variant": True}),
+    "dynamic_k": (MoEConfig("e128_like", T=1500, H=512, E=128, k=8, I=192, norm=True,
+                            dtype="bf16"), {"dynamic_k_min": 4}),
+    "w4": (MoEConfig("decode_like", T=64, H=512, E=128, k=8, I=512, norm=True, dtype="bf16",
+                     zipf_s=1.2), {"w4": True}),
+}
+
+
+@pytest.mark.parametrize("case", list(OPTION_CASES))
+def test_option_paths_before_rounding(orc, case):
+    """The routing of a block run with the option; then the experts and the
+    fp32 combine on that routing, against the oracle's block output for the
+    same routing (the routing itself is checked by the option's own tests)."""
+    from sparse_mixture_experts_40_amd.inputs import make_router_variant_inputs, make_w4_inputs
+    cfg, opt = OPTION_CASES[case]
+    inp = make_inputs(cfg, seed=0, weights=not opt.get("w4"))
+    w4 = make_w4_inputs(cfg, seed=0) if opt.get("w4") else None
+    kw = {}
+    if opt.get("variant"):
+        var = make_router_variant_inputs(cfg, seed=0)
+        kw = dict(noise=var["noise"], w_noise=var["w_noise"], select_bias=var["select_bias"])
+    if opt.get("dynamic_k_min"):
+        kw["dynamic_k_min"] = opt["dynamic_k_min"]
+    blk = binding.MoEBlock(cfg, inp, w4=w4, **kw)
+    blk.forward(dev(inp["x"]))
+    torch.cuda.synchronize()
+    g_idx, g_w = host(blk.topk_idx), host(blk.topk_w)
+    cap = orc.capacity(cfg.T, cfg.E, cfg.k, opt["cf"]) if "cf" in opt else 0
+    out, keep = _fp32_chain(cfg, inp, g_idx, g_w, cap=cap, w4=w4)
+    idx_r = np.where(keep, g_idx, -1).astype(np.int32)
+    if cap:
+        assert (~keep & (g_idx >= 0)).any()  # the case drops pairs
+    tokens = np.arange(cfg.T, dtype=np.int32)
+    ref = orc.forward_routed(inp, cfg, idx_r, g_w, tokens=tokens, w4=w4)
+    mx, rm = check_output(out, ref, "bf16", "out_before_rounding", bf16_rounded=False)
+    print(f"{cfg.name} [{case}]: {cfg.T} tokens, before the output rounding max|d|/RMS "
+          f"{mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
