@@ -5,7 +5,6 @@ again after new input values are copied into the captured input buffer. The
 library only launches kernels on the caller's stream (no allocation, no
 synchronisation, no memset), so the whole forward can be captured. All calls
 go through the C ABI."""
-import numpy as np
 import pytest
 import torch
 
