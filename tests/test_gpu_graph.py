@@ -10,7 +10,8 @@ import torch
 
 from sparse_mixture_experts_40_amd import binding
 from sparse_mixture_experts_40_amd.configs import MoEConfig, WORKLOADS
-from sparse_mixture_experts_40_amd.inputs import make_inputs, make_w4_inputs
+from sparse_mixture_experts_40_amd.inputs import (make_inputs, make_router_variant_inputs,
+                                                  make_w4_inputs)
 
 from gpu_common import dev
 
@@ -26,6 +27,10 @@ CASES = {
     "dynamic_k": (MoEConfig("dyn", T=300, H=256, E=32, k=8, I=128, norm=True, dtype="bf16"),
                   {"dynamic_k_min": 4}),
     "w4": (MoEConfig("w4", T=64, H=512, E=16, k=4, I=512, norm=True, dtype="bf16"), {"w4": 1}),
+    "capacity": (MoEConfig("cap", T=1500, H=512, E=32, k=4, I=512, norm=True, dtype="bf16",
+                           zipf_s=1.0), {"capacity": 120}),
+    "noise+bias": (MoEConfig("var", T=700, H=512, E=8, k=2, I=1024, norm=False, dtype="bf16"),
+                   {"variant": 1}),
 }
 
 
@@ -34,8 +39,14 @@ def _bits(t):
 
 
 def _outputs(blk):
-    return [blk.out, blk.topk_idx, blk.topk_w, blk.counts, blk.f, blk.P, blk.aux,
-            blk.logits]
+    """Every output the forward writes: the block output, the routing, the
+    statistics, the z-loss, the drop count (written with a capacity) and the
+    per-token k (written with dynamic k)."""
+    outs = [blk.out, blk.topk_idx, blk.topk_w, blk.counts, blk.f, blk.P, blk.aux, blk.logits,
+            blk.z_loss, blk.dropped]
+    if blk.opts is not None and blk.opts.dynamic_k_min:
+        outs.append(blk.k_per_token)
+    return outs
 
 
 def _snapshot(blk):
@@ -65,9 +76,14 @@ def _capture(fn):
 @pytest.mark.parametrize("case", list(CASES))
 def test_layer_forward_graph_replays_match_eager(case):
     cfg, kw = CASES[case]
+    kw = dict(kw)
     inp = make_inputs(cfg, seed=1, weights="w4" not in kw)
     if "w4" in kw:
         kw = {**kw, "w4": make_w4_inputs(cfg, seed=1)}
+    if kw.pop("variant", 0):
+        var = make_router_variant_inputs(cfg, seed=1)
+        kw = {**kw, "noise": var["noise"], "w_noise": var["w_noise"],
+              "select_bias": var["select_bias"]}
     blk = binding.MoEBlock(cfg, inp, **kw)
     x = dev(inp["x"])
     blk.forward(x)
