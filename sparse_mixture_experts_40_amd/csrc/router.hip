@@ -720,7 +720,6 @@ hipError_t launch_router(const moe_config& c, const void* x, const void* w_route
                          float* topk_w, float* prob_partials, bool do_select, hipStream_t s,
                          const RouterExtras& ex) {
   const int E = c.num_experts;
-  const int EP = (E + 31) & ~31;
   size_t lds = (size_t)kTok * router_ls(E, 64) * sizeof(float);
   if (x && c.dtype == MOE_DTYPE_BF16) {
     const size_t tiles = router_tile_lds(E);
