@@ -293,6 +293,9 @@ E2E = [
     MoEConfig("single_token", T=1, H=256, E=16, k=4, I=128, norm=True, dtype="bf16"),
     MoEConfig("k_equals_E", T=50, H=128, E=8, k=8, I=128, norm=True, dtype="bf16"),
     MoEConfig("k1", T=130, H=128, E=8, k=1, I=128, norm=False, dtype="bf16"),
+    # one expert: the block degenerates to a dense SwiGLU MLP (p = 1)
+    MoEConfig("one_expert", T=70, H=128, E=1, k=1, I=128, norm=True, dtype="bf16"),
+    MoEConfig("one_expert_decode", T=8, H=256, E=1, k=1, I=256, norm=False, dtype="bf16"),
     MoEConfig("decode_skewed", T=48, H=768, E=64, k=6, I=512, norm=True, dtype="bf16",
               zipf_s=1.5),
 ]
