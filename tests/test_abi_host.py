@@ -60,6 +60,7 @@ def test_workspace_size(lib):
     ((4, 64, 8, 2, 100, 1, 1), 2),    # I % 64
     ((1, 65536, 2, 1, 32768, 1, 1), 2),     # H*I >= 2^31 (32-bit per-expert offsets)
     ((1 << 20, 4096, 8, 2, 1024, 1, 1), 2),  # T*k*max(H,I) >= 2^31
+    ((65536, 4096, 128, 8, 1536, 1, 1), 2),  # T*k*H == 2^31 exactly (one token past the limit)
     ((1, 1 << 23, 256, 1, 64, 1, 1), 2),     # E*H >= 2^31 (32-bit router offsets)
 ])
 def test_config_validation_returns_status(lib, fields, status):

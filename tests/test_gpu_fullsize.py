@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from sparse_mixture_experts_40_amd import binding
-from sparse_mixture_experts_40_amd.configs import WORKLOADS
+from sparse_mixture_experts_40_amd.configs import MoEConfig, WORKLOADS
 from sparse_mixture_experts_40_amd.inputs import make_inputs
 
 from gpu_common import check_output, compare_selection, dev, host, sample_tokens
@@ -60,6 +60,38 @@ def test_full_size_block(orc, name):
     torch.cuda.synchronize()
     bits = (lambda t: t.view(torch.int16)) if first.dtype == torch.bfloat16 else (lambda t: t)
     assert torch.equal(bits(first), bits(blk.out))
+
+
+def test_largest_accepted_batch(orc):
+    """The largest batch of the 128-expert model the library accepts: T = 65535,
+    so T*k*H is 32768 elements below 2^31 and the layer forward's fp16 y rows
+    fill all but 64 KiB of 4 GiB. One token more is rejected. Sampled tokens,
+    the last one included, against the oracle; counts and finiteness over
+    all tokens."""
+    base = WORKLOADS["prefill128_bf16"]
+    cfg = MoEConfig("prefill128_max_T", T=65535, H=base.H, E=base.E, k=base.k, I=base.I,
+                    norm=base.norm, dtype=base.dtype)
+    over = binding.moe_config(cfg.T + 1, cfg.H, cfg.E, cfg.k, cfg.I, int(cfg.norm),
+                              binding.MOE_DTYPE[cfg.dtype])
+    assert binding.workspace_size(over) == 0
+    assert binding.workspace_size(binding.make_config(cfg)) > 0
+    print(f"[{cfg.name}] generating inputs", flush=True)
+    inp = make_inputs(cfg)
+    blk = binding.MoEBlock(cfg, inp)
+    blk.forward(dev(inp["x"]))
+    torch.cuda.synchronize()
+    print(f"[{cfg.name}] forward done", flush=True)
+    tokens = np.unique(np.append(sample_tokens(cfg.T, 24, seed=2), cfg.T - 1)).astype(np.int32)
+    gi, gw = host(blk.topk_idx), host(blk.topk_w)
+    r, nmis = compare_selection(orc, cfg, inp, tokens, gi[tokens], gw[tokens])
+    mx, rm = check_output(host(blk.out)[tokens], r["out"], cfg.dtype)
+    print(f"[{cfg.name}] sampled {len(tokens)} tokens: near-tie selections {nmis}, "
+          f"max|d|/RMS {mx:.4f}, RMS(d)/RMS {rm:.5f}", flush=True)
+    counts = host(blk.counts)
+    assert (counts == np.bincount(gi.ravel(), minlength=cfg.E)).all()
+    assert counts.sum() == cfg.T * cfg.k
+    assert torch.isfinite(blk.out).all().item()
+    del blk
 
 
 @pytest.mark.parametrize("name", ["prefill128_bf16", "decode128_bf16"])
