@@ -766,7 +766,7 @@ def main():
                     help="run this same command under rocprofv3 (child processes) and write "
                          "a summary: kernel statistics, HBM traffic per launch (with the copy "
                          "calibration) or bf16 MFMA work per launch")
-    ap.add_argument("--rocprof-dir", default="gpurun_out/rocprof",
+    ap.add_argument("--rocprof-dir", default="rocprof_out",
                     help="where --rocprof puts the profiler output and summary.md")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times: the "
