@@ -34,6 +34,7 @@ static void* upload(FILE* f, size_t n) {
   if (fread(h, 1, n, f) != n || hipMalloc(&d, n ? n : 1) != hipSuccess ||
       hipMemcpy(d, h, n, hipMemcpyHostToDevice) != hipSuccess) {
     free(h);
+    if (d) (void)hipFree(d);
     return NULL;
   }
   free(h);
@@ -133,6 +134,9 @@ int main(int argc, char** argv) {
     return 1;
   }
   fclose(o);
+  void* bufs[] = {x, wr, wg, wu, wd, bias, out, idx, w, counts, f, P, aux, ws};
+  for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i)
+    if (bufs[i]) HIP_OK(hipFree(bufs[i]));
   printf("moe_c_example: T=%zu H=%zu E=%zu k=%zu I=%zu dtype=%s workspace=%zu bytes: ok\n", T, H,
          E, k, I, c.dtype == MOE_DTYPE_BF16 ? "bf16" : "f32", wsb);
   return 0;
