@@ -94,4 +94,16 @@ hipError_t launch_dispatch_aux(const moe_config& c, const int32_t* topk_idx, int
                                int32_t* hist, int32_t* rank0, int capacity, int32_t* dropped,
                                const AuxSmallArgs& aux, bool* fused, hipStream_t s);
 
+// Decode-sized bf16 gate/up of a one-chunk routing with the dispatch inside
+// it (gate_up_sorts_itself): each block of the weight-streaming kernel sorts
+// topk_idx in its LDS like the one-chunk dispatch (same capacity rule);
+// block 0 writes counts (nullable), offsets, sorted_pair, pair_pos and
+// *dropped (nullable), block 1 the statistics *aux (nullable: none).
+bool gate_up_sorts_itself(const moe_config& c);
+hipError_t launch_gate_up_sorting(const moe_config& c, const void* x, const int32_t* topk_idx,
+                                  int capacity, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_pair, int32_t* pair_pos, int32_t* dropped,
+                                  const AuxSmallArgs* aux, const void* w_gate, const void* w_up,
+                                  void* h, hipStream_t s);
+
 }  // namespace moe

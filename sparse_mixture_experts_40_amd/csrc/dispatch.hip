@@ -27,27 +27,14 @@
 // pair_pos = -1.
 // No device-to-host traffic; everything stays on the stream.
 #include "aux_small.h"
+#include "dispatch_chunk.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kChunk = 2048;
-constexpr int kThreads = 256;
-
-__device__ __forceinline__ int clamp_expert(int v, int E) { return v < 0 ? 0 : (v >= E ? E - 1 : v); }
-
-// LDS histogram of the chunk starting at pair p0 (s_h zeroed by the caller).
-__device__ __forceinline__ void hist_chunk(int P, int E, const int32_t* __restrict__ idx, int p0,
-                                           int* s_h) {
-  for (int i = threadIdx.x; i < kChunk; i += kThreads) {
-    const int p = p0 + i;
-    if (p < P) {
-      const int v = idx[p];
-      if (v >= 0) atomicAdd(&s_h[clamp_expert(v, E)], 1);  // v < 0: empty slot
-    }
-  }
-}
+constexpr int kChunk = kDispChunk;
+constexpr int kThreads = kDispThreads;
 
 __global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(int P, int E,
                                                                  const int32_t* __restrict__ idx,
@@ -100,53 +87,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
   if (dropped && e == 0) *dropped = s_drop;
 }
 
-// Stable scatter of the chunk starting at pair p0. s_rank[e]: rank inside
-// expert e of the chunk's first pair of e; s_off[e]: the expert's first
-// sorted row; s_wc zeroed; all three visible to the block (caller syncs).
-__device__ __forceinline__ void scatter_chunk(int P, int E, int cap,
-                                              const int32_t* __restrict__ idx, int p0,
-                                              int* s_rank, const int* s_off, int (*s_wc)[256],
-                                              int32_t* __restrict__ sorted_pair,
-                                              int32_t* __restrict__ pair_pos) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  for (int it = 0; it < kChunk / kThreads; ++it) {
-    if (p0 + it * kThreads >= P) break;  // block-uniform: the rest of the chunk is past P
-    const int p = p0 + it * kThreads + tid;
-    const int raw = p < P ? idx[p] : -1;
-    const bool valid = raw >= 0;  // a negative id is an empty slot: no pair
-    if (p < P && !valid) pair_pos[p] = -1;
-    const int v = valid ? clamp_expert(raw, E) : 0;
-    unsigned long long same = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (v >> b) & 1;
-      const unsigned long long bb = __ballot(bit);
-      same &= bit ? bb : ~bb;
-    }
-    const int rank = __popcll(same & lt_mask);
-    if (valid && rank == 0) s_wc[wave][v] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int r = s_rank[v] + rank;
-      for (int w = 0; w < wave; ++w) r += s_wc[w][v];
-      if (cap <= 0 || r < cap) {
-        const int pos = s_off[v] + r;
-        sorted_pair[pos] = p;
-        pair_pos[p] = pos;
-      } else {
-        pair_pos[p] = -1;
-      }
-    }
-    __syncthreads();
-    if (tid < E) {
-      s_rank[tid] += s_wc[0][tid] + s_wc[1][tid] + s_wc[2][tid] + s_wc[3][tid];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
-    }
-    __syncthreads();
+// The global outputs of a scatter: sorted_pair[pos] = p, pair_pos[p] = pos,
+// and pair_pos = -1 for a dropped pair or an empty slot.
+struct GlobalSink {
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  __device__ void operator()(int p, int pos) const {
+    sorted_pair[pos] = p;
+    pair_pos[p] = pos;
   }
-}
+};
+struct GlobalDrop {
+  int32_t* pair_pos;
+  __device__ void operator()(int p) const { pair_pos[p] = -1; }
+};
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     int P, int E, int cap, const int32_t* __restrict__ idx, const int32_t* __restrict__ rank0,
@@ -163,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
 #pragma unroll
   for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
   __syncthreads();
-  scatter_chunk(P, E, cap, idx, blockIdx.x * kChunk, s_rank, s_off, s_wc, sorted_pair, pair_pos);
+  scatter_chunk(P, E, cap, idx, blockIdx.x * kChunk, s_rank, s_off, s_wc,
+                GlobalSink{sorted_pair, pair_pos}, GlobalDrop{pair_pos});
 }
 
 // One chunk (P <= kChunk): histogram, scan and scatter in one block. Every
@@ -213,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_single_kernel(
   s_off[e] = excl;
   s_h[e] = 0;  // becomes the running rank of each expert
   __syncthreads();
-  scatter_chunk(P, E, cap, idx, 0, s_h, s_off, s_wc, sorted_pair, pair_pos);
+  scatter_chunk(P, E, cap, idx, 0, s_h, s_off, s_wc, GlobalSink{sorted_pair, pair_pos},
+                GlobalDrop{pair_pos});
 }
 
 // Least-loaded fallback of a capacity limit ([QWEN3-ROUTE] §四: a token left
@@ -244,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void capacity_fallback_kernel(
     e = idx[p];
     wv = w[p];
     if (e >= 0) {  // a pair (a negative id is an empty slot)
-      kept = pair_pos[p] - offsets[clamp_expert(e, E)] < cap;
+      kept = pair_pos[p] - offsets[disp_clamp_expert(e, E)] < cap;
       drop = !kept;
     }
   }

@@ -26,6 +26,8 @@
 // Decode-sized batches (few rows per expert) take the weight-streaming
 // kernels further down instead.
 // fp32 path (fp32 workloads): plain FMA kernels, one block per sorted row.
+#include "aux_small.h"
+#include "dispatch_chunk.h"
 #include "moe_internal.h"
 
 #include <atomic>
@@ -755,6 +757,19 @@ __device__ __forceinline__ void dec_kloop(int ng, const uint16_t* ring, uint32_t
 
 // The loads of one work item as a wave sees them: weight descriptors and
 // per-lane offsets, token offsets of its (single) pass.
+// The one-chunk sort of a SORT gate/up launch (idx null otherwise).
+struct DecSort {
+  const int32_t* idx;  // [P] expert of each routing pair (-1: empty slot)
+  int P, cap;          // pairs; capacity (0: none)
+  int32_t* counts;     // [E] pairs per expert (nullable)
+  int32_t* offsets;    // [E+1] first sorted row of each expert
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int32_t* dropped;  // pairs past the capacity (nullable)
+  int do_aux;        // block 1 writes the statistics `aux`
+  AuxSmallArgs aux;
+};
+
 struct DecItem {
   i32x4_t rw0, rw1;
   uint32_t w_off[8], t_off[8];
@@ -866,20 +881,58 @@ __device__ __forceinline__ void dec_epilogue(const f32x16_t (&acc)[NB][2], float
 
 // act holds act_bytes bytes (token rows x K); every byte offset formed below
 // is smaller than that (the launcher checks it fits 32 bits).
-template <bool GATEUP>
+// SORT (gate/up of a one-chunk routing): every block sorts the routing pairs
+// ds.idx in its own LDS (the dispatch's stable counting sort) and takes its
+// rows' tokens from there, so no dispatch launch precedes the kernel. Block 0
+// writes the sort's outputs for the kernels that follow (counts, offsets,
+// sorted_pair, pair_pos, the dropped count), block 1 the load-balance
+// statistics when ds.do_aux; both then run their items like the others.
+template <bool GATEUP, bool SORT = false>
 __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
     int E, int K, int N_out, int k_top, const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, void* __restrict__ out,
-    int n_chunks) {
+    int n_chunks, DecSort ds) {
   constexpr int NB = 2;  // weight blocks of 32 rows: gate + up, or 2 down blocks
   static_assert(NB * 2 * 16 * 64 <= kDecRegion / 2, "partial sums fit the wave's ring");
+  static_assert(sizeof(DispLds) <= sizeof(uint16_t) * 4 * kDecRegion, "sort LDS fits the ring");
   __shared__ __align__(1024) uint16_t s_ring[4 * kDecRegion];
   __shared__ int s_scan[2 * 256 + 2];
+  __shared__ uint16_t s_tok[SORT ? kDispChunk : 1];  // token of each sorted row
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // s_scan[e]: inclusive count of experts with rows; offsets in s_scan[E+1..]
-  for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  if constexpr (SORT) {
+    DispLds& L = *reinterpret_cast<DispLds*>(s_ring);  // the ring is not in use yet
+    const int tot = disp_counts(ds.P, E, ds.cap, ds.idx, L);
+    if (blockIdx.x == 1 && ds.do_aux) aux_small_body(ds.aux, tot);  // block-uniform
+    const bool b0 = blockIdx.x == 0;
+    if (b0) {
+      if (tid < E) {
+        if (ds.counts) ds.counts[tid] = tot;
+        ds.offsets[tid] = L.off[tid];
+      }
+      if (tid == 0) {
+        ds.offsets[E] = L.c[255];
+        if (ds.dropped) *ds.dropped = L.drop;
+      }
+    }
+    for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = i < E ? L.off[i] : L.c[255];
+    scatter_chunk(
+        ds.P, E, ds.cap, ds.idx, 0, L.h, L.off, L.wc,
+        [&](int p, int pos) {
+          s_tok[pos] = (uint16_t)(p / k_top);
+          if (b0) {
+            ds.sorted_pair[pos] = p;
+            ds.pair_pos[p] = pos;
+          }
+        },
+        [&](int p) {
+          if (b0) ds.pair_pos[p] = -1;
+        });  // ends with a barrier: L is free for the ring
+  } else {
+    for (int i = tid; i <= E; i += blockDim.x) s_scan[E + 1 + i] = offsets[i];
+  }
   __syncthreads();
   if (tid < E) s_scan[tid] = (s_scan[E + 2 + tid] > s_scan[E + 1 + tid]) ? 1 : 0;
   __syncthreads();
@@ -936,7 +989,8 @@ __global__ __launch_bounds__(256, kDecOcc) void decode_gemm_bf16_kernel(
       const int t = kDecRPI * j + lrow;  // token row of the pass (LDS row 64 + t)
       int gi = p0 + t;
       gi = gi < r1 ? gi : r1 - 1;
-      const int arow = GATEUP ? sorted_pair[gi] / k_top : gi;
+      int arow = gi;
+      if constexpr (GATEUP) arow = SORT ? (int)s_tok[gi] : sorted_pair[gi] / k_top;
       d.t_off[j] = ((uint32_t)arow * (uint32_t)K + (uint32_t)(wave * kw) +
                     (uint32_t)((lch ^ swz_f<kDecK>(t)) * 8)) * 2u;
     }
@@ -1579,7 +1633,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
     decode_gemm_bf16_kernel<true><<<persistent_grid() * kDecOcc, 256, 0, s>>>(
         c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
         (uint32_t)((size_t)c.num_tokens * c.hidden * 2), sorted_pair, offsets, static_cast<const uint16_t*>(w_gate),
-        static_cast<const uint16_t*>(w_up), h, nch);
+        static_cast<const uint16_t*>(w_up), h, nch, DecSort{});
     return hipGetLastError();
   }
   const int ntn = (c.intermediate + 127) / 128;
@@ -1598,6 +1652,37 @@ hipError_t launch_gate_up(const moe_config& c, const void* x, const int32_t* sor
   return hipGetLastError();
 }
 
+bool gate_up_sorts_itself(const moe_config& c) {
+  const long P = (long)c.num_tokens * c.top_k;
+  return c.dtype == MOE_DTYPE_BF16 && use_decode_path(c) && P <= kDispChunk &&
+         c.num_experts <= 256 && persistent_grid() >= 2;
+}
+
+hipError_t launch_gate_up_sorting(const moe_config& c, const void* x, const int32_t* topk_idx,
+                                  int capacity, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_pair, int32_t* pair_pos, int32_t* dropped,
+                                  const AuxSmallArgs* aux, const void* w_gate, const void* w_up,
+                                  void* h, hipStream_t s) {
+  if (!gate_up_sorts_itself(c)) return hipErrorInvalidValue;
+  DecSort ds{};
+  ds.idx = topk_idx;
+  ds.P = c.num_tokens * c.top_k;
+  ds.cap = capacity;
+  ds.counts = counts;
+  ds.offsets = offsets;
+  ds.sorted_pair = sorted_pair;
+  ds.pair_pos = pair_pos;
+  ds.dropped = dropped;
+  ds.do_aux = aux ? 1 : 0;
+  if (aux) ds.aux = *aux;
+  const int nch = (c.intermediate + 31) / 32;
+  decode_gemm_bf16_kernel<true, true><<<persistent_grid() * kDecOcc, 256, 0, s>>>(
+      c.num_experts, c.hidden, c.intermediate, c.top_k, static_cast<const uint16_t*>(x),
+      (uint32_t)((size_t)c.num_tokens * c.hidden * 2), nullptr, nullptr,
+      static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), h, nch, ds);
+  return hipGetLastError();
+}
+
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offsets,
                        const void* w_down, void* y, hipStream_t s, int8_t* y_exp,
                        bool* y_half) {
@@ -1613,7 +1698,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* offset
     const int nch = (c.hidden + 63) / 64;
     decode_gemm_bf16_kernel<false><<<persistent_grid() * kDecOcc, 256, 0, s>>>(
         c.num_experts, c.intermediate, c.hidden, c.top_k, static_cast<const uint16_t*>(h),
-        (uint32_t)((size_t)P * c.intermediate * 2), nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch);
+        (uint32_t)((size_t)P * c.intermediate * 2), nullptr, offsets, static_cast<const uint16_t*>(w_down), nullptr, y, nch, DecSort{});
     return hipGetLastError();
   }
   const int ntn = (c.hidden + 255) / 256;

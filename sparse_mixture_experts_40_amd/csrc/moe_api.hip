@@ -234,7 +234,20 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
   // with few router blocks and one dispatch chunk (decode batches) the
   // statistics come out of the dispatch block itself
   bool aux_done = false;
-  if ((want_aux || ao.z_loss) && aux_small_fits(c, router_blocks)) {
+  // decode batches of one dispatch chunk: the gate/up kernel sorts the
+  // routing itself, with the statistics in its second block, so no dispatch
+  // launch sits between the router and it (with the fallback, the first
+  // dispatch feeds the fallback kernel and keeps its launch)
+  const bool sort_in_gemm = !fallback && !w4 && gate_up_sorts_itself(c);
+  AuxSmallArgs sort_aux{};
+  const AuxSmallArgs* sort_aux_p = nullptr;
+  if (sort_in_gemm) {
+    if ((want_aux || ao.z_loss) && aux_small_fits(c, router_blocks)) {
+      sort_aux = aux_small_args(c, L.partials, router_blocks, ao, ex.zpart, router_blocks);
+      sort_aux_p = &sort_aux;
+      aux_done = true;
+    }
+  } else if ((want_aux || ao.z_loss) && aux_small_fits(c, router_blocks)) {
     st = launched(launch_dispatch_aux(
         c, idx, L.counts, L.offsets, L.sorted_pair, L.pair_pos, L.hist, L.base, cap1, drop1,
         aux_small_args(c, L.partials, router_blocks, ao, ex.zpart, router_blocks), &aux_done,
@@ -267,7 +280,12 @@ moe_status layer_forward_impl(const moe_config* cfg, const moe_options* opt, con
     if (st != MOE_OK) return st;
     st = launched(launch_down_w4(c, L.h, L.offsets, *w4, L.y, stream));
   } else {
-    st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
+    if (sort_in_gemm)
+      st = launched(launch_gate_up_sorting(c, x, idx, cap1, L.counts, L.offsets, L.sorted_pair,
+                                           L.pair_pos, drop1, sort_aux_p, w_gate, w_up, L.h,
+                                           stream));
+    else
+      st = launched(launch_gate_up(c, x, L.sorted_pair, L.offsets, w_gate, w_up, L.h, stream));
     if (st != MOE_OK) return st;
     st = launched(launch_down(c, L.h, L.offsets, w_down, L.y, stream, y_exp, &y_half));
   }
