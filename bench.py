@@ -77,10 +77,10 @@ FETCH_SCALE = 1048576.0 / 524304.8
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     # workload: (sources sha256, FETCH_SIZE KiB, WRITE_SIZE KiB) per gate/up launch
-    "prefill128_bf16": ("068f6fbdb519562eb8580a6fbcceaabff02a8b7f131b4a4d00722bba08f0565f",
-                        4050803.9, 393975.5),
-    "decode128_bf16": ("068f6fbdb519562eb8580a6fbcceaabff02a8b7f131b4a4d00722bba08f0565f",
-                       542847.1, 1537.4),
+    "prefill128_bf16": ("b4d81da6824de0e0b6f68dc276a530695be055012a8f348e97d73be92cc231ee",
+                        3856735.1, 393996.8),
+    "decode128_bf16": ("b4d81da6824de0e0b6f68dc276a530695be055012a8f348e97d73be92cc231ee",
+                       542915.6, 1564.6),
 }
 
 

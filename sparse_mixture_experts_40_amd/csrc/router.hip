@@ -648,7 +648,92 @@ __global__ __launch_bounds__(kThreads) void router_reduce_kernel(int T, int E, i
   if (logits_out) logits_out[i] = s;
 }
 
+// Small-T router logits in one launch, without split-K partials (a decode
+// batch): block (tg, eg) computes tokens [4 tg, 4 tg + 4) x 4 kRlEpw experts,
+// wave w the kRlEpw experts from (4 eg + w) kRlEpw on. Lane l holds the K
+// elements (64 c + l) 8 .. + 7 for c < H / 512, so each load instruction
+// reads 1 KB of consecutive elements; it sums them in c order with fp32 FMA,
+// the wave adds its lanes by a fixed butterfly (deterministic), then the
+// bias is added. H % 512 == 0.
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
+    acc = fmaf(__uint_as_float(av[i] & 0xFFFF0000u), __uint_as_float(bv[i] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
+
+#ifndef MOE_RL_EPW
+#define MOE_RL_EPW 1
+#endif
+constexpr int kRlEpw = MOE_RL_EPW;  // experts per wave
+
+__global__ __launch_bounds__(kThreads) void router_logits_direct_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 4, e0 = blockIdx.y * (4 * kRlEpw) + wave * kRlEpw;
+  const uint16_t* xr[4];
+  const uint16_t* wrow[kRlEpw];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr[i] = x + (size_t)min(t0 + i, T - 1) * H;
+#pragma unroll
+  for (int j = 0; j < kRlEpw; ++j) wrow[j] = wr + (size_t)min(e0 + j, E - 1) * H;
+  float acc[4][kRlEpw];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kRlEpw; ++j) acc[i][j] = 0.0f;
+  const int nc = H / 512;
+#pragma unroll 4
+  for (int c = 0; c < nc; ++c) {
+    const int off = (c * 64 + lane) * 8;
+    uint4 xv[4], wv[kRlEpw];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xr[i] + off);
+#pragma unroll
+    for (int j = 0; j < kRlEpw; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow[j] + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kRlEpw; ++j) acc[i][j] = dot8_bf16(xv[i], wv[j], acc[i][j]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kRlEpw; ++j) acc[i][j] += __shfl_xor(acc[i][j], d);
+  if (lane < 4 * kRlEpw) {  // lane kRlEpw i + j writes (token t0 + i, expert e0 + j)
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kRlEpw; ++j)
+        if (lane == kRlEpw * i + j) v = acc[i][j];
+    const int t = t0 + lane / kRlEpw, e = e0 + lane % kRlEpw;
+    if (t < T && e < E) out[(size_t)t * E + e] = bias ? v + bias[e] : v;
+  }
+}
+
 }  // namespace
+
+// Small-T logits in one launch (router_logits_direct_kernel) instead of
+// split-K partials and their sum.
+static bool router_direct(const moe_config& c) {
+  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0;
+}
+
+static void launch_logits_direct(const moe_config& c, const void* x, const void* w,
+                                 const float* bias, float* out, hipStream_t s) {
+  const dim3 grid((c.num_tokens + 3) / 4, (c.num_experts + 4 * kRlEpw - 1) / (4 * kRlEpw));
+  router_logits_direct_kernel<<<grid, kThreads, 0, s>>>(c.num_tokens, c.hidden, c.num_experts,
+                                                        static_cast<const uint16_t*>(x),
+                                                        static_cast<const uint16_t*>(w), bias,
+                                                        out);
+}
 
 // Tokens per router block: 64 when the block computes its logits (one MFMA
 // tile); fewer when it starts from logits and T is small, so that the tokens
@@ -695,6 +780,18 @@ hipError_t launch_router_split(const moe_config& c, const void* x, const void* w
                                const float* bias, float* logits_out, float* part,
                                int32_t* topk_idx, float* topk_w, float* prob_partials,
                                hipStream_t s, const RouterExtras& ex) {
+  if (router_direct(c)) {  // the logits in one launch, then the top-k pass from them
+    float* lg = logits_out ? logits_out : part;
+    launch_logits_direct(c, x, w_router, bias, lg, s);
+    RouterExtras e2 = ex;
+    e2.noise = nullptr;
+    e2.nlogits = nullptr;
+    e2.logits_final = nullptr;
+    e2.part = nullptr;
+    e2.nsplit = 0;
+    return launch_router(c, nullptr, nullptr, nullptr, lg, false, topk_idx, topk_w,
+                         prob_partials, true, s, e2);
+  }
   launch_partial(c, x, w_router, part, s);
   RouterExtras e2 = ex;
   e2.noise = nullptr;  // the split path serves the plain logits
@@ -708,6 +805,10 @@ hipError_t launch_router_split(const moe_config& c, const void* x, const void* w
 
 hipError_t launch_logits_split(const moe_config& c, const void* x, const void* w,
                                const float* bias, float* out, float* part, hipStream_t s) {
+  if (router_direct(c)) {
+    launch_logits_direct(c, x, w, bias, out, s);
+    return hipGetLastError();
+  }
   launch_partial(c, x, w, part, s);
   const int n = c.num_tokens * c.num_experts;
   router_reduce_kernel<<<(n + kThreads - 1) / kThreads, kThreads, 0, s>>>(
