@@ -721,9 +721,11 @@ __global__ __launch_bounds__(kThreads) void router_logits_direct_kernel(
 }  // namespace
 
 // Small-T logits in one launch (router_logits_direct_kernel) instead of
-// split-K partials and their sum.
+// split-K partials and their sum: decode batches (T <= 256). Larger split
+// grids keep the MFMA partials, since every expert group of the direct
+// kernel reads all of x again.
 static bool router_direct(const moe_config& c) {
-  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0;
+  return c.dtype == MOE_DTYPE_BF16 && c.hidden % 512 == 0 && c.num_tokens <= 256;
 }
 
 static void launch_logits_direct(const moe_config& c, const void* x, const void* w,
