@@ -228,10 +228,12 @@ moe_status moe_router_topk(const moe_config* cfg, const void* x, const void* w_r
  * Noise needs x (the noise logits are computed from it) and a workspace of
  * moe_workspace_size bytes; logits (if non-NULL) receives the noisy logits.
  * Without noise the workspace may be NULL. When it is given and T is small
- * (bf16, fewer than one router block per CU), the logits are computed split
- * along H over many blocks and the partial sums added in a fixed order, the
- * order moe_layer_forward uses; moe_router_topk (no workspace) sums along H in
- * one block, so its logits may differ from these in the last bits. */
+ * (bf16, fewer than one router block per CU), the logits are computed over
+ * many blocks in a fixed order, the order moe_layer_forward uses: for
+ * T <= 256 with H a multiple of 512 all T x E logits in one launch (each
+ * logit one wave's fixed-order sum along H), otherwise split along H with
+ * the partial sums added in split order. moe_router_topk (no workspace) sums
+ * along H in one block, so its logits may differ from these in the last bits. */
 moe_status moe_router_topk_ex(const moe_config* cfg, const moe_options* opt, const void* x,
                               const void* w_router, const float* logit_bias, float* logits,
                               int32_t* topk_idx, float* topk_w, void* workspace,
